@@ -1,0 +1,183 @@
+"""Plain fp64 CPU oracle for BigBird block-sparse self-attention (forward).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code, tables or helpers with the HIP
+library; the two meet only through the seeded inputs handed to both.
+
+Sources (the pages this follows; no code was available, only prose):
+  [P2-pattern]  page "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的完整实践"
+                (TF Model Garden walkthrough), section
+                "BigBird：从二次方注意力到线性稀疏注意力" -- the three-part pattern
+                (3-block band, first/last block global, num_rand_blocks random
+                blocks), the -10000 offset on masked logits and the softmax.
+  [P2-randmask] same page, section "随机块掩码是如何生成的" -- random blocks are
+                drawn from the block ids without the first and last block, the
+                row's own window excluded; one table per head; the [B, L] input
+                mask.
+  [P4-method]   page "Big Bird: Transformers for Longer Sequences" (paper card),
+                section "方法适配" -- global + window + random, block-level.
+
+What it computes (the plainest reading of those passages; every reading the
+pages leave open is listed in the design notes of the repository):
+  nb = L / block, blk(t) = t // block, G = {0, nb-1},
+  R_h(i) = set(rand_idx[h, i-1, :]) for middle block i in [1, nb-2].
+  Allowed_h(t, u) <=> blk(t) in G  or  blk(u) in G  or  |blk(t)-blk(u)| <= 1
+                      or  blk(u) in R_h(blk(t))
+  s[b,h,t,u] = q.k / sqrt(d) - 10000 * [pad[b,u] == 0]      (allowed pairs)
+  out[b,h,t] = sum_u softmax_u(s[b,h,t,:]) v[b,h,u]           (others: -inf)
+
+Every step is a plain definition evaluated with numpy in float64: build the
+block adjacency, expand it to the explicit token mask, dense masked softmax
+attention.  Rows may be evaluated in groups (each row's softmax is
+independent), which bounds host memory at long L; nothing else is blocked,
+fused or reordered.
+
+Pins: see the test suite (brute force on tiny inputs, a hand-derived golden
+fixture, closed-form allowed-key counts, dense/global special cases against
+torch's scaled_dot_product_attention, invariants).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MASK_OFFSET = -10000.0  # [P2-pattern]: masked logits get -10000 added
+
+
+def num_blocks(L: int, block: int) -> int:
+    if block <= 0 or L % block != 0:
+        raise ValueError(f"L={L} is not a multiple of block={block}")
+    nb = L // block
+    if nb < 3:
+        raise ValueError(f"need at least 3 blocks (two global + one middle), got {nb}")
+    return nb
+
+
+def check_rand_idx(rand_idx, H: int, L: int, block: int, r: int) -> None:
+    """Raise ValueError unless rand_idx is a valid random-block table.
+
+    [P2-randmask]: per head, one row per middle block (nb-2 rows), each row
+    holding num_rand_blocks distinct block ids drawn from the middle blocks
+    1..nb-2 with the row's own window {i-1, i, i+1} removed.  Row i-1 belongs
+    to middle block i.  Order inside a row is not a constraint.
+    """
+    nb = num_blocks(L, block)
+    a = np.asarray(rand_idx)
+    if a.shape != (H, nb - 2, r):
+        raise ValueError(f"rand_idx shape {a.shape} != {(H, nb - 2, r)}")
+    if r == 0:
+        return
+    if not np.issubdtype(a.dtype, np.integer):
+        raise ValueError(f"rand_idx must be integer, got {a.dtype}")
+    for h in range(H):
+        for row in range(nb - 2):
+            i = row + 1  # the middle block this row belongs to
+            seen = set()
+            for e in a[h, row].tolist():
+                if not (1 <= e <= nb - 2):
+                    raise ValueError(f"head {h} block {i}: random block {e} outside 1..{nb - 2}")
+                if e in (i - 1, i, i + 1):
+                    raise ValueError(f"head {h} block {i}: random block {e} inside the window")
+                if e in seen:
+                    raise ValueError(f"head {h} block {i}: random block {e} repeated")
+                seen.add(e)
+
+
+def block_adjacency(rand_idx_h, nb: int) -> np.ndarray:
+    """Block-level attention pattern of one head: bool [nb, nb], row = query block.
+
+    [P2-pattern]: the first and last query blocks attend every key block; a
+    middle block i attends its band {i-1, i, i+1}, the two global key blocks
+    and its random blocks R_h(i).
+    """
+    A = np.zeros((nb, nb), dtype=bool)
+    A[0, :] = True
+    A[nb - 1, :] = True
+    ri = np.asarray(rand_idx_h)
+    for i in range(1, nb - 1):
+        A[i, i - 1:i + 2] = True          # band
+        A[i, 0] = True                    # global key blocks
+        A[i, nb - 1] = True
+        if ri.size:
+            A[i, ri[i - 1]] = True        # random blocks of row i-1
+    return A
+
+
+def token_mask(adj: np.ndarray, block: int) -> np.ndarray:
+    """Explicit L x L token mask: kron(adj, ones(block, block))."""
+    return np.kron(adj, np.ones((block, block), dtype=bool)).astype(bool)
+
+
+def _mask_rows(adj: np.ndarray, block: int, rows: np.ndarray) -> np.ndarray:
+    """Rows `rows` of token_mask(adj, block), without building all L x L."""
+    return np.repeat(adj[rows // block], block, axis=1)
+
+
+def attention_rows(q_bh, k_bh, v_bh, pad_b, adj, block: int, rows) -> np.ndarray:
+    """Output rows `rows` of one (batch, head): fp64 [len(rows), d].
+
+    q_bh/k_bh/v_bh: [L, d]; pad_b: [L] (nonzero = valid token) or None;
+    adj: the head's block adjacency.  Dense masked softmax attention in fp64.
+    """
+    q = np.asarray(q_bh, dtype=np.float64)
+    k = np.asarray(k_bh, dtype=np.float64)
+    v = np.asarray(v_bh, dtype=np.float64)
+    L, d = k.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    s = (q[rows] @ k.T) / math.sqrt(d)
+    if pad_b is not None:
+        padded = (np.asarray(pad_b) == 0).astype(np.float64)
+        s = s + MASK_OFFSET * padded[None, :]
+    allowed = _mask_rows(adj, block, rows)
+    s = np.where(allowed, s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def attention_probs(q_bh, k_bh, pad_b, adj, block: int) -> np.ndarray:
+    """Full probability matrix P [L, L] of one (batch, head); tiny inputs only."""
+    q = np.asarray(q_bh, dtype=np.float64)
+    k = np.asarray(k_bh, dtype=np.float64)
+    L, d = k.shape
+    s = (q @ k.T) / math.sqrt(d)
+    if pad_b is not None:
+        s = s + MASK_OFFSET * (np.asarray(pad_b) == 0).astype(np.float64)[None, :]
+    s = np.where(token_mask(adj, block), s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def attention_forward(q, k, v, pad_mask, rand_idx, block: int,
+                      row_group: int = 4096, units=None) -> np.ndarray:
+    """BigBird block-sparse attention forward in fp64.
+
+    q, k, v: [B, H, L, d] (any real dtype; upcast to fp64 exactly as given);
+    pad_mask: [B, L] (nonzero = valid) or None (no padding);
+    rand_idx: [H, nb-2, r] integer table (validated first).
+    units: optional iterable of (b, h) pairs to evaluate; other units are NaN.
+    Returns fp64 [B, H, L, d].
+    """
+    B, H, L, d = np.shape(q)
+    nb = num_blocks(L, block)
+    rand_idx = np.asarray(rand_idx)
+    r = rand_idx.shape[2] if rand_idx.ndim == 3 else 0
+    check_rand_idx(rand_idx, H, L, block, r)
+    out = np.full((B, H, L, d), np.nan, dtype=np.float64)
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(H)]
+    adjs = {}
+    for b, h in units:
+        if h not in adjs:
+            adjs[h] = block_adjacency(rand_idx[h], nb)
+        pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
+        for r0 in range(0, L, row_group):
+            rows = np.arange(r0, min(L, r0 + row_group))
+            out[b, h, rows] = attention_rows(q[b, h], k[b, h], v[b, h], pad_b,
+                                             adjs[h], block, rows)
+    return out
