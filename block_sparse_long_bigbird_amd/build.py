@@ -1,0 +1,58 @@
+"""Build libbb_attn.so in-tree with hipcc for gfx950.
+
+    python -m block_sparse_long_bigbird_amd.build
+
+Compiles the HIP kernels + C-ABI launcher (csrc/bb_attn.hip) and the host
+adjacency builder (csrc/bb_adjacency.cpp) into block_sparse_long_bigbird_amd/lib/.
+Packed-fp32 instructions are switched off for all device code.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBDIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIBDIR, "libbb_attn.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libbb_attn.so)")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIBDIR, exist_ok=True)
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Wall", "-I", INCLUDE,
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        os.path.join(CSRC, "bb_attn.hip"),
+        os.path.join(CSRC, "bb_adjacency.cpp"),
+        "-o", tmp,
+    ]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "packed-fp32-ops"  # the host pass does not know this device feature
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,139 @@
+/*
+ * bb_attn.h -- C ABI of libbb_attn.so: BigBird block-sparse self-attention
+ * forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的完整实践",
+ * section "BigBird：从二次方注意力到线性稀疏注意力"; paper card "Big Bird:
+ * Transformers for Longer Sequences", section "方法适配"):
+ *   Q, K, V are cut into blocks of `block` tokens, nb = L / block.  Query
+ *   blocks 0 and nb-1 are global and attend every key.  A middle query block
+ *   i (1 <= i <= nb-2) attends the band {i-1, i, i+1}, the two global key
+ *   blocks and the r random blocks listed in rand_idx[h][i-1][:].  Logits are
+ *   q.k / sqrt(d); keys marked as padding get -10000 added; one softmax per
+ *   query row over all attended keys; out = softmax . V.
+ *
+ * Conventions for every function below:
+ *   - Return value is a bb_status; nothing throws across the ABI.
+ *   - All argument validation happens on the host before any HIP call.  On a
+ *     validation error nothing is launched and no memory is touched.
+ *   - The library never allocates or frees memory; the caller owns every
+ *     buffer.  It keeps no mutable global state.
+ *   - Tensors are dense, row-major, contiguous.
+ */
+#ifndef BB_ATTN_H_
+#define BB_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BB_ABI_VERSION 1
+
+typedef enum {
+  BB_OK = 0,
+  BB_ERR_NULL = 1,       /* a required pointer is NULL */
+  BB_ERR_SHAPE = 2,      /* unsupported or inconsistent sizes */
+  BB_ERR_DTYPE = 3,      /* dtype is not a bb_dtype value */
+  BB_ERR_RAND_IDX = 4,   /* random-block table violates its constraints */
+  BB_ERR_WORKSPACE = 5,  /* workspace smaller than bb_attn_workspace_bytes() */
+  BB_ERR_HIP = 6,        /* a HIP launch reported an error */
+  BB_ERR_ALIAS = 7,      /* out overlaps q, k or v */
+  BB_ERR_ALIGN = 8       /* a device pointer is not aligned as documented */
+} bb_status;
+
+typedef enum { BB_FP32 = 0, BB_BF16 = 1 } bb_dtype;
+
+/* Flags for bb_attn_forward_ex. */
+#define BB_LAUNCH_FUSED 0u /* one launch: global-row and middle-block work units share a grid */
+#define BB_LAUNCH_SPLIT 1u /* two launches on `stream`: the global-row kernel, then the middle-block kernel */
+
+/* Version of this ABI (BB_ABI_VERSION of the built library). */
+int bb_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* bb_status_str(int status);
+
+/*
+ * Build the per-head random-block table on the host.
+ * Source: page "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的完整实践",
+ * section "随机块掩码是如何生成的": one table per head, one row per middle block,
+ * num_rand_blocks ids drawn from the middle blocks with the row's own window
+ * removed.
+ *
+ *   seed      64-bit seed (the reference layer uses the layer index).
+ *   H, L      heads and sequence length; block divides L; nb = L/block >= 3.
+ *   r         random blocks per middle row; 0 <= r <= max(0, nb-5).
+ *   rand_idx  HOST buffer of H*(nb-2)*r int32, caller-allocated, written as
+ *             [H][nb-2][r]; row i-1 belongs to middle block i.
+ * Each row is a uniform r-subset of {1..nb-2} \ {i-1, i, i+1}, stored in
+ * ascending order.  Draws: SplitMix64 (Steele, Lea & Flood 2014), one stream
+ * per head seeded from (seed, h); bounded integers by Lemire's (2019)
+ * multiply-shift method with rejection; partial Fisher-Yates shuffle.  The
+ * same arguments give the same bytes on every machine.
+ * Errors: BB_ERR_SHAPE (sizes), BB_ERR_NULL (rand_idx NULL while H*(nb-2)*r > 0).
+ */
+int bb_rand_idx_build(uint64_t seed, int H, int L, int block, int r, int32_t* rand_idx);
+
+/*
+ * Validate a HOST random-block table [H][nb-2][r]: every entry in 1..nb-2,
+ * outside {i-1, i, i+1} for its middle block i, no repeat within a row.  Row
+ * order is free.  Returns BB_OK, BB_ERR_RAND_IDX, BB_ERR_SHAPE or BB_ERR_NULL.
+ */
+int bb_rand_idx_check(const int32_t* rand_idx, int H, int L, int block, int r);
+
+/*
+ * Bytes of device workspace bb_attn_forward needs for these sizes (split-K
+ * partial results of the two global query blocks plus per-(b, h, block)
+ * arrival counters).  0 for empty inputs.  Returns 0 also for unsupported
+ * sizes (bb_attn_forward then reports BB_ERR_SHAPE).
+ */
+size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block);
+
+/*
+ * BigBird block-sparse self-attention forward.
+ *
+ *   q, k, v    DEVICE [B][H][L][d] in `dtype` (bf16 or fp32), 16-byte aligned.
+ *   pad_mask   DEVICE uint8 [B][L], nonzero = real token, 0 = padding (the key
+ *              gets -10000 added to its logit), 8-byte aligned; or NULL for
+ *              no padding.  Only the key side is masked; padded query rows are
+ *              computed by the same rule.
+ *   rand_idx   DEVICE int32 [H][nb-2][r]; validate it with bb_rand_idx_check
+ *              first (the kernels clamp entries into 1..nb-2 so a bad table
+ *              cannot read out of bounds, but its result is then undefined).
+ *              May be NULL when r == 0.
+ *   B, H, L    batch, heads, sequence length (B == 0 or H == 0: no-op, BB_OK).
+ *   d          head dimension; must be 64.
+ *   block      block size; 64 or 128; L % block == 0; nb = L/block >= 3.
+ *   r          random blocks per middle row, 0 <= r <= min(16, max(0, nb-5)).
+ *   out        DEVICE [B][H][L][d] in `dtype`, 16-byte aligned, fully
+ *              overwritten; must not overlap q, k or v.
+ *   dtype      BB_BF16 (fp32 accumulation, bf16 output rounded to nearest
+ *              even) or BB_FP32.
+ *   workspace  DEVICE buffer of at least bb_attn_workspace_bytes(...) bytes,
+ *              256-byte aligned.  It must be zero-filled before its first use;
+ *              every completed call leaves it zero-ready for the next one.
+ *              Calls that run concurrently need distinct workspaces.
+ *   stream     hipStream_t to enqueue on (NULL = the null stream).
+ * The call is asynchronous: results are valid once `stream` has been
+ * synchronised.  Launch errors map to BB_ERR_HIP.
+ */
+int bb_attn_forward(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                    const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                    void* out, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* bb_attn_forward with launch flags (BB_LAUNCH_FUSED or BB_LAUNCH_SPLIT);
+ * both give the same result bit for bit.  Unknown flags: BB_ERR_SHAPE. */
+int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                       const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                       void* out, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream, unsigned flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BB_ATTN_H_ */

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (max |gpu - oracle| over the compared outputs, padded query rows
+included): 1e-5 for fp32 inputs, 2e-2 for bf16 inputs with fp32 accumulation.
+Small shapes are compared on every output; the full benchmark shapes on every
+output of sampled (batch, head) units and query blocks (all global rows, the
+edge middle blocks, interior blocks, blocks in the padded region), plus a
+NaN scan of the whole output (the output buffer is NaN-poisoned first).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_bigbird_amd import binding as bb
+from block_sparse_long_bigbird_amd.workloads import STRESS_LONG, WORKLOADS, make_inputs, small
+from oracle import attention_forward, attention_rows, block_adjacency
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    bb.lib()  # fail loudly if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def poisoned_workspace(w, dev):
+    """Workspace whose counters are zero and whose partial-result area is NaN."""
+    n = bb.bb_attn_workspace_bytes(w.B, w.H, w.L, w.d, w.block)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
+    ctr_bytes = -(-(w.B * w.H * 2 * 4) // 256) * 256
+    ws[:ctr_bytes] = 0
+    return ws
+
+
+def run_gpu(w, dev, flags=bb.BB_LAUNCH_FUSED, inputs=None, ws=None):
+    q, k, v, pad = inputs if inputs is not None else make_inputs(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    dpad = None if pad is None else pad.to(dev)
+    dri = torch.from_numpy(ri).to(dev) if w.r > 0 else None
+    out = torch.full_like(dq, float("nan"))
+    if ws is None:
+        ws = poisoned_workspace(w, dev)
+    say(f"  launch {w.name} B={w.B} H={w.H} L={w.L} block={w.block} r={w.r} {w.dtype} flags={flags}")
+    bb.bb_attn_forward(dq, dk, dv, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws, flags=flags)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), (q, k, v, pad), ri
+
+
+def f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def compare_full(w, got, inputs, ri):
+    q, k, v, pad = inputs
+    exp = attention_forward(f64(q), f64(k), f64(v), None if pad is None else pad.numpy(), ri, w.block)
+    assert not np.isnan(got).any(), "unwritten (NaN) outputs"
+    err = np.abs(got - exp)
+    nb = w.nb
+    glob = np.zeros(w.L, dtype=bool)
+    glob[: w.block] = True
+    glob[(nb - 1) * w.block:] = True
+    say(f"  max err global rows {err[:, :, glob].max():.3e}  middle rows "
+        f"{err[:, :, ~glob].max() if (~glob).any() else 0:.3e}")
+    assert err.max() <= TOL[w.dtype], err.max()
+
+
+def sampled_rows(w, pad):
+    nb = w.nb
+    blocks = {0, 1, 2, nb // 2, nb - 3, nb - 2, nb - 1}
+    if pad is not None:                      # a block in the padded region, and the boundary
+        for b in range(w.B):
+            valid = int(pad[b].sum())
+            blocks.add(min(nb - 2, valid // w.block))
+            blocks.add(max(1, min(nb - 2, valid // w.block + 3)))
+    blocks = sorted(x for x in blocks if 0 <= x < nb)
+    return np.concatenate([np.arange(x * w.block, (x + 1) * w.block) for x in blocks])
+
+
+def compare_sampled(w, got, inputs, ri, units):
+    q, k, v, pad = inputs
+    assert not np.isnan(got).any(), "unwritten (NaN) outputs"
+    rows = sampled_rows(w, None if pad is None else pad.numpy())
+    worst = 0.0
+    for b, h in units:
+        adj = block_adjacency(ri[h], w.nb)
+        pb = None if pad is None else pad[b].numpy()
+        exp = attention_rows(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), pb, adj, w.block, rows)
+        err = np.abs(got[b, h, rows] - exp).max()
+        worst = max(worst, err)
+    say(f"  max err over {len(units)} units x {len(rows)} rows: {worst:.3e}")
+    assert worst <= TOL[w.dtype], worst
+
+
+# ------------------------------------------------------------ small shapes ---
+
+SMALL = [
+    small("nb3_dense", B=2, H=3, L=3 * 64, block=64, r=0, data_seed=11),
+    small("nb4_dense", B=1, H=2, L=4 * 64, block=64, r=0, data_seed=12),
+    small("nb5", B=2, H=2, L=5 * 64, block=64, r=0, data_seed=13),
+    small("nb6_r1", B=1, H=3, L=6 * 64, block=64, r=1, data_seed=14),
+    small("nb9_r4_two_chunks", B=2, H=2, L=9 * 64, block=64, r=4, data_seed=15),
+    small("nb17_r3_ragged_chunk", B=1, H=2, L=17 * 64, block=64, r=3, data_seed=16),
+    small("nb12_r3_pad", B=3, H=2, L=12 * 64, block=64, r=3, pad="per_seq_blocks",
+          pad_lo_blocks=4, pad_hi_blocks=12, data_seed=17),
+    small("nb10_r2_pad_ragged", B=1, H=2, L=10 * 64, block=64, r=2, pad="fixed",
+          valid_len=10 * 64 - 37, data_seed=18),
+    small("nb20_r5_scale_small", B=1, H=2, L=20 * 64, block=64, r=5, value_scale=0.125, data_seed=19),
+    small("bs128_nb3", B=1, H=2, L=3 * 128, block=128, r=0, data_seed=20),
+    small("bs128_nb6_r1", B=2, H=1, L=6 * 128, block=128, r=1, data_seed=21),
+    small("bs128_nb11_r4_pad", B=1, H=2, L=11 * 128, block=128, r=4, pad="fixed",
+          valid_len=11 * 128 - 200, data_seed=22),
+    small("fp32_nb3", B=1, H=2, L=3 * 64, block=64, r=0, dtype="fp32", data_seed=23),
+    small("fp32_nb9_r3_pad", B=2, H=2, L=9 * 64, block=64, r=3, dtype="fp32", pad="fixed",
+          valid_len=9 * 64 - 70, data_seed=24),
+    small("fp32_bs128_nb7_r2", B=1, H=2, L=7 * 128, block=128, r=2, dtype="fp32", data_seed=25),
+    small("outliers_unscaled", B=1, H=2, L=16 * 64, block=64, r=3, outlier_frac=0.02,
+          outlier_mult=8.0, data_seed=26),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_shapes_full_parity(dev, w):
+    say(f"case {w.name}")
+    got, inputs, ri = run_gpu(w, dev)
+    compare_full(w, got, inputs, ri)
+
+
+@pytest.mark.parametrize("w", [SMALL[5], SMALL[6], SMALL[11], SMALL[14]],
+                         ids=lambda w: w.name)
+def test_split_launch_matches_fused_bitwise(dev, w):
+    say(f"case split-vs-fused {w.name}")
+    inputs = make_inputs(w)
+    a, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_FUSED, inputs=inputs)
+    b, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_SPLIT, inputs=inputs)
+    assert np.array_equal(a, b)
+
+
+def test_deterministic_and_workspace_reuse(dev):
+    """Same call twice gives identical bits; the workspace is ready for the next call,
+    also for a different, smaller shape."""
+    big = small("reuse_big", B=2, H=3, L=20 * 64, block=64, r=3, pad="fixed", valid_len=1200,
+                data_seed=30)
+    tiny = small("reuse_small", B=1, H=2, L=9 * 64, block=64, r=2, data_seed=31)
+    say("case workspace reuse")
+    ws = poisoned_workspace(big, dev)
+    inputs = make_inputs(big)
+    a, _, ri = run_gpu(big, dev, inputs=inputs, ws=ws)
+    b, _, _ = run_gpu(big, dev, inputs=inputs, ws=ws)
+    assert np.array_equal(a, b)
+    compare_full(big, a, inputs, ri)
+    c, inputs2, ri2 = run_gpu(tiny, dev, ws=ws)
+    compare_full(tiny, c, inputs2, ri2)
+    d, _, _ = run_gpu(big, dev, inputs=inputs, ws=ws)
+    assert np.array_equal(a, d)
+
+
+# ----------------------------------------------------- full benchmark shapes ---
+
+def test_fp32_L1024_full(dev):
+    w = WORKLOADS["fp32_B1_H2_L1024"]
+    say(f"case {w.name}")
+    got, inputs, ri = run_gpu(w, dev)
+    compare_full(w, got, inputs, ri)
+
+
+@pytest.mark.parametrize("name,units", [
+    ("base_B4_H12_L4096_pad", [(0, 0), (1, 5), (2, 7), (3, 11)]),
+    ("large_B8_H16_L4096", [(0, 0), (3, 9), (7, 15)]),
+    ("pathx_B1_H8_L16384_pad", [(0, 0), (0, 7)]),
+    ("long_B1_H12_L32768_bs128", [(0, 0), (0, 11)]),
+])
+def test_full_shape_sampled_parity(dev, name, units):
+    w = WORKLOADS[name]
+    say(f"case {w.name}")
+    got, inputs, ri = run_gpu(w, dev)
+    compare_sampled(w, got, inputs, ri, units)
+
+
+def test_stress_unscaled_outliers(dev):
+    """32K tokens, block 128, unscaled values with x8 key outliers: the running max moves."""
+    w = STRESS_LONG
+    say(f"case {w.name}")
+    got, inputs, ri = run_gpu(w, dev)
+    compare_sampled(w, got, inputs, ri, [(0, 3)])
+
+
+# --------------------------------------------------------------- error paths ---
+
+def test_errors_raise_before_launch(dev):
+    w = SMALL[4]
+    q, k, v, _ = make_inputs(w)
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(dq)
+    ri = torch.from_numpy(bb.bb_rand_idx_build(0, w.H, w.L, w.block, w.r)).to(dev)
+    ws = bb.alloc_workspace(w.B, w.H, w.L, w.d, w.block, dev)
+    with pytest.raises(bb.BBError, match="BB_ERR_WORKSPACE"):
+        bb.bb_attn_forward(dq, dk, dv, None, ri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws[:64])
+    with pytest.raises(bb.BBError, match="BB_ERR_SHAPE"):
+        bb.bb_attn_forward(dq, dk, dv, None, ri, w.B, w.H, w.L, w.d, w.block, w.L // 64, out, ws)
+    with pytest.raises(bb.BBError, match="BB_ERR_ALIAS"):
+        bb.bb_attn_forward(dq, dk, dv, None, ri, w.B, w.H, w.L, w.d, w.block, w.r, dq, ws)
+    with pytest.raises(bb.BBError, match="BB_ERR_DTYPE"):
+        bb.bb_attn_forward(dq.half(), dk.half(), dv.half(), None, ri, w.B, w.H, w.L, w.d, w.block,
+                           w.r, out.half(), ws)
+    torch.cuda.synchronize()

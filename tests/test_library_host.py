@@ -1,0 +1,206 @@
+"""Host-side tests of libbb_attn.so (no GPU needed).
+
+- the library loads and exports every function include/bb_attn.h declares;
+- the seeded random-block builder: exact constraints (checked by the oracle's
+  independent checker), canonical ascending rows, determinism, uniformity
+  against the closed form r/|C(i)|, independence across heads;
+- the C checker agrees with the oracle's checker on valid and corrupted tables;
+- bb_attn_forward's argument validation: every error path returns its code
+  before any HIP call (fake, never-dereferenced pointers are enough).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from block_sparse_long_bigbird_amd import binding as bb
+from block_sparse_long_bigbird_amd.workloads import WORKLOADS
+from oracle import check_rand_idx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bb_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bb.LIB_PATH):
+        from block_sparse_long_bigbird_amd.build import build
+        build()
+    return bb.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(bb_\w+)\s*\(", text, flags=re.M))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert declared == set(bb.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert bb.bb_abi_version() == 1
+    for s in range(0, 9):
+        assert len(bb.bb_status_str(s)) > 0
+    assert bb.bb_status_str(12345) == "unknown status"
+
+
+# ------------------------------------------------------------- the builder ---
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_builder_tables_satisfy_oracle_constraints(lib, name):
+    w = WORKLOADS[name]
+    t = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    assert t.shape == (w.H, w.nb - 2, w.r) and t.dtype == np.int32
+    check_rand_idx(t, w.H, w.L, w.block, w.r)          # independent checker
+    assert bb.bb_rand_idx_check(t, w.H, w.L, w.block, w.r) == bb.BB_OK
+    assert (np.diff(t, axis=2) > 0).all()               # canonical: ascending rows
+
+
+def test_builder_edge_sizes(lib):
+    for nb, r in [(3, 0), (4, 0), (5, 0), (6, 1), (7, 2), (9, 4), (40, 35)]:
+        for block in (1, 64):
+            t = bb.bb_rand_idx_build(7, 3, nb * block, block, r)
+            check_rand_idx(t, 3, nb * block, block, r)
+            if r == nb - 5 and r > 0:
+                # interior rows have exactly r candidates: the row is forced
+                for i in range(2, nb - 2):
+                    exp = [j for j in range(1, nb - 1) if j not in (i - 1, i, i + 1)]
+                    assert t[0, i - 1].tolist() == exp
+    with pytest.raises(bb.BBError):
+        bb.bb_rand_idx_build(0, 1, 6 * 64, 64, 2)       # r > nb-5
+    with pytest.raises(bb.BBError):
+        bb.bb_rand_idx_build(0, 1, 2 * 64, 64, 0)       # nb < 3
+    with pytest.raises(bb.BBError):
+        bb.bb_rand_idx_build(0, 1, 100, 64, 0)          # L % block != 0
+
+
+def test_builder_is_deterministic(lib):
+    a = bb.bb_rand_idx_build(12345, 12, 4096, 64, 3)
+    b = bb.bb_rand_idx_build(12345, 12, 4096, 64, 3)
+    c = bb.bb_rand_idx_build(12346, 12, 4096, 64, 3)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, c)
+    assert not np.array_equal(a[0], a[1])               # heads draw different tables
+
+
+def test_builder_uniform_subsets(lib):
+    """Each candidate j of row i appears with frequency r/|C(i)| (chi-square)."""
+    nb, r, H, seeds = 16, 3, 4, 2500
+    counts = np.zeros((nb - 2, nb), dtype=np.int64)
+    for s in range(seeds):
+        t = bb.bb_rand_idx_build(s * 7919 + 1, H, nb, 1, r)
+        for h in range(H):
+            for row in range(nb - 2):
+                counts[row, t[h, row]] += 1
+    n = seeds * H
+    for row in range(nb - 2):
+        i = row + 1
+        cand = [j for j in range(1, nb - 1) if j not in (i - 1, i, i + 1)]
+        assert counts[row].sum() == n * r
+        assert counts[row, [j for j in range(nb) if j not in cand]].sum() == 0
+        obs = counts[row, cand]
+        exp = np.full(len(cand), n * r / len(cand))
+        p = stats.chisquare(obs, exp).pvalue
+        assert p > 1e-3, (row, obs, p)
+
+
+def test_builder_heads_independent(lib):
+    """Joint inclusion of (head0 picks x, head1 picks y) factorises (chi-square)."""
+    nb, r, seeds, row = 12, 2, 4000, 4          # row 4 = middle block 5
+    i = row + 1
+    cand = [j for j in range(1, nb - 1) if j not in (i - 1, i, i + 1)]
+    joint = np.zeros((len(cand), len(cand)), dtype=np.int64)
+    pos = {c: n for n, c in enumerate(cand)}
+    for s in range(seeds):
+        t = bb.bb_rand_idx_build(s, 2, nb, 1, r)
+        a = min(t[0, row]); b = min(t[1, row])      # smallest pick of each head
+        joint[pos[a], pos[b]] += 1
+    nz = joint[joint.sum(axis=1) > 0][:, joint.sum(axis=0) > 0]
+    p = stats.chi2_contingency(nz).pvalue
+    assert p > 1e-3
+
+
+# -------------------------------------------------------- the C checker ---
+
+def test_c_checker_matches_oracle_checker(lib):
+    rng = np.random.default_rng(3)
+    H, nb, r, block = 3, 14, 4, 2
+    L = nb * block
+    base = bb.bb_rand_idx_build(99, H, L, block, r)
+    for trial in range(400):
+        t = base.copy()
+        for _ in range(rng.integers(1, 3)):
+            h, row, c = rng.integers(H), rng.integers(nb - 2), rng.integers(r)
+            t[h, row, c] = rng.integers(-2, nb + 2)
+        try:
+            check_rand_idx(t, H, L, block, r)
+            ok = True
+        except ValueError:
+            ok = False
+        st = bb.bb_rand_idx_check(t, H, L, block, r)
+        assert (st == bb.BB_OK) == ok, (trial, st)
+        if not ok:
+            assert st == 4   # BB_ERR_RAND_IDX
+    assert bb.bb_rand_idx_check(base, H, L + 1, block, r) == 2     # shape error
+    assert lib.bb_rand_idx_check(None, H, L, block, r) == 1        # NULL table
+
+
+# ------------------------------------------- forward argument validation ---
+
+FAKE = 1 << 20          # 16-byte aligned fake device addresses, never dereferenced
+
+
+def fwd(lib, q=FAKE, k=2 * FAKE, v=3 * FAKE, pad=None, rand=4 * FAKE, B=2, H=3, L=1024, d=64,
+        block=64, r=3, out=5 * FAKE, dtype=1, ws=6 * FAKE, ws_bytes=1 << 30, flags=0):
+    P = ctypes.c_void_p
+    return lib.bb_attn_forward_ex(P(q), P(k), P(v), P(pad), P(rand), B, H, L, d, block, r, P(out),
+                                  dtype, P(ws), ws_bytes, None, flags)
+
+
+def test_forward_validation_errors(lib):
+    assert fwd(lib, dtype=7) == 3                       # BB_ERR_DTYPE
+    assert fwd(lib, flags=5) == 2                       # unknown flags
+    assert fwd(lib, d=128) == 2
+    assert fwd(lib, block=32) == 2
+    assert fwd(lib, L=1000) == 2                        # L % block
+    assert fwd(lib, L=128) == 2                         # nb < 3
+    assert fwd(lib, r=12) == 2                          # r > nb-5 (nb = 16)
+    assert fwd(lib, L=64 * 40, r=17) == 2               # r above the kernel's limit
+    assert fwd(lib, B=-1) == 2
+    assert fwd(lib, q=0) == 1                           # BB_ERR_NULL
+    assert fwd(lib, out=0) == 1
+    assert fwd(lib, ws=0) == 1
+    assert fwd(lib, rand=0) == 1                        # r > 0 needs a table
+    assert fwd(lib, q=FAKE + 4) == 8                    # BB_ERR_ALIGN
+    assert fwd(lib, pad=FAKE * 7 + 2) == 8
+    assert fwd(lib, ws=6 * FAKE + 64) == 8
+    assert fwd(lib, out=FAKE) == 7                      # BB_ERR_ALIAS (out == q)
+    assert fwd(lib, out=2 * FAKE + 4096) == 7           # out starts inside k
+    need = lib.bb_attn_workspace_bytes(2, 3, 1024, 64, 64)
+    assert need > 0
+    assert fwd(lib, ws_bytes=need - 1) == 5             # BB_ERR_WORKSPACE
+
+
+def test_forward_empty_is_noop(lib):
+    """B == 0 or H == 0: nothing to do, BB_OK without touching any pointer."""
+    assert fwd(lib, B=0, q=0, k=0, v=0, out=0, ws=0, rand=0) == 0
+    assert fwd(lib, H=0, q=0, k=0, v=0, out=0, ws=0, rand=0) == 0
+    assert lib.bb_attn_workspace_bytes(0, 12, 4096, 64, 64) == 0
+
+
+def test_workspace_size_formula(lib):
+    for B, H, L, block in [(4, 12, 4096, 64), (1, 12, 32768, 128), (1, 2, 192, 64)]:
+        nb = L // block
+        n_s = -(-nb // 8)
+        units = B * H * 2
+        def a256(x):
+            return (x + 255) // 256 * 256
+        exp = a256(units * 4) + 2 * a256(units * n_s * block * 4) + units * n_s * block * 64 * 4
+        assert lib.bb_attn_workspace_bytes(B, H, L, 64, block) == exp
+    assert lib.bb_attn_workspace_bytes(1, 1, 1000, 64, 64) == 0   # unsupported -> 0
