@@ -118,10 +118,10 @@ def _stream_handle(t, stream):
 
 
 def alloc_workspace(B: int, H: int, L: int, d: int, block: int, device):
-    """Zero-filled device workspace of the size the library asks for."""
+    """Device workspace of the size the library asks for (contents need no initialisation)."""
     import torch
     n = bb_attn_workspace_bytes(B, H, L, d, block)
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def _check_device_tensor(name, t):

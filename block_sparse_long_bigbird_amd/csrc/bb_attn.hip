@@ -14,8 +14,9 @@
 //     (5 + r tiles, 4 + r at i = 1 and i = nb-2), finalised in place;
 //   - global unit: query block 0 or nb-1 against a chunk of kChunkTiles
 //     consecutive key tiles (split-K over L); it writes an unnormalised
-//     partial (row max, row sum, O) and the last unit of its block to arrive
-//     merges all partials in fixed chunk order (deterministic).
+//     partial (row max, row sum, O) to the workspace.  A small merge kernel,
+//     launched next on the same stream, combines the partials of each global
+//     block in fixed chunk order (deterministic).
 // The paper packs the attended blocks into dense tensors (rolled key copies,
 // gathered random blocks) for TPU matrix units; here each attended block is
 // one contiguous BS x 64 slab of K and of V that a workgroup copies from HBM
@@ -62,29 +63,28 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
 template <typename T, int BS>
 struct Cfg {
   static constexpr int ES = sizeof(T);
-  static constexpr int EPC = 16 / ES;           // elements per 16-byte chunk
-  static constexpr int CPR_K = kD * ES / 16;    // chunks per K row in LDS (and per Q/V row)
-  static constexpr int CPR_V = BS * ES / 16;    // chunks per V^T row in LDS
-  static constexpr int WQ = BS / 32;            // query groups
-  static constexpr int WK = 2;                  // key halves
-  static constexpr int NW = WQ * WK;            // waves per workgroup
-  static constexpr int NT = 64 * NW;            // threads per workgroup
-  static constexpr int NSUB = BS / (32 * WK);   // 32-key subtiles per wave per tile
-  static constexpr int K_BYTES = BS * kD * ES;
-  static constexpr int STAGE = 2 * K_BYTES;     // K tile + V^T tile
-  static constexpr int K_TASKS = BS * CPR_K / NT;        // K chunks per thread per tile
-  static constexpr int V_TASKS = (BS / 2) * CPR_K / NT;  // V row-pair chunks per thread
-  static constexpr int QC = CPR_K / 2;          // Q chunks per lane
-  static constexpr int MERGE_BYTES = WQ * 34 * 64 * 4;
-  static constexpr int SMEM = (2 * STAGE > MERGE_BYTES ? 2 * STAGE : MERGE_BYTES);
-  static_assert(K_TASKS * NT == BS * CPR_K, "K staging must tile evenly");
-  static_assert(V_TASKS * NT == (BS / 2) * CPR_K, "V staging must tile evenly");
-  static_assert(NSUB >= 1, "at least one subtile per wave");
-  static_assert(CPR_V % 8 == 0 && CPR_K % 8 == 0, "swizzle needs 8-chunk groups");
+  static constexpr int ROWB = kD * ES;              // bytes per K/V row
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int WQ = BS / 32;                // query groups (32 rows each)
+  static constexpr int WK = 2;                      // key halves
+  static constexpr int NW = WQ * WK;                // waves per workgroup
+  static constexpr int NT = 64 * NW;                // threads per workgroup
+  static constexpr int NSUB = BS / (32 * WK);       // 32-key subtiles per wave per tile
+  static constexpr int TILE = BS * ROWB;            // bytes of one K (or V) tile
+  static constexpr int NSTAGE = 6 * TILE <= 96 * 1024 ? 3 : 2;  // LDS ring depth
+  static constexpr int DMA_MAT = BS * CPR / 64 / NW;  // DMA instructions per wave per matrix
+  static constexpr int QC = CPR / 2;                // Q chunks per lane
+  static_assert(DMA_MAT * 64 * NW == BS * CPR, "tile DMA must split evenly over waves");
+  static_assert(CPR % 8 == 0, "swizzles act on groups of 8 chunks");
+  static_assert(WQ * 16 * 64 * 4 <= TILE, "merge area must fit in one stage matrix");
 };
 
 struct Args {
@@ -94,17 +94,32 @@ struct Args {
   const uint8_t* pad;
   const int32_t* rand_idx;
   char* out;
-  uint32_t* ctr;   // [B*H][2] arrival counters
   float* pm;       // [B*H][2][n_s][BS] partial row max (q.k units)
   float* pl;       // [B*H][2][n_s][BS] partial row sum
   float* po;       // [B*H][2][n_s][BS][kD] partial unnormalised output
   int H, L, nb, r, n_s;
 };
 
-// 16-byte LDS chunk swizzle.  A wave reads rows perm_row(0..31) (+ a multiple
-// of 32) at one logical chunk; the 8 lanes served together hit rows
-// {R..R+3, R+8..R+11}, which this XOR spreads over 8 distinct chunk slots.
-__device__ __forceinline__ int swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// LDS ring: one object per (dtype, block, stage) holding that stage's K and V
+// tiles.  Distinct objects let the compiler tell a read of one stage from a
+// DMA still in flight into another (it tracks only a few DMA targets).
+template <typename T, int BS, int S>
+struct Stage {
+  static __device__ __forceinline__ char* buf() {
+    __shared__ __attribute__((aligned(1024))) char b[2 * Cfg<T, BS>::TILE];
+    return b;
+  }
+  static __device__ __forceinline__ char* k() { return buf(); }
+  static __device__ __forceinline__ char* v() { return buf() + Cfg<T, BS>::TILE; }
+};
+
+// 16-byte chunk swizzles (physical chunk = logical chunk ^ swz(row)).
+// K: a score-MFMA operand read hits rows perm_row(0..7) = {R..R+3, R+8..R+11}
+//    in one 8-lane phase; this XOR gives them 8 distinct chunk slots.
+// V: a transposing read hits 4 consecutive rows x 4 dim quads per 16 lanes;
+//    XOR with 2*(row%4) gives the 16 lanes 16 distinct 8-byte slots.
+__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
 
 // MFMA row i (0..31) -> key / dim offset inside a 32-wide subtile, chosen so
 // that accumulator register v of lane group g holds offset
@@ -126,79 +141,52 @@ __device__ __forceinline__ bool has_zero_byte(uint64_t x) {
   return ((x - 0x0101010101010101ull) & ~x & 0x8080808080808080ull) != 0;
 }
 
-template <typename T, int BS>
-struct StageRegs {
-  u32x4 k[Cfg<T, BS>::K_TASKS];
-  u32x4 v0[Cfg<T, BS>::V_TASKS];
-  u32x4 v1[Cfg<T, BS>::V_TASKS];
-  u32x4 pad;
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS ring.  The LDS reads of the previous step
+// were consumed by MFMAs before this point; DMA writes into a stage are
+// ordered by the explicit vmcnt waits.  No memory fence: a fence would drain
+// the DMA prefetches that are meant to stay in flight.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy key tile `tile` of K and V from HBM straight into LDS stage S.  Each DMA instruction moves 64 x 16 bytes; lane l of
+// instruction i fills physical chunk slot 64*i + l, so it fetches the logical
+// chunk that the swizzle places there.  Rows stay contiguous 128-byte runs.
+template <typename T, int BS, int S>
+__device__ __forceinline__ void issue_tile(const char* kbh, const char* vbh, int tile, int wave,
+                                           int lane) {
+  using C = Cfg<T, BS>;
+  const char* kt = kbh + static_cast<size_t>(tile) * C::TILE;
+  const char* vt = vbh + static_cast<size_t>(tile) * C::TILE;
+#pragma unroll
+  for (int jj = 0; jj < C::DMA_MAT; ++jj) {
+    const int ins = wave + C::NW * jj;
+    const int slot = ins * 64 + lane;
+    const int row = slot / C::CPR, p = slot % C::CPR;
+    __builtin_amdgcn_global_load_lds(
+        (const glb_void_t*)(kt + row * C::ROWB + ((p ^ swz_k(row)) << 4)),
+        (lds_void_t*)(Stage<T, BS, S>::k() + ins * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        (const glb_void_t*)(vt + row * C::ROWB + ((p ^ swz_v(row)) << 4)),
+        (lds_void_t*)(Stage<T, BS, S>::v() + ins * 1024), 16, 0, 0);
+  }
+}
+
+// Per-wave online-softmax state for 32 query rows (one per lane pair).
+struct WaveState {
+  f32x16 o[2];   // O^T, dims [0,32) and [32,64)
+  float m;       // running row max in q.k units (may lag the true max by < tau/scale)
+  float l;       // this lane's part of the row sum
 };
-
-// Global -> registers for key tile `tile` of (b, h).
-template <typename T, int BS>
-__device__ __forceinline__ void load_tile(StageRegs<T, BS>& st, const char* kbh, const char* vbh,
-                                          const uint8_t* pad_b, int tile, int tid) {
-  using C = Cfg<T, BS>;
-  constexpr int ROWB = kD * C::ES;
-  const char* kt = kbh + static_cast<size_t>(tile) * BS * ROWB;
-  const char* vt = vbh + static_cast<size_t>(tile) * BS * ROWB;
-#pragma unroll
-  for (int t = 0; t < C::K_TASKS; ++t) {
-    const int task = tid + C::NT * t;
-    const int row = task / C::CPR_K, c = task % C::CPR_K;
-    st.k[t] = *reinterpret_cast<const u32x4*>(kt + row * ROWB + c * 16);
-  }
-#pragma unroll
-  for (int t = 0; t < C::V_TASKS; ++t) {
-    const int task = tid + C::NT * t;
-    const int dc = task % C::CPR_K, kp = task / C::CPR_K;
-    st.v0[t] = *reinterpret_cast<const u32x4*>(vt + (2 * kp) * ROWB + dc * 16);
-    st.v1[t] = *reinterpret_cast<const u32x4*>(vt + (2 * kp + 1) * ROWB + dc * 16);
-  }
-  if (pad_b != nullptr && tid < BS / 16)
-    st.pad = *reinterpret_cast<const u32x4*>(pad_b + static_cast<size_t>(tile) * BS + tid * 16);
-}
-
-// Registers -> LDS stage: K as [key][dim], V transposed as [dim][key].
-template <typename T, int BS>
-__device__ __forceinline__ void store_tile(const StageRegs<T, BS>& st, char* sb, uint8_t* spad,
-                                           bool has_pad, int tid) {
-  using C = Cfg<T, BS>;
-#pragma unroll
-  for (int t = 0; t < C::K_TASKS; ++t) {
-    const int task = tid + C::NT * t;
-    const int row = task / C::CPR_K, c = task % C::CPR_K;
-    *reinterpret_cast<u32x4*>(sb + (row * C::CPR_K + (c ^ swz(row))) * 16) = st.k[t];
-  }
-  char* vt = sb + C::K_BYTES;
-#pragma unroll
-  for (int t = 0; t < C::V_TASKS; ++t) {
-    const int task = tid + C::NT * t;
-    const int dc = task % C::CPR_K, kp = task / C::CPR_K;
-    const int key = 2 * kp;
-    const int ck = key / C::EPC;                 // chunk of the key pair in a V^T row
-    const int off = (key % C::EPC) * C::ES;      // byte offset of the pair in that chunk
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = st.v0[t][w], b = st.v1[t][w];
-        const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo, b.lo)
-        const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi, b.hi)
-        const int d0 = dc * 8 + 2 * w, d1 = d0 + 1;
-        *reinterpret_cast<uint32_t*>(vt + (d0 * C::CPR_V + (ck ^ swz(d0))) * 16 + off) = lo;
-        *reinterpret_cast<uint32_t*>(vt + (d1 * C::CPR_V + (ck ^ swz(d1))) * 16 + off) = hi;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dd = dc * 4 + e;
-        f32x2 pr = {__uint_as_float(st.v0[t][e]), __uint_as_float(st.v1[t][e])};
-        *reinterpret_cast<f32x2*>(vt + (dd * C::CPR_V + (ck ^ swz(dd))) * 16 + off) = pr;
-      }
-    }
-  }
-  if (has_pad && tid < BS / 16) *reinterpret_cast<u32x4*>(spad + tid * 16) = st.pad;
-}
 
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 acc, __bf16*) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -212,27 +200,22 @@ __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 acc, float*) 
   return acc;
 }
 
-// Per-wave online-softmax state for 32 query rows (one per lane pair).
-struct WaveState {
-  f32x16 o[2];   // O^T, dims [0,32) and [32,64)
-  float m;       // running row max in q.k units (may lag the true max by < tau/scale)
-  float l;       // this lane's part of the row sum
-};
-
-// One 32-key subtile: scores, online softmax, PV.
-template <typename T, int BS>
+// One 32-key subtile of stage S: scores, online softmax, PV.
+template <typename T, int BS, int S, bool HAS_PAD>
 __device__ __forceinline__ void subtile(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC],
-                                        const char* sb, const uint8_t* spad, bool has_pad,
-                                        int kbase, int j, int g) {
+                                        const uint8_t* pad_t, int kbase, int lane) {
   using C = Cfg<T, BS>;
+  const int j = lane & 31, g = lane >> 5;
   // ---- S^T = K . Q^T (+ key bias) -------------------------------------------
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  if (has_pad) {
-    const uint64_t w0 = *reinterpret_cast<const uint64_t*>(spad + kbase + 8 * g);
-    const uint64_t w1 = *reinterpret_cast<const uint64_t*>(spad + kbase + 16 + 8 * g);
-    if (__any(has_zero_byte(w0) || has_zero_byte(w1))) {
+  if constexpr (HAS_PAD) {
+    // The 32 pad bytes of this subtile, read with wave-uniform (scalar) loads.
+    const uint64_t* pw = reinterpret_cast<const uint64_t*>(pad_t + kbase);
+    const uint64_t p0 = pw[0], p1 = pw[1], p2 = pw[2], p3 = pw[3];
+    if (has_zero_byte(p0) || has_zero_byte(p1) || has_zero_byte(p2) || has_zero_byte(p3)) {
+      const uint64_t w0 = g ? p1 : p0, w1 = g ? p3 : p2;
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         acc[v] = ((w0 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
@@ -241,20 +224,26 @@ __device__ __forceinline__ void subtile(WaveState& ws, const u32x4 (&qop)[Cfg<T,
     }
   }
   {
+    const char* sk = Stage<T, BS, S>::k();
     const int row = kbase + perm_row(j);
-    const int sw = swz(row);
+    const int sw = swz_k(row);
 #pragma unroll
     for (int x = 0; x < C::QC; ++x) {
-      const int c = 2 * x + g;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(sb + (row * C::CPR_K + (c ^ sw)) * 16);
+      const u32x4 a =
+          *reinterpret_cast<const u32x4*>(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
       acc = mfma_qk(a, qop[x], acc, static_cast<T*>(nullptr));
     }
   }
   // ---- online softmax (lane = query row; 16 of its 32 keys) ----------------
-  float mloc = acc[0];
+  float mloc = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, acc[v]);
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  for (int v = 3; v < 15; v += 2) mloc = fmaxf(fmaxf(mloc, acc[v]), acc[v + 1]);
+  mloc = fmaxf(mloc, acc[15]);
+  {
+    const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc),
+                                                      false, false);
+    mloc = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+  }
   const float m_new = fmaxf(ws.m, mloc);
   if (__any((m_new - ws.m) * kScaleLog2 > kRescaleTau)) {
     const float alpha = __builtin_amdgcn_exp2f((ws.m - m_new) * kScaleLog2);
@@ -268,53 +257,85 @@ __device__ __forceinline__ void subtile(WaveState& ws, const u32x4 (&qop)[Cfg<T,
   }
   const float mc = ws.m * kScaleLog2;
   float p[16];
-  float lsum = 0.0f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-    lsum += p[v];
-  }
-  ws.l += lsum;
+  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
   // ---- O^T += V^T . P^T -------------------------------------------------------
-  const char* vt = sb + C::K_BYTES;
+  const char* sv = Stage<T, BS, S>::v();
   if constexpr (sizeof(T) == 2) {
     bf16x8 pb[2];
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float lsum = ws.l;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         f32x2 pr = {p[8 * h + e], p[8 * h + e + 1]};
-        bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
+        const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, lsum, false);  // row sum of bf16(P)
         pb[h][e] = c2[0];
         pb[h][e + 1] = c2[1];
       }
+    ws.l = lsum;
+    // Transposing LDS reads: lane (dim, g) gets V[key][dim] for 4 consecutive
+    // keys; lanes 4e+m of each 16-lane group address row key0+e at dim quad m.
+    const int e4 = (lane >> 2) & 3;
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh) {
-      const int row = dh * 32 + perm_row(j);
-      const int sw = swz(row);
+      const int dstart = dh * 32 + perm_row(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+      const int dchunk = dstart >> 3, dbyte = (dstart & 7) * 2;
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const int c = kbase / 8 + 2 * mm + g;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vt + (row * C::CPR_V + (c ^ sw)) * 16);
-        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[mm],
-                                                           ws.o[dh], 0, 0, 0);
+        const int r0 = kbase + 16 * mm + 8 * g + e4, r1 = r0 + 4;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sv + r0 * C::ROWB + ((dchunk ^ swz_v(r0)) << 4) + dbyte));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(sv + r1 * C::ROWB + ((dchunk ^ swz_v(r1)) << 4) + dbyte));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mm], ws.o[dh], 0, 0, 0);
       }
     }
   } else {
+    float lsum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) lsum += p[v];
+    ws.l += lsum;
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh) {
-      const int row = dh * 32 + perm_row(j);
-      const int sw = swz(row);
+      const int dim = dh * 32 + perm_row(j);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c = kbase / 4 + 4 * (q4 >> 1) + 2 * g + (q4 & 1);
-        const f32x4 a = *reinterpret_cast<const f32x4*>(vt + (row * C::CPR_V + (c ^ sw)) * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], p[4 * q4 + e], ws.o[dh], 0, 0, 0);
+      for (int v = 0; v < 16; ++v) {
+        const int key = kbase + 16 * (v >> 3) + 8 * g + (v & 7);
+        const float a = *reinterpret_cast<const float*>(
+            sv + key * C::ROWB + (((dim >> 2) ^ swz_v(key)) << 4) + (dim & 3) * 4);
+        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[v], ws.o[dh], 0, 0, 0);
       }
     }
   }
+}
+
+// One step of the tile loop: tile u sits in stage S.
+template <typename T, int BS, int S, bool HAS_PAD>
+__device__ __forceinline__ void step(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC],
+                                     const int* s_tiles, int u, int ntiles, const char* kbh,
+                                     const char* vbh, const uint8_t* pad_b, int wave, int lane,
+                                     int wk) {
+  using C = Cfg<T, BS>;
+  constexpr int NS = C::NSTAGE;
+  constexpr int NDMA = 2 * C::DMA_MAT;
+  const int tile = __builtin_amdgcn_readfirstlane(s_tiles[u]);
+  const uint8_t* pad_t = HAS_PAD ? pad_b + static_cast<size_t>(tile) * BS : nullptr;
+  if (NS == 3 && u + 1 < ntiles)
+    wait_vm<NDMA>();     // tile u landed; tile u+1 may still be in flight
+  else
+    wait_vm<0>();
+  ring_barrier();        // every wave's part of tile u is in LDS; stage u-1 is free
+#pragma unroll
+  for (int s = 0; s < C::NSUB; ++s)
+    subtile<T, BS, S, HAS_PAD>(ws, qop, pad_t, wk * (BS / 2) + 32 * s, lane);
+  if (u + NS - 1 < ntiles)  // refill the stage freed by tile u-1
+    issue_tile<T, BS, (S + NS - 1) % NS>(kbh, vbh, __builtin_amdgcn_readfirstlane(s_tiles[u + NS - 1]),
+                                         wave, lane);
 }
 
 __device__ __forceinline__ void store_row8(char* dst, const float* x, __bf16*) {
@@ -344,20 +365,18 @@ __device__ __forceinline__ void store_f32x4(char* dst, f32x4 x, float*) {
   *reinterpret_cast<f32x4*>(dst) = x;
 }
 
-
 // One work unit on (b, h).  gsel < 0: middle query block qb, finalised in
 // place.  gsel in {0, 1}: global query block qb (0 or nb-1), key chunk
 // `chunk` of split-K; the last chunk to arrive merges all partials.
-template <typename T, int BS>
+template <typename T, int BS, bool HAS_PAD>
 __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, int gsel, int chunk) {
   using C = Cfg<T, BS>;
-  constexpr int ROWB = kD * C::ES;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  __shared__ __attribute__((aligned(16))) uint8_t spad[2][BS];
-  __shared__ int s_tiles[kMaxTiles];
-  __shared__ int s_last;
+  constexpr int ROWB = C::ROWB;
+  constexpr int NS = C::NSTAGE;
+  __shared__ int s_tiles[kMaxTiles + 8];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave % C::WQ, wk = wave / C::WQ;
   const int j = lane & 31, g = lane >> 5;
   const int nb = a.nb, L = a.L;
@@ -365,10 +384,9 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
   const char* qbh = a.q + bh * L * ROWB;
   const char* kbh = a.k + bh * L * ROWB;
   const char* vbh = a.v + bh * L * ROWB;
-  const bool has_pad = a.pad != nullptr;
-  const uint8_t* pad_b = has_pad ? a.pad + static_cast<size_t>(b) * L : nullptr;
+  const uint8_t* pad_b = HAS_PAD ? a.pad + static_cast<size_t>(b) * L : nullptr;
 
-  // ---- key-tile list --------------------------------------------------------
+  // ---- key-tile list (identical in every thread; kept in LDS) ---------------
   int ntiles;
   if (gsel < 0) {
     const int lo = qb - 1 < 1 ? 1 : qb - 1;            // band without the global blocks
@@ -391,8 +409,12 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
     ntiles = nb - t0 < kChunkTiles ? nb - t0 : kChunkTiles;
     if (tid < ntiles) s_tiles[tid] = t0 + tid;
   }
+  __syncthreads();
 
-  // ---- this wave's 32 query rows as the B operand of the score MFMA --------
+  // ---- prologue: first NS-1 tiles in flight, Q into registers ---------------
+  issue_tile<T, BS, 0>(kbh, vbh, __builtin_amdgcn_readfirstlane(s_tiles[0]), wave, lane);
+  if (NS == 3 && ntiles > 1)
+    issue_tile<T, BS, 1 % NS>(kbh, vbh, __builtin_amdgcn_readfirstlane(s_tiles[1]), wave, lane);
   const int q0 = qb * BS + wq * 32;
   u32x4 qop[C::QC];
   {
@@ -400,7 +422,6 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
 #pragma unroll
     for (int x = 0; x < C::QC; ++x) qop[x] = *reinterpret_cast<const u32x4*>(qrow + (2 * x + g) * 16);
   }
-
   WaveState ws;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -410,45 +431,42 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
   ws.m = -__builtin_inff();
   ws.l = 0.0f;
 
-  // ---- double-buffered tile loop ---------------------------------------------
-  __syncthreads();
-  StageRegs<T, BS> st;
-  load_tile<T, BS>(st, kbh, vbh, pad_b, s_tiles[0], tid);
-  store_tile<T, BS>(st, smem, spad[0], has_pad, tid);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < ntiles) load_tile<T, BS>(st, kbh, vbh, pad_b, s_tiles[t + 1], tid);
-    const char* sb = smem + cur * C::STAGE;
-#pragma unroll
-    for (int s = 0; s < C::NSUB; ++s)
-      subtile<T, BS>(ws, qop, sb, spad[cur], has_pad, wk * (BS / 2) + 32 * s, j, g);
-    if (t + 1 < ntiles) store_tile<T, BS>(st, smem + (cur ^ 1) * C::STAGE, spad[cur ^ 1], has_pad, tid);
-    __syncthreads();
+  // ---- tile loop: 9 steps per trip (3 turns of a 3-stage ring, or 4.5 of 2) --
+  // Units of the usual shapes have at most 9 tiles, so the loop back edge --
+  // where the compiler's LDS-DMA wait tracking turns conservative -- is rare.
+  for (int u = 0; u < ntiles; u += 9) {
+#define BB_STEP(k)                                                                              \
+  if (u + (k) < ntiles)                                                                         \
+    step<T, BS, (k) % NS, HAS_PAD>(ws, qop, s_tiles, u + (k), ntiles, kbh, vbh, pad_b, wave, lane, wk);
+    BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5) BB_STEP(6) BB_STEP(7) BB_STEP(8)
+#undef BB_STEP
   }
 
   // ---- merge the two key halves of each query group ------------------------
-  float* mrg = reinterpret_cast<float*>(smem) + wq * 34 * 64;
+  __syncthreads();
+  float* mo0 = reinterpret_cast<float*>(Stage<T, BS, 0>::k()) + wq * 16 * 64;
+  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, 0>::v()) + wq * 16 * 64;
+  float* mml = reinterpret_cast<float*>(Stage<T, BS, 1 % NS>::k()) + wq * 2 * 64;
   if (wk == 1) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      mrg[v * 64 + lane] = ws.o[0][v];
-      mrg[(16 + v) * 64 + lane] = ws.o[1][v];
+      mo0[v * 64 + lane] = ws.o[0][v];
+      mo1[v * 64 + lane] = ws.o[1][v];
     }
-    mrg[32 * 64 + lane] = ws.m;
-    mrg[33 * 64 + lane] = ws.l;
+    mml[lane] = ws.m;
+    mml[64 + lane] = ws.l;
   }
   __syncthreads();
   if (wk == 0) {
-    const float m1 = mrg[32 * 64 + lane], l1 = mrg[33 * 64 + lane];
+    const float m1 = mml[lane], l1 = mml[64 + lane];
     const float mm = fmaxf(ws.m, m1);
     const float a0 = __builtin_amdgcn_exp2f((ws.m - mm) * kScaleLog2);
     const float a1 = __builtin_amdgcn_exp2f((m1 - mm) * kScaleLog2);
     float o[2][16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      o[0][v] = ws.o[0][v] * a0 + mrg[v * 64 + lane] * a1;
-      o[1][v] = ws.o[1][v] * a0 + mrg[(16 + v) * 64 + lane] * a1;
+      o[0][v] = ws.o[0][v] * a0 + mo0[v * 64 + lane] * a1;
+      o[1][v] = ws.o[1][v] * a0 + mo1[v * 64 + lane] * a1;
     }
     float l = ws.l * a0 + l1 * a1;
     l += __shfl_xor(l, 32);
@@ -478,21 +496,20 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
       }
     }
   }
-  if (gsel < 0) return;
+}
 
-  // ---- split-K: the last chunk of this global block merges all partials -----
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.ctr + bh * 2 + gsel, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == static_cast<unsigned>(a.n_s - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const size_t base = (bh * 2 + gsel) * a.n_s;
-  for (int idx = tid; idx < BS * kD / 4; idx += C::NT) {
+// Split-K merge of the two global query blocks of one (b, h): the partials of
+// the n_s key chunks (row max m_s, row sum l_s, unnormalised O_s) combine as
+// out = sum_s 2^((m_s - m)c) O_s / sum_s 2^((m_s - m)c) l_s, m = max_s m_s,
+// summed in chunk order.  Runs as its own launch after the global-row units,
+// so their partials are complete and visible without any in-kernel fence.
+template <typename T, int BS>
+__global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
+  constexpr int ROWB = kD * sizeof(T);
+  const int bh = blockIdx.x >> 1, gsel = blockIdx.x & 1;
+  const int qb = gsel ? a.nb - 1 : 0;
+  const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.n_s;
+  for (int idx = threadIdx.x; idx < BS * kD / 4; idx += 256) {
     const int ql = idx / (kD / 4), dq = idx % (kD / 4);
     float mx = -__builtin_inff();
     for (int s = 0; s < a.n_s; ++s) mx = fmaxf(mx, a.pm[(base + s) * BS + ql]);
@@ -506,16 +523,16 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
       num += w * po;
     }
     const float inv = 1.0f / den;
-    store_f32x4(a.out + (bh * L + static_cast<size_t>(qb) * BS + ql) * ROWB + dq * 4 * C::ES,
+    store_f32x4(a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + ql) * ROWB +
+                    dq * 4 * sizeof(T),
                 num * inv, static_cast<T*>(nullptr));
   }
-  if (tid == 0) __hip_atomic_store(a.ctr + bh * 2 + gsel, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Decode a work unit.  Per (b, h): 2*n_s global units (block 0 chunks, then
 // block nb-1 chunks) followed by nb-2 middle units.  kind selects which of
 // them this grid covers: 0 = all, 1 = global units only, 2 = middle only.
-template <typename T, int BS, int kind>
+template <typename T, int BS, int kind, bool HAS_PAD>
 __device__ __forceinline__ void dispatch(const Args& a) {
   const int n_g = kind == 2 ? 0 : 2 * a.n_s;
   const int n_m = kind == 1 ? 0 : a.nb - 2;
@@ -533,20 +550,20 @@ __device__ __forceinline__ void dispatch(const Args& a) {
     chunk = 0;
     qb = u - n_g + 1;
   }
-  run_unit<T, BS>(a, b, h, qb, gsel, chunk);
+  run_unit<T, BS, HAS_PAD>(a, b, h, qb, gsel, chunk);
 }
 
-template <typename T, int BS>
+template <typename T, int BS, bool HAS_PAD>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_fused_kernel(Args a) {
-  dispatch<T, BS, 0>(a);
+  dispatch<T, BS, 0, HAS_PAD>(a);
 }
-template <typename T, int BS>
+template <typename T, int BS, bool HAS_PAD>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_global_rows_kernel(Args a) {
-  dispatch<T, BS, 1>(a);
+  dispatch<T, BS, 1, HAS_PAD>(a);
 }
-template <typename T, int BS>
+template <typename T, int BS, bool HAS_PAD>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_middle_rows_kernel(Args a) {
-  dispatch<T, BS, 2>(a);
+  dispatch<T, BS, 2, HAS_PAD>(a);
 }
 
 // ---------------------------------------------------------------- host side --
@@ -554,15 +571,14 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_middle_rows_kernel(Args a
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-  size_t ctr, pm, pl, po, total;
+  size_t pm, pl, po, total;
 };
 
 Layout workspace_layout(int B, int H, int nb, int block) {
   const size_t n_s = static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
   const size_t units = static_cast<size_t>(B) * H * 2;
   Layout w;
-  w.ctr = 0;
-  w.pm = align256(units * sizeof(uint32_t));
+  w.pm = 0;
   w.pl = w.pm + align256(units * n_s * block * sizeof(float));
   w.po = w.pl + align256(units * n_s * block * sizeof(float));
   w.total = w.po + units * n_s * block * kD * sizeof(float);
@@ -592,18 +608,20 @@ bool overlap(const void* a, const void* b, size_t n) {
   return x < y + n && y < x + n;
 }
 
-template <typename T, int BS>
+template <typename T, int BS, bool HAS_PAD>
 int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
   using C = Cfg<T, BS>;
   const int per_g = 2 * a.n_s, per_m = a.nb - 2;
   const unsigned bhs = static_cast<unsigned>(B) * static_cast<unsigned>(H);
   if (flags == BB_LAUNCH_SPLIT) {
-    bb_global_rows_kernel<T, BS><<<dim3(bhs * per_g), dim3(C::NT), 0, stream>>>(a);
+    bb_global_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_g), dim3(C::NT), 0, stream>>>(a);
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-    bb_middle_rows_kernel<T, BS><<<dim3(bhs * per_m), dim3(C::NT), 0, stream>>>(a);
+    bb_middle_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_m), dim3(C::NT), 0, stream>>>(a);
   } else {
-    bb_fused_kernel<T, BS><<<dim3(bhs * (per_g + per_m)), dim3(C::NT), 0, stream>>>(a);
+    bb_fused_kernel<T, BS, HAS_PAD><<<dim3(bhs * (per_g + per_m)), dim3(C::NT), 0, stream>>>(a);
   }
+  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  bb_global_merge_kernel<T, BS><<<dim3(bhs * 2), dim3(256), 0, stream>>>(a);
   return hipGetLastError() == hipSuccess ? BB_OK : BB_ERR_HIP;
 }
 
@@ -664,7 +682,6 @@ extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, c
   a.rand_idx = rand_idx;
   a.out = static_cast<char*>(out);
   char* ws = static_cast<char*>(workspace);
-  a.ctr = reinterpret_cast<uint32_t*>(ws + w.ctr);
   a.pm = reinterpret_cast<float*>(ws + w.pm);
   a.pl = reinterpret_cast<float*>(ws + w.pl);
   a.po = reinterpret_cast<float*>(ws + w.po);
@@ -674,9 +691,13 @@ extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, c
   a.r = r;
   a.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == BB_BF16)
-    return block == 64 ? launch<__bf16, 64>(a, B, H, s, flags) : launch<__bf16, 128>(a, B, H, s, flags);
-  return block == 64 ? launch<float, 64>(a, B, H, s, flags) : launch<float, 128>(a, B, H, s, flags);
+  const bool p = pad_mask != nullptr;
+  if (dtype == BB_BF16) {
+    if (block == 64) return p ? launch<__bf16, 64, true>(a, B, H, s, flags) : launch<__bf16, 64, false>(a, B, H, s, flags);
+    return p ? launch<__bf16, 128, true>(a, B, H, s, flags) : launch<__bf16, 128, false>(a, B, H, s, flags);
+  }
+  if (block == 64) return p ? launch<float, 64, true>(a, B, H, s, flags) : launch<float, 64, false>(a, B, H, s, flags);
+  return p ? launch<float, 128, true>(a, B, H, s, flags) : launch<float, 128, false>(a, B, H, s, flags);
 }
 
 extern "C" int bb_attn_forward(const void* q, const void* k, const void* v, const uint8_t* pad_mask,

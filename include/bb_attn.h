@@ -47,8 +47,8 @@ typedef enum {
 typedef enum { BB_FP32 = 0, BB_BF16 = 1 } bb_dtype;
 
 /* Flags for bb_attn_forward_ex. */
-#define BB_LAUNCH_FUSED 0u /* one launch: global-row and middle-block work units share a grid */
-#define BB_LAUNCH_SPLIT 1u /* two launches on `stream`: the global-row kernel, then the middle-block kernel */
+#define BB_LAUNCH_FUSED 0u /* global-row and middle-block work units share one grid, then the split-K merge */
+#define BB_LAUNCH_SPLIT 1u /* global-row kernel, middle-block kernel, split-K merge: three launches */
 
 /* Version of this ABI (BB_ABI_VERSION of the built library). */
 int bb_abi_version(void);
@@ -85,10 +85,10 @@ int bb_rand_idx_build(uint64_t seed, int H, int L, int block, int r, int32_t* ra
 int bb_rand_idx_check(const int32_t* rand_idx, int H, int L, int block, int r);
 
 /*
- * Bytes of device workspace bb_attn_forward needs for these sizes (split-K
- * partial results of the two global query blocks plus per-(b, h, block)
- * arrival counters).  0 for empty inputs.  Returns 0 also for unsupported
- * sizes (bb_attn_forward then reports BB_ERR_SHAPE).
+ * Bytes of device workspace bb_attn_forward needs for these sizes: the
+ * split-K partial results (row max, row sum, unnormalised output, fp32) of
+ * the two global query blocks of every (b, h).  0 for empty inputs.  Returns
+ * 0 also for unsupported sizes (bb_attn_forward then reports BB_ERR_SHAPE).
  */
 size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block);
 
@@ -113,9 +113,9 @@ size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block);
  *   dtype      BB_BF16 (fp32 accumulation, bf16 output rounded to nearest
  *              even) or BB_FP32.
  *   workspace  DEVICE buffer of at least bb_attn_workspace_bytes(...) bytes,
- *              256-byte aligned.  It must be zero-filled before its first use;
- *              every completed call leaves it zero-ready for the next one.
- *              Calls that run concurrently need distinct workspaces.
+ *              256-byte aligned.  Its contents need no initialisation (every
+ *              byte read is written earlier in the same call).  Calls that run
+ *              concurrently need distinct workspaces.
  *   stream     hipStream_t to enqueue on (NULL = the null stream).
  * The call is asynchronous: results are valid once `stream` has been
  * synchronised.  Launch errors map to BB_ERR_HIP.

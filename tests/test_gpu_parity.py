@@ -36,12 +36,9 @@ def dev():
 
 
 def poisoned_workspace(w, dev):
-    """Workspace whose counters are zero and whose partial-result area is NaN."""
+    """Workspace filled with NaN bytes: any partial read before it is written shows up."""
     n = bb.bb_attn_workspace_bytes(w.B, w.H, w.L, w.d, w.block)
-    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
-    ctr_bytes = -(-(w.B * w.H * 2 * 4) // 256) * 256
-    ws[:ctr_bytes] = 0
-    return ws
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
 
 
 def run_gpu(w, dev, flags=bb.BB_LAUNCH_FUSED, inputs=None, ws=None):

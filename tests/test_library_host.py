@@ -201,6 +201,6 @@ def test_workspace_size_formula(lib):
         units = B * H * 2
         def a256(x):
             return (x + 255) // 256 * 256
-        exp = a256(units * 4) + 2 * a256(units * n_s * block * 4) + units * n_s * block * 64 * 4
+        exp = 2 * a256(units * n_s * block * 4) + units * n_s * block * 64 * 4
         assert lib.bb_attn_workspace_bytes(B, H, L, 64, block) == exp
     assert lib.bb_attn_workspace_bytes(1, 1, 1000, 64, 64) == 0   # unsupported -> 0
