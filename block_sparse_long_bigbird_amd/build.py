@@ -37,6 +37,9 @@ def build(verbose: bool = False) -> str:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Wall", "-I", INCLUDE,
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep MFMA accumulators in VGPRs: the softmax reads the score tile
+        # every step, and AGPR<->VGPR copies cost both issue slots and registers
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         os.path.join(CSRC, "bb_attn.hip"),
         os.path.join(CSRC, "bb_adjacency.cpp"),
         "-o", tmp,

@@ -73,18 +73,23 @@ struct Cfg {
   static constexpr int ES = sizeof(T);
   static constexpr int ROWB = kD * ES;              // bytes per K/V row
   static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
-  static constexpr int WQ = BS / 32;                // query groups (32 rows each)
-  static constexpr int WK = 2;                      // key halves
-  static constexpr int NW = WQ * WK;                // waves per workgroup
+  static constexpr int QROWS = 64;                  // query rows per work unit
+  static constexpr int QSPLIT = BS / QROWS;         // work units per query block (1 or 2)
+  static constexpr int WQ = QROWS / 32;             // query groups (32 rows each)
+  static constexpr int WK = BS / 32;                // key groups: one 32-key subtile per wave
+  static constexpr int NW = WQ * WK;                // waves per workgroup (4 or 8)
   static constexpr int NT = 64 * NW;                // threads per workgroup
-  static constexpr int NSUB = BS / (32 * WK);       // 32-key subtiles per wave per tile
   static constexpr int TILE = BS * ROWB;            // bytes of one K (or V) tile
   static constexpr int NSTAGE = 6 * TILE <= 96 * 1024 ? 3 : 2;  // LDS ring depth
   static constexpr int DMA_MAT = BS * CPR / 64 / NW;  // DMA instructions per wave per matrix
   static constexpr int QC = CPR / 2;                // Q chunks per lane
+  // key-group merge at the end: round with the most writers has WK/2 of them
+  static constexpr int MERGE_O = (WK / 2) * WQ * 16 * 64 * 4;   // 16 O registers per lane
+  static constexpr int MERGE_ML = (WK / 2) * WQ * 2 * 64 * 4;   // row max and row sum
   static_assert(DMA_MAT * 64 * NW == BS * CPR, "tile DMA must split evenly over waves");
   static_assert(CPR % 8 == 0, "swizzles act on groups of 8 chunks");
-  static_assert(WQ * 16 * 64 * 4 <= TILE, "merge area must fit in one stage matrix");
+  static_assert(MERGE_O <= 2 * TILE, "merge area must fit in one stage");
+  static_assert(NSTAGE == 3 || MERGE_O + MERGE_ML <= 2 * TILE, "merge area (two stages)");
 };
 
 struct Args {
@@ -161,23 +166,24 @@ __device__ __forceinline__ void ring_barrier() {
 // Copy key tile `tile` of K and V from HBM straight into LDS stage S.  Each DMA instruction moves 64 x 16 bytes; lane l of
 // instruction i fills physical chunk slot 64*i + l, so it fetches the logical
 // chunk that the swizzle places there.  Rows stay contiguous 128-byte runs.
+typedef const __attribute__((address_space(1))) char* gchar_ptr;
+
 template <typename T, int BS, int S>
-__device__ __forceinline__ void issue_tile(const char* kbh, const char* vbh, int tile, int wave,
-                                           int lane) {
+__device__ __forceinline__ void issue_tile(gchar_ptr kbh, gchar_ptr vbh, int tile, int wave, int lane) {
   using C = Cfg<T, BS>;
-  const char* kt = kbh + static_cast<size_t>(tile) * C::TILE;
-  const char* vt = vbh + static_cast<size_t>(tile) * C::TILE;
+  const gchar_ptr kt = kbh + static_cast<size_t>(tile) * C::TILE;
+  const gchar_ptr vt = vbh + static_cast<size_t>(tile) * C::TILE;
 #pragma unroll
   for (int jj = 0; jj < C::DMA_MAT; ++jj) {
     const int ins = wave + C::NW * jj;
     const int slot = ins * 64 + lane;
     const int row = slot / C::CPR, p = slot % C::CPR;
-    __builtin_amdgcn_global_load_lds(
-        (const glb_void_t*)(kt + row * C::ROWB + ((p ^ swz_k(row)) << 4)),
-        (lds_void_t*)(Stage<T, BS, S>::k() + ins * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(
-        (const glb_void_t*)(vt + row * C::ROWB + ((p ^ swz_v(row)) << 4)),
-        (lds_void_t*)(Stage<T, BS, S>::v() + ins * 1024), 16, 0, 0);
+    const uint32_t ko = row * C::ROWB + ((p ^ swz_k(row)) << 4);
+    const uint32_t vo = row * C::ROWB + ((p ^ swz_v(row)) << 4);
+    __builtin_amdgcn_global_load_lds((const glb_void_t*)(kt + ko),
+                                     (lds_void_t*)(Stage<T, BS, S>::k() + ins * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const glb_void_t*)(vt + vo),
+                                     (lds_void_t*)(Stage<T, BS, S>::v() + ins * 1024), 16, 0, 0);
   }
 }
 
@@ -186,6 +192,18 @@ struct WaveState {
   f32x16 o[2];   // O^T, dims [0,32) and [32,64)
   float m;       // running row max in q.k units (may lag the true max by < tau/scale)
   float l;       // this lane's part of the row sum
+};
+
+// V^T operands of one subtile for the PV MFMAs: [dim half][16-key half].
+template <typename T>
+struct VOp;
+template <>
+struct VOp<__bf16> {
+  bf16x8 a[2][2];
+};
+template <>
+struct VOp<float> {
+  float a[2][16];
 };
 
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 acc, __bf16*) {
@@ -200,51 +218,124 @@ __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 acc, float*) 
   return acc;
 }
 
-// One 32-key subtile of stage S: scores, online softmax, PV.
+typedef const __attribute__((address_space(4))) uint64_t* const_u64_ptr;
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+// S^T = K . Q^T (+ key bias) for this wave's 32-key subtile of stage S.
 template <typename T, int BS, int S, bool HAS_PAD>
-__device__ __forceinline__ void subtile(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC],
-                                        const uint8_t* pad_t, int kbase, int lane) {
+__device__ __forceinline__ f32x16 scores(const u32x4 (&qop)[Cfg<T, BS>::QC], const uint8_t* pad_t,
+                                         int kbase, int lane) {
   using C = Cfg<T, BS>;
   const int j = lane & 31, g = lane >> 5;
-  // ---- S^T = K . Q^T (+ key bias) -------------------------------------------
+  const char* sk = Stage<T, BS, S>::k();
+  const int row = kbase + perm_row(j);
+  const int sw = swz_k(row);
+  u32x4 a[C::QC];
+#pragma unroll
+  for (int x = 0; x < C::QC; ++x)
+    a[x] = *reinterpret_cast<const u32x4*>(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int x = 0; x < C::QC; ++x) acc = mfma_qk(a[x], qop[x], acc, static_cast<T*>(nullptr));
   if constexpr (HAS_PAD) {
-    // The 32 pad bytes of this subtile, read with wave-uniform (scalar) loads.
-    const uint64_t* pw = reinterpret_cast<const uint64_t*>(pad_t + kbase);
+    // The 32 pad bytes of this subtile, read with wave-uniform (scalar) loads;
+    // the -10000 offset (in q.k units) is added only where a key is padding.
+    const const_u64_ptr pw = (const_u64_ptr)(pad_t + kbase);
     const uint64_t p0 = pw[0], p1 = pw[1], p2 = pw[2], p3 = pw[3];
     if (has_zero_byte(p0) || has_zero_byte(p1) || has_zero_byte(p2) || has_zero_byte(p3)) {
       const uint64_t w0 = g ? p1 : p0, w1 = g ? p3 : p2;
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
-        acc[v] = ((w0 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
-        acc[8 + v] = ((w1 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
+        acc[v] += ((w0 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
+        acc[8 + v] += ((w1 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
       }
     }
   }
-  {
-    const char* sk = Stage<T, BS, S>::k();
-    const int row = kbase + perm_row(j);
-    const int sw = swz_k(row);
+  return acc;
+}
+
+// V^T operands of this wave's subtile of stage S.
+template <typename T, int BS, int S>
+__device__ __forceinline__ VOp<T> load_v(int kbase, int lane) {
+  using C = Cfg<T, BS>;
+  const char* sv = Stage<T, BS, S>::v();
+  VOp<T> vo;
+  if constexpr (sizeof(T) == 2) {
+    // Transposing LDS reads (ds_read_b64_tr_b16): lane (dim, g) gets V[key][dim]
+    // for 4 consecutive keys; lanes 4e+m of each 16-lane group address row
+    // key0+e at dim quad m.  Rows key0 + {0, 4, 16, 20} share the swizzle
+    // (it depends on row % 4), so one address per dim half serves all four
+    // reads through immediate offsets.  The reads sit in one asm block that
+    // ends with its own lgkmcnt wait: issued through the intrinsic, the
+    // compiler cannot tell them from the K/V DMA still in flight and would
+    // drain all vector memory before each of them.
+    const int g = lane >> 5, e4 = (lane >> 2) & 3;
+    const int r0 = kbase + 8 * g + e4;
+    uint32_t addr[2];
 #pragma unroll
-    for (int x = 0; x < C::QC; ++x) {
-      const u32x4 a =
-          *reinterpret_cast<const u32x4*>(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
-      acc = mfma_qk(a, qop[x], acc, static_cast<T*>(nullptr));
+    for (int dh = 0; dh < 2; ++dh) {
+      const int dstart = dh * 32 + perm_row(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+      const int dchunk = dstart >> 3, dbyte = (dstart & 7) * 2;
+      addr[dh] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (const __attribute__((address_space(3))) char*)(sv + r0 * C::ROWB + ((dchunk ^ swz_v(r0)) << 4) + dbyte)));
+    }
+    i16x4 t[2][4];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:%10\n"
+        "ds_read_b64_tr_b16 %2, %8 offset:%11\n"
+        "ds_read_b64_tr_b16 %3, %8 offset:%12\n"
+        "ds_read_b64_tr_b16 %4, %9\n"
+        "ds_read_b64_tr_b16 %5, %9 offset:%10\n"
+        "ds_read_b64_tr_b16 %6, %9 offset:%11\n"
+        "ds_read_b64_tr_b16 %7, %9 offset:%12\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[0][2]), "=&v"(t[0][3]),
+          "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[1][2]), "=&v"(t[1][3])
+        : "v"(addr[0]), "v"(addr[1]), "i"(4 * C::ROWB), "i"(16 * C::ROWB), "i"(20 * C::ROWB)
+        : "memory");
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+        vo.a[dh][mm] = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(t[dh][2 * mm], t[dh][2 * mm + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    const int j = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) {
+      const int dim = dh * 32 + perm_row(j);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kbase + 16 * (v >> 3) + 8 * g + (v & 7);
+        vo.a[dh][v] = *reinterpret_cast<const float*>(
+            sv + key * C::ROWB + (((dim >> 2) ^ swz_v(key)) << 4) + (dim & 3) * 4);
+      }
     }
   }
-  // ---- online softmax (lane = query row; 16 of its 32 keys) ----------------
-  float mloc = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
-#pragma unroll
-  for (int v = 3; v < 15; v += 2) mloc = fmaxf(fmaxf(mloc, acc[v]), acc[v + 1]);
-  mloc = fmaxf(mloc, acc[15]);
+  return vo;
+}
+
+// Online softmax of one score subtile (lane = query row, 16 of its 32 keys)
+// and O^T += V^T . P^T.  Registers only.
+template <typename T>
+__device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, const VOp<T>& vo) {
+  float m8[6];
+  m8[0] = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+  m8[1] = fmaxf(fmaxf(acc[3], acc[4]), acc[5]);
+  m8[2] = fmaxf(fmaxf(acc[6], acc[7]), acc[8]);
+  m8[3] = fmaxf(fmaxf(acc[9], acc[10]), acc[11]);
+  m8[4] = fmaxf(fmaxf(acc[12], acc[13]), acc[14]);
+  m8[5] = fmaxf(acc[15], ws.m);
+  float mloc = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), m8[2]), fmaxf(fmaxf(m8[3], m8[4]), m8[5]));
   {
     const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc),
                                                       false, false);
     mloc = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
   }
-  const float m_new = fmaxf(ws.m, mloc);
+  const float m_new = mloc;   // already includes the running max
   if (__any((m_new - ws.m) * kScaleLog2 > kRescaleTau)) {
     const float alpha = __builtin_amdgcn_exp2f((ws.m - m_new) * kScaleLog2);
 #pragma unroll
@@ -259,83 +350,95 @@ __device__ __forceinline__ void subtile(WaveState& ws, const u32x4 (&qop)[Cfg<T,
   float p[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-  // ---- O^T += V^T . P^T -------------------------------------------------------
-  const char* sv = Stage<T, BS, S>::v();
   if constexpr (sizeof(T) == 2) {
     bf16x8 pb[2];
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float lsum = ws.l;
+    float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         f32x2 pr = {p[8 * h + e], p[8 * h + e + 1]};
         const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, lsum, false);  // row sum of bf16(P)
+        if (h == 0)
+          ls0 = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, ls0, false);   // row sum of bf16(P)
+        else
+          ls1 = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, ls1, false);
         pb[h][e] = c2[0];
         pb[h][e + 1] = c2[1];
       }
-    ws.l = lsum;
-    // Transposing LDS reads: lane (dim, g) gets V[key][dim] for 4 consecutive
-    // keys; lanes 4e+m of each 16-lane group address row key0+e at dim quad m.
-    const int e4 = (lane >> 2) & 3;
+    ws.l += ls0 + ls1;
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-      const int dstart = dh * 32 + perm_row(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-      const int dchunk = dstart >> 3, dbyte = (dstart & 7) * 2;
+    for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const int r0 = kbase + 16 * mm + 8 * g + e4, r1 = r0 + 4;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sv + r0 * C::ROWB + ((dchunk ^ swz_v(r0)) << 4) + dbyte));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(sv + r1 * C::ROWB + ((dchunk ^ swz_v(r1)) << 4) + dbyte));
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mm], ws.o[dh], 0, 0, 0);
-      }
-    }
+      for (int dh = 0; dh < 2; ++dh)
+        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[dh][mm], pb[mm], ws.o[dh], 0, 0, 0);
   } else {
     float lsum = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) lsum += p[v];
     ws.l += lsum;
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-      const int dim = dh * 32 + perm_row(j);
+    for (int v = 0; v < 16; ++v)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kbase + 16 * (v >> 3) + 8 * g + (v & 7);
-        const float a = *reinterpret_cast<const float*>(
-            sv + key * C::ROWB + (((dim >> 2) ^ swz_v(key)) << 4) + (dim & 3) * 4);
-        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[v], ws.o[dh], 0, 0, 0);
-      }
-    }
+      for (int dh = 0; dh < 2; ++dh)
+        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x2f32(vo.a[dh][v], p[v], ws.o[dh], 0, 0, 0);
   }
 }
 
-// One step of the tile loop: tile u sits in stage S.
+// Key tiles of a work unit, computed on the fly (all values wave-uniform).
+struct TileList {
+  int first;             // global unit: first tile of its chunk; middle unit: band start
+  int nwin;              // middle unit: band blocks inside 1..nb-2
+  int nb;
+  bool global;
+  const_i32_ptr rand;    // middle unit: its row of the random-block table
+};
+
+__device__ __forceinline__ int tile_at(const TileList& tl, int u) {
+  if (tl.global) return tl.first + u;
+  if (u == 0) return 0;
+  if (u <= tl.nwin) return tl.first + u - 1;
+  if (u == tl.nwin + 1) return tl.nb - 1;
+  int e = tl.rand[u - tl.nwin - 2];
+  return e < 1 ? 1 : (e > tl.nb - 2 ? tl.nb - 2 : e);   // never read outside the sequence
+}
+
+// Carried from one tile step to the next: the scores and V operands of the
+// previous tile, whose softmax and PV run while the next tile's score MFMAs do.
+template <typename T>
+struct Carry {
+  f32x16 s;
+  VOp<T> v;
+};
+
+// Step u of the software-pipelined tile loop (tile u sits in stage S; tile_u
+// and tile_fill are the ids of tile u and of tile u+NS-1).  Reads the carry of
+// tile u-1 from `prev` and leaves tile u's in `next` (two register sets used
+// alternately, so nothing is copied).  u == ntiles only drains `prev`.
 template <typename T, int BS, int S, bool HAS_PAD>
-__device__ __forceinline__ void step(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC],
-                                     const int* s_tiles, int u, int ntiles, const char* kbh,
-                                     const char* vbh, const uint8_t* pad_b, int wave, int lane,
-                                     int wk) {
+__device__ __forceinline__ void step(WaveState& ws, const Carry<T>& prev, Carry<T>& next,
+                                     const u32x4 (&qop)[Cfg<T, BS>::QC], int u, int ntiles,
+                                     int tile_u, int tile_fill, gchar_ptr kbh, gchar_ptr vbh,
+                                     const uint8_t* pad_b, int wave, int lane, int kbase) {
   using C = Cfg<T, BS>;
   constexpr int NS = C::NSTAGE;
   constexpr int NDMA = 2 * C::DMA_MAT;
-  const int tile = __builtin_amdgcn_readfirstlane(s_tiles[u]);
-  const uint8_t* pad_t = HAS_PAD ? pad_b + static_cast<size_t>(tile) * BS : nullptr;
-  if (NS == 3 && u + 1 < ntiles)
-    wait_vm<NDMA>();     // tile u landed; tile u+1 may still be in flight
-  else
-    wait_vm<0>();
-  ring_barrier();        // every wave's part of tile u is in LDS; stage u-1 is free
-#pragma unroll
-  for (int s = 0; s < C::NSUB; ++s)
-    subtile<T, BS, S, HAS_PAD>(ws, qop, pad_t, wk * (BS / 2) + 32 * s, lane);
-  if (u + NS - 1 < ntiles)  // refill the stage freed by tile u-1
-    issue_tile<T, BS, (S + NS - 1) % NS>(kbh, vbh, __builtin_amdgcn_readfirstlane(s_tiles[u + NS - 1]),
-                                         wave, lane);
+  if (u < ntiles) {
+    // Tile u has landed (tile u+1 may still be in flight); this wave's LDS
+    // reads of the previous step are complete.  Then every wave's part is
+    // visible and the stage of tile u-1 is free.
+    if (NS == 3 && u + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt((NDMA & 15) | ((NDMA >> 4) << 14) | (7 << 4) | (0 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+    ring_barrier();
+    if (u + NS - 1 < ntiles) issue_tile<T, BS, (S + NS - 1) % NS>(kbh, vbh, tile_fill, wave, lane);
+    const uint8_t* pad_t = HAS_PAD ? pad_b + static_cast<size_t>(tile_u) * BS : nullptr;
+    next.v = load_v<T, BS, S>(kbase, lane);
+    next.s = scores<T, BS, S, HAS_PAD>(qop, pad_t, kbase, lane);
+  }
+  if (u > 0) softmax_pv<T>(ws, prev.s, prev.v);
 }
 
 __device__ __forceinline__ void store_row8(char* dst, const float* x, __bf16*) {
@@ -365,15 +468,16 @@ __device__ __forceinline__ void store_f32x4(char* dst, f32x4 x, float*) {
   *reinterpret_cast<f32x4*>(dst) = x;
 }
 
-// One work unit on (b, h).  gsel < 0: middle query block qb, finalised in
-// place.  gsel in {0, 1}: global query block qb (0 or nb-1), key chunk
-// `chunk` of split-K; the last chunk to arrive merges all partials.
+// One work unit on (b, h): query rows [qb*BS + qh*64, +64).  gsel < 0: middle
+// query block qb, finalised in place.  gsel in {0, 1}: global query block qb
+// (0 or nb-1), key chunk `chunk` of split-K, written as a partial for the
+// merge kernel.
 template <typename T, int BS, bool HAS_PAD>
-__device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, int gsel, int chunk) {
+__device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, int qh, int gsel,
+                                         int chunk) {
   using C = Cfg<T, BS>;
   constexpr int ROWB = C::ROWB;
   constexpr int NS = C::NSTAGE;
-  __shared__ int s_tiles[kMaxTiles + 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -382,40 +486,34 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
   const int nb = a.nb, L = a.L;
   const size_t bh = static_cast<size_t>(b) * a.H + h;
   const char* qbh = a.q + bh * L * ROWB;
-  const char* kbh = a.k + bh * L * ROWB;
-  const char* vbh = a.v + bh * L * ROWB;
+  const gchar_ptr kbh = (gchar_ptr)(a.k) + bh * L * ROWB;
+  const gchar_ptr vbh = (gchar_ptr)(a.v) + bh * L * ROWB;
   const uint8_t* pad_b = HAS_PAD ? a.pad + static_cast<size_t>(b) * L : nullptr;
+  const int kbase = wk * 32;             // this wave's 32 keys of every tile
 
-  // ---- key-tile list (identical in every thread; kept in LDS) ---------------
+  // ---- key-tile list ----------------------------------------------------------
+  TileList tl;
+  tl.nb = nb;
+  tl.global = gsel >= 0;
   int ntiles;
   if (gsel < 0) {
     const int lo = qb - 1 < 1 ? 1 : qb - 1;            // band without the global blocks
     const int hi = qb + 1 > nb - 2 ? nb - 2 : qb + 1;
-    ntiles = 2 + (hi - lo + 1) + a.r;
-    if (tid == 0) {
-      int n = 0;
-      s_tiles[n++] = 0;
-      for (int t = lo; t <= hi; ++t) s_tiles[n++] = t;
-      s_tiles[n++] = nb - 1;
-      const int32_t* rr = a.rand_idx + (static_cast<size_t>(h) * (nb - 2) + (qb - 1)) * a.r;
-      for (int t = 0; t < a.r; ++t) {
-        int e = rr[t];
-        e = e < 1 ? 1 : (e > nb - 2 ? nb - 2 : e);    // never read outside the sequence
-        s_tiles[n++] = e;
-      }
-    }
+    tl.first = lo;
+    tl.nwin = hi - lo + 1;
+    tl.rand = (const_i32_ptr)(a.rand_idx + (static_cast<size_t>(h) * (nb - 2) + (qb - 1)) * a.r);
+    ntiles = 2 + tl.nwin + a.r;
   } else {
-    const int t0 = chunk * kChunkTiles;
-    ntiles = nb - t0 < kChunkTiles ? nb - t0 : kChunkTiles;
-    if (tid < ntiles) s_tiles[tid] = t0 + tid;
+    tl.first = chunk * kChunkTiles;
+    tl.nwin = 0;
+    tl.rand = nullptr;
+    ntiles = nb - tl.first < kChunkTiles ? nb - tl.first : kChunkTiles;
   }
-  __syncthreads();
 
   // ---- prologue: first NS-1 tiles in flight, Q into registers ---------------
-  issue_tile<T, BS, 0>(kbh, vbh, __builtin_amdgcn_readfirstlane(s_tiles[0]), wave, lane);
-  if (NS == 3 && ntiles > 1)
-    issue_tile<T, BS, 1 % NS>(kbh, vbh, __builtin_amdgcn_readfirstlane(s_tiles[1]), wave, lane);
-  const int q0 = qb * BS + wq * 32;
+  issue_tile<T, BS, 0>(kbh, vbh, tile_at(tl, 0), wave, lane);
+  if (NS == 3 && ntiles > 1) issue_tile<T, BS, 1 % NS>(kbh, vbh, tile_at(tl, 1), wave, lane);
+  const int q0 = qb * BS + qh * C::QROWS + wq * 32;
   u32x4 qop[C::QC];
   {
     const char* qrow = qbh + static_cast<size_t>(q0 + j) * ROWB;
@@ -430,70 +528,93 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
   }
   ws.m = -__builtin_inff();
   ws.l = 0.0f;
+  Carry<T> cy0, cy1;
 
-  // ---- tile loop: 9 steps per trip (3 turns of a 3-stage ring, or 4.5 of 2) --
-  // Units of the usual shapes have at most 9 tiles, so the loop back edge --
-  // where the compiler's LDS-DMA wait tracking turns conservative -- is rare.
-  for (int u = 0; u < ntiles; u += 9) {
-#define BB_STEP(k)                                                                              \
-  if (u + (k) < ntiles)                                                                         \
-    step<T, BS, (k) % NS, HAS_PAD>(ws, qop, s_tiles, u + (k), ntiles, kbh, vbh, pad_b, wave, lane, wk);
-    BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5) BB_STEP(6) BB_STEP(7) BB_STEP(8)
+  // ---- tile loop: trips of 12 straight-line steps ----------------------------
+  // Step u reads the carry of tile u-1 and writes tile u's, alternating two
+  // register sets; step u == ntiles drains the last carry.  Units of the
+  // usual shapes have at most 11 tiles, so one trip covers them and the loop
+  // back edge -- where the compiler's LDS-DMA wait tracking turns
+  // conservative -- is not taken.  Tile ids are computed once per trip.
+  constexpr int TRIP = 12;
+  static_assert(TRIP % 2 == 0 && TRIP % NS == 0, "trip must keep stage and parity aligned");
+  for (int u = 0; u <= ntiles; u += TRIP) {
+    int tid_[TRIP + NS - 1];
+#pragma unroll
+    for (int k = 0; k < TRIP + NS - 1; ++k) tid_[k] = u + k < ntiles ? tile_at(tl, u + k) : 0;
+#define BB_STEP(k)                                                                               \
+  if (u + (k) <= ntiles)                                                                         \
+    step<T, BS, (k) % NS, HAS_PAD>(ws, (k) % 2 ? cy0 : cy1, (k) % 2 ? cy1 : cy0, qop, u + (k),     \
+                                   ntiles, tid_[k], tid_[(k) + NS - 1], kbh, vbh, pad_b, wave,    \
+                                   lane, kbase);
+    BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
+    BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
   }
 
-  // ---- merge the two key halves of each query group ------------------------
-  __syncthreads();
-  float* mo0 = reinterpret_cast<float*>(Stage<T, BS, 0>::k()) + wq * 16 * 64;
-  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, 0>::v()) + wq * 16 * 64;
-  float* mml = reinterpret_cast<float*>(Stage<T, BS, 1 % NS>::k()) + wq * 2 * 64;
-  if (wk == 1) {
+  // ---- merge the key groups of each query group (tree over LDS) ------------
+  float* mo0 = reinterpret_cast<float*>(Stage<T, BS, 0>::buf());
+  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, 1 % NS>::buf()) + (NS == 3 ? 0 : 0);
+  float* mml = NS == 3 ? reinterpret_cast<float*>(Stage<T, BS, 2 % NS>::buf())
+                       : reinterpret_cast<float*>(Stage<T, BS, 1 % NS>::buf()) + C::MERGE_O / 4;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      mo0[v * 64 + lane] = ws.o[0][v];
-      mo1[v * 64 + lane] = ws.o[1][v];
-    }
-    mml[lane] = ws.m;
-    mml[64 + lane] = ws.l;
-  }
-  __syncthreads();
-  if (wk == 0) {
-    const float m1 = mml[lane], l1 = mml[64 + lane];
-    const float mm = fmaxf(ws.m, m1);
-    const float a0 = __builtin_amdgcn_exp2f((ws.m - mm) * kScaleLog2);
-    const float a1 = __builtin_amdgcn_exp2f((m1 - mm) * kScaleLog2);
-    float o[2][16];
+  for (int stride = C::WK / 2; stride >= 1; stride /= 2) {
+    __syncthreads();
+    if (wk >= stride && wk < 2 * stride) {
+      const int slot = (wk - stride) * C::WQ + wq;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      o[0][v] = ws.o[0][v] * a0 + mo0[v * 64 + lane] * a1;
-      o[1][v] = ws.o[1][v] * a0 + mo1[v * 64 + lane] * a1;
-    }
-    float l = ws.l * a0 + l1 * a1;
-    l += __shfl_xor(l, 32);
-    if (gsel < 0) {
-      char* orow = a.out + (bh * L + q0 + j) * ROWB;
-      const float inv = 1.0f / l;
-#pragma unroll
-      for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = o[dh][8 * h8 + e] * inv;
-          store_row8(orow + (dh * 32 + 16 * h8 + 8 * g) * C::ES, x, static_cast<T*>(nullptr));
-        }
-    } else {
-      const size_t pidx = ((bh * 2 + gsel) * a.n_s + chunk) * BS + wq * 32 + j;
-      char* prow = reinterpret_cast<char*>(a.po + pidx * kD);
-#pragma unroll
-      for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8)
-          store_row8(prow + (dh * 32 + 16 * h8 + 8 * g) * 4, &o[dh][8 * h8], static_cast<float*>(nullptr));
-      if (g == 0) {
-        a.pm[pidx] = mm;
-        a.pl[pidx] = l;
+      for (int v = 0; v < 16; ++v) {
+        mo0[(slot * 16 + v) * 64 + lane] = ws.o[0][v];
+        mo1[(slot * 16 + v) * 64 + lane] = ws.o[1][v];
       }
+      mml[(slot * 2) * 64 + lane] = ws.m;
+      mml[(slot * 2 + 1) * 64 + lane] = ws.l;
+    }
+    __syncthreads();
+    if (wk < stride) {
+      const int slot = wk * C::WQ + wq;
+      const float m1 = mml[(slot * 2) * 64 + lane], l1 = mml[(slot * 2 + 1) * 64 + lane];
+      const float mm = fmaxf(ws.m, m1);
+      const float a0 = __builtin_amdgcn_exp2f((ws.m - mm) * kScaleLog2);
+      const float a1 = __builtin_amdgcn_exp2f((m1 - mm) * kScaleLog2);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        ws.o[0][v] = ws.o[0][v] * a0 + mo0[(slot * 16 + v) * 64 + lane] * a1;
+        ws.o[1][v] = ws.o[1][v] * a0 + mo1[(slot * 16 + v) * 64 + lane] * a1;
+      }
+      ws.l = ws.l * a0 + l1 * a1;
+      ws.m = mm;
+    }
+  }
+  if (wk != 0) return;
+  float l = ws.l + __shfl_xor(ws.l, 32);
+  if (gsel < 0) {
+    char* orow = a.out + (bh * L + q0 + j) * ROWB;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = ws.o[dh][8 * h8 + e] * inv;
+        store_row8(orow + (dh * 32 + 16 * h8 + 8 * g) * C::ES, x, static_cast<T*>(nullptr));
+      }
+  } else {
+    const size_t pidx = ((bh * 2 + gsel) * a.n_s + chunk) * BS + qh * C::QROWS + wq * 32 + j;
+    char* prow = reinterpret_cast<char*>(a.po + pidx * kD);
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = ws.o[dh][8 * h8 + e];
+        store_row8(prow + (dh * 32 + 16 * h8 + 8 * g) * 4, x, static_cast<float*>(nullptr));
+      }
+    if (g == 0) {
+      a.pm[pidx] = ws.m;
+      a.pl[pidx] = l;
     }
   }
 }
@@ -501,56 +622,65 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
 // Split-K merge of the two global query blocks of one (b, h): the partials of
 // the n_s key chunks (row max m_s, row sum l_s, unnormalised O_s) combine as
 // out = sum_s 2^((m_s - m)c) O_s / sum_s 2^((m_s - m)c) l_s, m = max_s m_s,
-// summed in chunk order.  Runs as its own launch after the global-row units,
-// so their partials are complete and visible without any in-kernel fence.
+// accumulated in chunk order with a running maximum (deterministic).  Runs as
+// its own launch after the global-row units, so their partials are complete
+// and visible without any in-kernel fence.  One thread per 4 output values;
+// a workgroup covers 16 query rows of one global block.
 template <typename T, int BS>
 __global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
   constexpr int ROWB = kD * sizeof(T);
-  const int bh = blockIdx.x >> 1, gsel = blockIdx.x & 1;
+  constexpr int SLICES = BS / 16;
+  const int slice = blockIdx.x % SLICES, gblk = blockIdx.x / SLICES;
+  const int bh = gblk >> 1, gsel = gblk & 1;
   const int qb = gsel ? a.nb - 1 : 0;
+  const int ql = slice * 16 + (threadIdx.x >> 4), dq = threadIdx.x & 15;
   const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.n_s;
-  for (int idx = threadIdx.x; idx < BS * kD / 4; idx += 256) {
-    const int ql = idx / (kD / 4), dq = idx % (kD / 4);
-    float mx = -__builtin_inff();
-    for (int s = 0; s < a.n_s; ++s) mx = fmaxf(mx, a.pm[(base + s) * BS + ql]);
-    f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
-    float den = 0.0f;
-    for (int s = 0; s < a.n_s; ++s) {              // fixed order: deterministic
-      const size_t pi = (base + s) * BS + ql;
-      const float w = __builtin_amdgcn_exp2f((a.pm[pi] - mx) * kScaleLog2);
-      den += w * a.pl[pi];
-      const f32x4 po = *reinterpret_cast<const f32x4*>(a.po + pi * kD + dq * 4);
-      num += w * po;
-    }
-    const float inv = 1.0f / den;
-    store_f32x4(a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + ql) * ROWB +
-                    dq * 4 * sizeof(T),
-                num * inv, static_cast<T*>(nullptr));
+  float m = -__builtin_inff(), den = 0.0f;
+  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+  for (int s = 0; s < a.n_s; ++s) {
+    const size_t pi = (base + s) * BS + ql;
+    const float ms = a.pm[pi], ls = a.pl[pi];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(a.po + pi * kD + dq * 4);
+    const float mn = fmaxf(m, ms);
+    const float wa = __builtin_amdgcn_exp2f((m - mn) * kScaleLog2);
+    const float wb = __builtin_amdgcn_exp2f((ms - mn) * kScaleLog2);
+    den = den * wa + ls * wb;
+    num = num * wa + os * wb;
+    m = mn;
   }
+  store_f32x4(a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + ql) * ROWB +
+                  dq * 4 * sizeof(T),
+              num * (1.0f / den), static_cast<T*>(nullptr));
 }
 
-// Decode a work unit.  Per (b, h): 2*n_s global units (block 0 chunks, then
-// block nb-1 chunks) followed by nb-2 middle units.  kind selects which of
-// them this grid covers: 0 = all, 1 = global units only, 2 = middle only.
+// Decode a work unit.  Per (b, h): the global units (block 0 chunks, then
+// block nb-1 chunks; QSPLIT row slices each) followed by the middle units
+// (nb-2 blocks, QSPLIT row slices each).  kind selects which of them this
+// grid covers: 0 = all, 1 = global units only, 2 = middle units only.
 template <typename T, int BS, int kind, bool HAS_PAD>
 __device__ __forceinline__ void dispatch(const Args& a) {
-  const int n_g = kind == 2 ? 0 : 2 * a.n_s;
-  const int n_m = kind == 1 ? 0 : a.nb - 2;
+  constexpr int QS = Cfg<T, BS>::QSPLIT;
+  const int n_g = kind == 2 ? 0 : 2 * a.n_s * QS;
+  const int n_m = kind == 1 ? 0 : (a.nb - 2) * QS;
   const int per_bh = n_g + n_m;
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = unit / per_bh, u = unit % per_bh;
   const int b = bh / a.H, h = bh % a.H;
-  int qb, gsel, chunk;
+  int qb, qh, gsel, chunk;
   if (u < n_g) {
-    gsel = u / a.n_s;
-    chunk = u % a.n_s;
+    gsel = u / (a.n_s * QS);
+    const int rem = u % (a.n_s * QS);
+    chunk = rem / QS;
+    qh = rem % QS;
     qb = gsel ? a.nb - 1 : 0;
   } else {
     gsel = -1;
     chunk = 0;
-    qb = u - n_g + 1;
+    qb = (u - n_g) / QS + 1;
+    qh = (u - n_g) % QS;
   }
-  run_unit<T, BS, HAS_PAD>(a, b, h, qb, gsel, chunk);
+  run_unit<T, BS, HAS_PAD>(a, b, h, qb, qh, gsel, chunk);
 }
 
 template <typename T, int BS, bool HAS_PAD>
@@ -595,7 +725,7 @@ int check_shape(int B, int H, int L, int d, int block, int r, int* nb_out) {
   const int r_max = nb - 5 > 0 ? nb - 5 : 0;
   if (r > r_max || r > kMaxR) return BB_ERR_SHAPE;
   const int n_s = (nb + kChunkTiles - 1) / kChunkTiles;
-  const long long units = static_cast<long long>(B) * H * (2LL * n_s + nb - 2);
+  const long long units = static_cast<long long>(B) * H * (2LL * n_s + nb - 2) * (block / 64);
   if (units > 0x7fffffffLL) return BB_ERR_SHAPE;
   *nb_out = nb;
   return BB_OK;
@@ -611,7 +741,7 @@ bool overlap(const void* a, const void* b, size_t n) {
 template <typename T, int BS, bool HAS_PAD>
 int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
   using C = Cfg<T, BS>;
-  const int per_g = 2 * a.n_s, per_m = a.nb - 2;
+  const int per_g = 2 * a.n_s * C::QSPLIT, per_m = (a.nb - 2) * C::QSPLIT;
   const unsigned bhs = static_cast<unsigned>(B) * static_cast<unsigned>(H);
   if (flags == BB_LAUNCH_SPLIT) {
     bb_global_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_g), dim3(C::NT), 0, stream>>>(a);
@@ -621,7 +751,7 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
     bb_fused_kernel<T, BS, HAS_PAD><<<dim3(bhs * (per_g + per_m)), dim3(C::NT), 0, stream>>>(a);
   }
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-  bb_global_merge_kernel<T, BS><<<dim3(bhs * 2), dim3(256), 0, stream>>>(a);
+  bb_global_merge_kernel<T, BS><<<dim3(bhs * 2 * (BS / 16)), dim3(256), 0, stream>>>(a);
   return hipGetLastError() == hipSuccess ? BB_OK : BB_ERR_HIP;
 }
 
