@@ -80,7 +80,10 @@ struct Cfg {
   static constexpr int NW = WQ * WK;                // waves per workgroup (4 or 8)
   static constexpr int NT = 64 * NW;                // threads per workgroup
   static constexpr int TILE = BS * ROWB;            // bytes of one K (or V) tile
-  static constexpr int NSTAGE = 6 * TILE <= 96 * 1024 ? 3 : 2;  // LDS ring depth
+  // LDS ring depth.  Two stages: tile u+1 streams in while tile u is used.
+  // (A third stage lets two tiles fly, but the compiler's LDS-DMA wait
+  // tracking then drains the queue on one stage of every three.)
+  static constexpr int NSTAGE = 2;
   static constexpr int DMA_MAT = BS * CPR / 64 / NW;  // DMA instructions per wave per matrix
   static constexpr int QC = CPR / 2;                // Q chunks per lane
   // key-group merge at the end: round with the most writers has WK/2 of them
@@ -89,7 +92,7 @@ struct Cfg {
   static_assert(DMA_MAT * 64 * NW == BS * CPR, "tile DMA must split evenly over waves");
   static_assert(CPR % 8 == 0, "swizzles act on groups of 8 chunks");
   static_assert(MERGE_O <= 2 * TILE, "merge area must fit in one stage");
-  static_assert(NSTAGE == 3 || MERGE_O + MERGE_ML <= 2 * TILE, "merge area (two stages)");
+  static_assert(MERGE_O + MERGE_ML <= 2 * TILE, "merge area (two stages)");
 };
 
 struct Args {
@@ -322,6 +325,21 @@ __device__ __forceinline__ VOp<T> load_v(int kbase, int lane) {
 // and O^T += V^T . P^T.  Registers only.
 template <typename T>
 __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, const VOp<T>& vo) {
+  // P = 2^((s - m) c) against the running max m first; the tile's own max
+  // is reduced meanwhile, and only if it exceeds m by more than tau/c (rare)
+  // are O and l rescaled and P recomputed.  Keeps the exps off the critical
+  // path of the max reduction.
+  if (ws.m == -__builtin_inff()) {   // first tile: start the running max from it
+    float mm = acc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mm = fmaxf(mm, acc[v]);
+    const auto sw0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mm), __float_as_uint(mm), false, false);
+    ws.m = fmaxf(__uint_as_float(sw0[0]), __uint_as_float(sw0[1]));
+  }
+  float mc = ws.m * kScaleLog2;
+  float p[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
   float m8[6];
   m8[0] = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
   m8[1] = fmaxf(fmaxf(acc[3], acc[4]), acc[5]);
@@ -335,21 +353,19 @@ __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, con
                                                       false, false);
     mloc = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
   }
-  const float m_new = mloc;   // already includes the running max
-  if (__any((m_new - ws.m) * kScaleLog2 > kRescaleTau)) {
-    const float alpha = __builtin_amdgcn_exp2f((ws.m - m_new) * kScaleLog2);
+  if (__any((mloc - ws.m) * kScaleLog2 > kRescaleTau)) {
+    const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       ws.o[0][v] *= alpha;
       ws.o[1][v] *= alpha;
     }
     ws.l *= alpha;
-    ws.m = m_new;
-  }
-  const float mc = ws.m * kScaleLog2;
-  float p[16];
+    ws.m = mloc;
+    mc = ws.m * kScaleLog2;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
+  }
   if constexpr (sizeof(T) == 2) {
     bf16x8 pb[2];
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
@@ -412,8 +428,8 @@ struct Carry {
   VOp<T> v;
 };
 
-// Step u of the software-pipelined tile loop (tile u sits in stage S; tile_u
-// and tile_fill are the ids of tile u and of tile u+NS-1).  Reads the carry of
+// Step u of the software-pipelined tile loop (tile u sits in stage S = u % 2;
+// tile_u and tile_fill are the ids of tiles u and u+1).  Reads the carry of
 // tile u-1 from `prev` and leaves tile u's in `next` (two register sets used
 // alternately, so nothing is copied).  u == ntiles only drains `prev`.
 template <typename T, int BS, int S, bool HAS_PAD>
@@ -421,19 +437,13 @@ __device__ __forceinline__ void step(WaveState& ws, const Carry<T>& prev, Carry<
                                      const u32x4 (&qop)[Cfg<T, BS>::QC], int u, int ntiles,
                                      int tile_u, int tile_fill, gchar_ptr kbh, gchar_ptr vbh,
                                      const uint8_t* pad_b, int wave, int lane, int kbase) {
-  using C = Cfg<T, BS>;
-  constexpr int NS = C::NSTAGE;
-  constexpr int NDMA = 2 * C::DMA_MAT;
   if (u < ntiles) {
-    // Tile u has landed (tile u+1 may still be in flight); this wave's LDS
-    // reads of the previous step are complete.  Then every wave's part is
-    // visible and the stage of tile u-1 is free.
-    if (NS == 3 && u + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt((NDMA & 15) | ((NDMA >> 4) << 14) | (7 << 4) | (0 << 8));
-    else
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+    // This wave's DMA of tile u has landed and its LDS reads of the previous
+    // step are complete (vmcnt = lgkmcnt = 0); after the barrier every wave's
+    // part of tile u is visible and the stage of tile u-1 is free to refill.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
     ring_barrier();
-    if (u + NS - 1 < ntiles) issue_tile<T, BS, (S + NS - 1) % NS>(kbh, vbh, tile_fill, wave, lane);
+    if (u + 1 < ntiles) issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
     const uint8_t* pad_t = HAS_PAD ? pad_b + static_cast<size_t>(tile_u) * BS : nullptr;
     next.v = load_v<T, BS, S>(kbase, lane);
     next.s = scores<T, BS, S, HAS_PAD>(qop, pad_t, kbase, lane);
@@ -477,7 +487,6 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
                                          int chunk) {
   using C = Cfg<T, BS>;
   constexpr int ROWB = C::ROWB;
-  constexpr int NS = C::NSTAGE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -510,9 +519,8 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
     ntiles = nb - tl.first < kChunkTiles ? nb - tl.first : kChunkTiles;
   }
 
-  // ---- prologue: first NS-1 tiles in flight, Q into registers ---------------
+  // ---- prologue: tile 0 in flight, Q into registers ----------------------------
   issue_tile<T, BS, 0>(kbh, vbh, tile_at(tl, 0), wave, lane);
-  if (NS == 3 && ntiles > 1) issue_tile<T, BS, 1 % NS>(kbh, vbh, tile_at(tl, 1), wave, lane);
   const int q0 = qb * BS + qh * C::QROWS + wq * 32;
   u32x4 qop[C::QC];
   {
@@ -530,23 +538,23 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
   ws.l = 0.0f;
   Carry<T> cy0, cy1;
 
-  // ---- tile loop: trips of 12 straight-line steps ----------------------------
+  // ---- tile loop: trips of 12 straight-line steps -----------------------------
   // Step u reads the carry of tile u-1 and writes tile u's, alternating two
   // register sets; step u == ntiles drains the last carry.  Units of the
   // usual shapes have at most 11 tiles, so one trip covers them and the loop
   // back edge -- where the compiler's LDS-DMA wait tracking turns
   // conservative -- is not taken.  Tile ids are computed once per trip.
   constexpr int TRIP = 12;
-  static_assert(TRIP % 2 == 0 && TRIP % NS == 0, "trip must keep stage and parity aligned");
+  static_assert(TRIP % 2 == 0, "trip must keep stage and parity aligned");
   for (int u = 0; u <= ntiles; u += TRIP) {
-    int tid_[TRIP + NS - 1];
+    int tid_[TRIP + 1];
 #pragma unroll
-    for (int k = 0; k < TRIP + NS - 1; ++k) tid_[k] = u + k < ntiles ? tile_at(tl, u + k) : 0;
+    for (int k = 0; k < TRIP + 1; ++k) tid_[k] = u + k < ntiles ? tile_at(tl, u + k) : 0;
 #define BB_STEP(k)                                                                               \
   if (u + (k) <= ntiles)                                                                         \
-    step<T, BS, (k) % NS, HAS_PAD>(ws, (k) % 2 ? cy0 : cy1, (k) % 2 ? cy1 : cy0, qop, u + (k),     \
-                                   ntiles, tid_[k], tid_[(k) + NS - 1], kbh, vbh, pad_b, wave,    \
-                                   lane, kbase);
+    step<T, BS, (k) % 2, HAS_PAD>(ws, (k) % 2 ? cy0 : cy1, (k) % 2 ? cy1 : cy0, qop, u + (k),      \
+                                  ntiles, tid_[k], tid_[(k) + 1], kbh, vbh, pad_b, wave, lane,     \
+                                  kbase);
     BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
     BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
@@ -554,9 +562,8 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
 
   // ---- merge the key groups of each query group (tree over LDS) ------------
   float* mo0 = reinterpret_cast<float*>(Stage<T, BS, 0>::buf());
-  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, 1 % NS>::buf()) + (NS == 3 ? 0 : 0);
-  float* mml = NS == 3 ? reinterpret_cast<float*>(Stage<T, BS, 2 % NS>::buf())
-                       : reinterpret_cast<float*>(Stage<T, BS, 1 % NS>::buf()) + C::MERGE_O / 4;
+  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, 1>::buf());
+  float* mml = reinterpret_cast<float*>(Stage<T, BS, 1>::buf()) + C::MERGE_O / 4;
 #pragma unroll
   for (int stride = C::WK / 2; stride >= 1; stride /= 2) {
     __syncthreads();
