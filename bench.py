@@ -1,26 +1,29 @@
 """Benchmark: BigBird block-sparse attention forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode cold|warm]
-                    [--launch fused|split] [--no-cpu-baseline]
+                    [--launch fused|split] [--no-cpu-baseline] [--copy-calibration]
+    python bench.py --pmc-summary FETCH_CSV WRITE_CSV --workload NAME --command "..."
 
-One step = one bb_attn_forward call over the whole batch: the key pad bias,
-tile lists, HBM->LDS staging, QK^T, online softmax, PV, the split-K global
-rows and their merge -- every per-call step of the hot path.  The random-block
-table is built once on the host beforehand, as the reference builds it once at
-layer construction.
+One step = one bb_attn_forward call over the whole batch: key pad bias, tile
+lists, HBM->LDS staging, QK^T, online softmax, PV, the split-K global rows and
+their merge -- every per-call step of the hot path.  The random-block table is
+built once on the host beforehand, as the reference builds it once at layer
+construction; its build time is reported separately.
 
 Prints ONE JSON line.  `value` is useful TFLOP/s: 4*d FLOPs per attended
 (query, key) pair, pairs counted from the block pattern (padding included),
-over the timed wall time of K steps (hipEvents on the launch stream, device
+over the wall time of K timed steps (hipEvents on the launch stream, device
 synchronised on both sides, inputs already resident in HBM).  Cold mode
 rotates among input sets whose total footprint exceeds twice the 256 MB
 last-level cache, so each call reads HBM.
 
-`roofline` is for the dominant kernel, timed per launch with events on its
-stream; `traffic` comes from the committed rocprofv3 counter summary when it
-was taken on the current kernel source, else null.  `cpu_baseline` times the
-fp64 oracle on a bounded sample of (batch, head) units of the same workload on
-this host's cores.
+`roofline` is for the dominant kernel (the fused work-unit kernel, which does
+every useful FLOP): a second pass runs the same K steps through the two-phase
+form of the call with events between the phases, so the kernel's own launch
+duration is measured on its stream.  `traffic` is the HBM bytes per launch from
+the committed rocprofv3 counter summary, used only if that summary was taken
+on the current kernel source.  `cpu_baseline` times the fp64 oracle on a
+bounded sample of (batch, head) units of the same workload on this host.
 """
 
 from __future__ import annotations
@@ -40,8 +43,10 @@ METRIC = "useful TFLOP/s + tokens/s, BigBird attn fwd L=4096 H=12 d=64 bf16, 1 G
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBPS = 8000.0
 LLC_BYTES = 256 * 2**20
+COPY_BYTES = 512 * 2**20                        # copy-kernel calibration size
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_long_bigbird_amd", "csrc", "bb_attn.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+MAIN_KERNEL = "bb_fused_kernel"
 
 
 def pairs_per_unit(L: int, block: int, r: int):
@@ -54,7 +59,7 @@ def pairs_per_unit(L: int, block: int, r: int):
 
 def useful_flops(w):
     g, m = pairs_per_unit(w.L, w.block, w.r)
-    return 4 * w.d * (g + m) * w.B * w.H, 4 * w.d * g * w.B * w.H, 4 * w.d * m * w.B * w.H
+    return 4 * w.d * (g + m) * w.B * w.H
 
 
 def algorithmic_bytes(w):
@@ -71,9 +76,13 @@ def source_sha256() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def committed_traffic(kernel: str, workload: str):
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"hbm_traffic_{MAIN_KERNEL}_{workload}.txt")
+
+
+def committed_traffic(workload: str):
     """HBM bytes per launch from profiles/, if measured on the current kernel source."""
-    path = os.path.join(PROFILES, f"hbm_traffic_{kernel}_{workload}.txt")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -90,9 +99,79 @@ def committed_traffic(kernel: str, workload: str):
         return None
 
 
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str, command: str) -> None:
+    """Turn two rocprofv3 --pmc counter CSVs into the committed traffic summary.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the main kernel are each
+    scaled by the factor that makes the same counter read exactly COPY_BYTES
+    for the calibration copy kernel that bench.py --copy-calibration runs.
+    """
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    def pick(vals, key):
+        names = [n for n in vals if key in n]
+        if not names:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r}")
+        return statistics.mean(v for n in names for v in vals[n]), sum(len(vals[n]) for n in names)
+
+    from block_sparse_long_bigbird_amd.workloads import WORKLOADS
+    w = WORKLOADS[workload]
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    wr = per_kernel(write_csv, "WRITE_SIZE")
+    # The calibration copy moves COPY_BYTES in and COPY_BYTES out.  Other copy
+    # dispatches (input-set clones) are far smaller, so keep the copy-kernel
+    # dispatches within 25% of the largest one.
+    def calib(vals):
+        keys = [n for n in vals if "copy" in n.lower()]
+        if not keys:
+            raise SystemExit("no copy-kernel dispatch found (run bench.py with --copy-calibration)")
+        allv = [(x, n) for n in keys for x in vals[n]]
+        top = max(x for x, _ in allv)
+        big = [x for x, _ in allv if x >= 0.75 * top]
+        name = max(allv)[1]
+        return statistics.median(big) * 1024.0, name
+    copy_fetch, copy_key = calib(f)
+    copy_write, _ = calib(wr)
+    kf, nf = pick(f, MAIN_KERNEL)
+    kw, nw = pick(wr, MAIN_KERNEL)
+    ffac, wfac = COPY_BYTES / copy_fetch, COPY_BYTES / copy_write
+    fetch_b, write_b = kf * 1024.0 * ffac, kw * 1024.0 * wfac
+    lines = [
+        f"# HBM traffic of {MAIN_KERNEL} on {workload} (rocprofv3 --pmc, one counter per run)",
+        f"command: {command}",
+        f"source_sha256: {source_sha256()}",
+        f"dispatches: FETCH_SIZE {nf}, WRITE_SIZE {nw}",
+        f"fetch_kib_per_dispatch: {kf:.1f}",
+        f"write_kib_per_dispatch: {kw:.1f}",
+        f"copy_kernel: {copy_key[:80]}",
+        f"copy_bytes: {COPY_BYTES}",
+        f"copy_fetch_kib: {copy_fetch / 1024.0:.1f}",
+        f"copy_write_kib: {copy_write / 1024.0:.1f}",
+        f"fetch_scale: {ffac:.4f}",
+        f"write_scale: {wfac:.4f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"algorithmic_bytes_per_call: {algorithmic_bytes(w)}",
+        f"traffic_over_algorithmic: {(fetch_b + write_b) / algorithmic_bytes(w):.3f}",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_path(workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, inputs, ri, budget_s: float):
     """Time the fp64 oracle on (b, h) units until `budget_s` is spent (at least one unit)."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import attention_forward
@@ -108,11 +187,10 @@ def cpu_baseline(w, inputs, ri, budget_s: float):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    flops_total, _, _ = useful_flops(w)
     frac = done / len(units)
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     return {
-        "value": round(flops_total * frac / el / 1e12, 6),
+        "value": round(useful_flops(w) * frac / el / 1e12, 6),
         "unit": "TFLOP/s",
         "tokens_per_s": round(w.tokens * frac / el, 1),
         "cores": int(threads),
@@ -132,13 +210,22 @@ def main():
     ap.add_argument("--launch", choices=["fused", "split"], default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed passes, run a plain device copy of a known size "
+                         "(reference point for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--command", default="", help="profiling command recorded by --pmc-summary")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); heads/batch shard with no communication, see the design notes.",
-              file=sys.stderr)
+              f"WORLD_SIZE={world}); (batch, head) units shard across GPUs with no "
+              "communication, but no multi-GPU path is built here.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -150,7 +237,7 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     bb.lib()
-    flags = bb.BB_LAUNCH_SPLIT if args.launch == "split" else bb.BB_LAUNCH_FUSED
+    launch = bb.BB_LAUNCH_SPLIT if args.launch == "split" else bb.BB_LAUNCH_FUSED
 
     t0 = time.perf_counter()
     ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
@@ -169,50 +256,63 @@ def main():
     ws = bb.alloc_workspace(w.B, w.H, w.L, w.d, w.block, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    def call(i, flags):
         a, b_, c, o = sets[i % n_sets]
         bb.bb_attn_forward(a, b_, c, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, o, ws,
                            stream=stream.cuda_stream, flags=flags)
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     for i in range(args.warmup):
-        step(i)
+        call(i, launch)
     torch.cuda.synchronize()
 
-    # Timed region: K steps, device synchronised on both sides.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Pass 1 -- the timed region: K whole steps, device synchronised on both sides.
+    start, end = ev(), ev()
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
+        call(i, launch)
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    per_launch_ms = [a.elapsed_time(b_) for a, b_ in ev]
-    ms_per_step = total_ms / args.steps
+    ms_per_step = start.elapsed_time(end) / args.steps
 
-    flops, flops_g, flops_m = useful_flops(w)
+    # Pass 2 -- per-kernel durations: the same steps in two phases with events
+    # around the work-unit launch (the dominant kernel) and the merge.
+    e = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e[i][0].record(stream)
+        call(i, launch | bb.BB_PHASE_UNITS)
+        e[i][1].record(stream)
+        call(i, launch | bb.BB_PHASE_MERGE)
+        e[i][2].record(stream)
+    torch.cuda.synchronize()
+    units_ms = float(np.mean([a.elapsed_time(b_) for a, b_, _ in e]))
+    merge_ms = float(np.mean([b_.elapsed_time(c) for _, b_, c in e]))
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flops = useful_flops(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    tokens_per_s = w.tokens / (ms_per_step * 1e-3)
     alg_bytes = algorithmic_bytes(w)
-    launch_ms = float(np.mean(per_launch_ms))
-
-    if args.launch == "fused":
-        kernel, kflops = "bb_fused_kernel", flops
-    else:
-        kernel, kflops = "bb_middle_rows_kernel", flops_m   # per-step events span both launches
-    achieved = kflops / (launch_ms * 1e-3) / 1e12
+    kernel = MAIN_KERNEL if args.launch == "fused" else "bb_global_rows_kernel+bb_middle_rows_kernel"
+    achieved = flops / (units_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = committed_traffic(kernel, w.name) if args.launch == "fused" else None
+    traffic = committed_traffic(w.name) if args.launch == "fused" else None
 
     out = {
         "metric": METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
-        "tokens_per_s": round(tokens_per_s, 1),
+        "tokens_per_s": round(w.tokens / (ms_per_step * 1e-3), 1),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -221,7 +321,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) draws, shapes of the BigBird-base attention layer)",
+        "data": "synthetic (seeded N(0,1) draws shaped like the BigBird-base attention layer)",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "block": w.block, "r": w.r,
             "pad": w.pad, "mode": args.mode, "input_sets": n_sets, "launch": args.launch,
@@ -237,12 +337,15 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "launch_us_mean": round(launch_ms * 1e3, 3),
-            "hbm_algorithmic_GBps": round(alg_bytes / (launch_ms * 1e-3) / 1e9, 1),
-            "hbm_algorithmic_frac": round(alg_bytes / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "launch_us_mean": round(units_ms * 1e3, 3),
+            "merge_us_mean": round(merge_ms * 1e3, 3),
+            "hbm_algorithmic_GBps": round(alg_bytes / (units_ms * 1e-3) / 1e9, 1),
+            "hbm_algorithmic_frac": round(alg_bytes / (units_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "cpu_baseline": None,
     }
+    if traffic is not None:
+        out["roofline"]["traffic_GBps"] = round(traffic / (units_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, ri, args.cpu_budget_s)
     print(json.dumps(out), flush=True)

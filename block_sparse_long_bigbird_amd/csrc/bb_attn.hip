@@ -750,16 +750,23 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
   using C = Cfg<T, BS>;
   const int per_g = 2 * a.n_s * C::QSPLIT, per_m = (a.nb - 2) * C::QSPLIT;
   const unsigned bhs = static_cast<unsigned>(B) * static_cast<unsigned>(H);
-  if (flags == BB_LAUNCH_SPLIT) {
-    bb_global_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_g), dim3(C::NT), 0, stream>>>(a);
+  const bool units = !(flags & BB_PHASE_MERGE) || (flags & BB_PHASE_UNITS);
+  const bool merge = !(flags & BB_PHASE_UNITS) || (flags & BB_PHASE_MERGE);
+  if (units) {
+    if (flags & BB_LAUNCH_SPLIT) {
+      bb_global_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_g), dim3(C::NT), 0, stream>>>(a);
+      if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+      bb_middle_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_m), dim3(C::NT), 0, stream>>>(a);
+    } else {
+      bb_fused_kernel<T, BS, HAS_PAD><<<dim3(bhs * (per_g + per_m)), dim3(C::NT), 0, stream>>>(a);
+    }
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-    bb_middle_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_m), dim3(C::NT), 0, stream>>>(a);
-  } else {
-    bb_fused_kernel<T, BS, HAS_PAD><<<dim3(bhs * (per_g + per_m)), dim3(C::NT), 0, stream>>>(a);
   }
-  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-  bb_global_merge_kernel<T, BS><<<dim3(bhs * 2 * (BS / 16)), dim3(256), 0, stream>>>(a);
-  return hipGetLastError() == hipSuccess ? BB_OK : BB_ERR_HIP;
+  if (merge) {
+    bb_global_merge_kernel<T, BS><<<dim3(bhs * 2 * (BS / 16)), dim3(256), 0, stream>>>(a);
+    if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  }
+  return BB_OK;
 }
 
 }  // namespace
@@ -794,7 +801,7 @@ extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, c
                                   void* out, int dtype, void* workspace, size_t workspace_bytes,
                                   void* stream, unsigned flags) {
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
-  if (flags != BB_LAUNCH_FUSED && flags != BB_LAUNCH_SPLIT) return BB_ERR_SHAPE;
+  if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE)) return BB_ERR_SHAPE;
   int nb = 0;
   const int st = check_shape(B, H, L, d, block, r, &nb);
   if (st != BB_OK) return st;

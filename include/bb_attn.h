@@ -46,9 +46,15 @@ typedef enum {
 
 typedef enum { BB_FP32 = 0, BB_BF16 = 1 } bb_dtype;
 
-/* Flags for bb_attn_forward_ex. */
+/* Flags for bb_attn_forward_ex.  One launch mode, optionally one phase. */
 #define BB_LAUNCH_FUSED 0u /* global-row and middle-block work units share one grid, then the split-K merge */
 #define BB_LAUNCH_SPLIT 1u /* global-row kernel, middle-block kernel, split-K merge: three launches */
+#define BB_PHASE_UNITS 2u  /* enqueue only the work-unit launch(es); the output rows of the two
+                              global blocks are not written yet */
+#define BB_PHASE_MERGE 4u  /* enqueue only the split-K merge that writes the global rows; it must
+                              follow a BB_PHASE_UNITS call with the same arguments and workspace
+                              on the same stream */
+                           /* neither phase bit, or both: the whole forward */
 
 /* Version of this ABI (BB_ABI_VERSION of the built library). */
 int bb_abi_version(void);
@@ -125,8 +131,10 @@ int bb_attn_forward(const void* q, const void* k, const void* v, const uint8_t* 
                     void* out, int dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
 
-/* bb_attn_forward with launch flags (BB_LAUNCH_FUSED or BB_LAUNCH_SPLIT);
- * both give the same result bit for bit.  Unknown flags: BB_ERR_SHAPE. */
+/* bb_attn_forward with flags: a launch mode (BB_LAUNCH_FUSED or BB_LAUNCH_SPLIT,
+ * which give the same result bit for bit) and optionally one phase
+ * (BB_PHASE_UNITS or BB_PHASE_MERGE) for callers that time the phases or
+ * enqueue other work between them.  Unknown flags: BB_ERR_SHAPE. */
 int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
                        const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
                        void* out, int dtype, void* workspace, size_t workspace_bytes,

@@ -145,6 +145,26 @@ def test_split_launch_matches_fused_bitwise(dev, w):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("w", [SMALL[6], SMALL[11]], ids=lambda w: w.name)
+def test_two_phase_call_matches_single_call(dev, w):
+    """BB_PHASE_UNITS then BB_PHASE_MERGE on the same stream == one full call, bit for bit."""
+    say(f"case two-phase {w.name}")
+    inputs = make_inputs(w)
+    a, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_FUSED, inputs=inputs)
+    q, k, v, pad = inputs
+    ri = torch.from_numpy(bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)).to(dev)
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    dpad = None if pad is None else pad.to(dev)
+    for launch in (bb.BB_LAUNCH_FUSED, bb.BB_LAUNCH_SPLIT):
+        out = torch.full_like(dq, float("nan"))
+        ws = poisoned_workspace(w, dev)
+        for phase in (bb.BB_PHASE_UNITS, bb.BB_PHASE_MERGE):
+            bb.bb_attn_forward(dq, dk, dv, dpad, ri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws,
+                               flags=launch | phase)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.float().cpu().numpy(), a)
+
+
 def test_deterministic_and_workspace_reuse(dev):
     """Same call twice gives identical bits; the workspace is ready for the next call,
     also for a different, smaller shape."""
