@@ -420,35 +420,23 @@ __device__ __forceinline__ int tile_at(const TileList& tl, int u) {
   return e < 1 ? 1 : (e > tl.nb - 2 ? tl.nb - 2 : e);   // never read outside the sequence
 }
 
-// Carried from one tile step to the next: the scores and V operands of the
-// previous tile, whose softmax and PV run while the next tile's score MFMAs do.
-template <typename T>
-struct Carry {
-  f32x16 s;
-  VOp<T> v;
-};
-
-// Step u of the software-pipelined tile loop (tile u sits in stage S = u % 2;
-// tile_u and tile_fill are the ids of tiles u and u+1).  Reads the carry of
-// tile u-1 from `prev` and leaves tile u's in `next` (two register sets used
-// alternately, so nothing is copied).  u == ntiles only drains `prev`.
+// Step u of the tile loop: tile u sits in stage S = u % 2; tile_u and
+// tile_fill are the ids of tiles u and u+1.
 template <typename T, int BS, int S, bool HAS_PAD>
-__device__ __forceinline__ void step(WaveState& ws, const Carry<T>& prev, Carry<T>& next,
-                                     const u32x4 (&qop)[Cfg<T, BS>::QC], int u, int ntiles,
-                                     int tile_u, int tile_fill, gchar_ptr kbh, gchar_ptr vbh,
-                                     const uint8_t* pad_b, int wave, int lane, int kbase) {
-  if (u < ntiles) {
-    // This wave's DMA of tile u has landed and its LDS reads of the previous
-    // step are complete (vmcnt = lgkmcnt = 0); after the barrier every wave's
-    // part of tile u is visible and the stage of tile u-1 is free to refill.
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
-    ring_barrier();
-    if (u + 1 < ntiles) issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
-    const uint8_t* pad_t = HAS_PAD ? pad_b + static_cast<size_t>(tile_u) * BS : nullptr;
-    next.v = load_v<T, BS, S>(kbase, lane);
-    next.s = scores<T, BS, S, HAS_PAD>(qop, pad_t, kbase, lane);
-  }
-  if (u > 0) softmax_pv<T>(ws, prev.s, prev.v);
+__device__ __forceinline__ void step(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC], int u,
+                                     int ntiles, int tile_u, int tile_fill, gchar_ptr kbh,
+                                     gchar_ptr vbh, const uint8_t* pad_b, int wave, int lane,
+                                     int kbase) {
+  // This wave's DMA of tile u has landed and its LDS reads of the previous
+  // step are complete (vmcnt = lgkmcnt = 0); after the barrier every wave's
+  // part of tile u is visible and the stage of tile u-1 is free to refill.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+  ring_barrier();
+  if (u + 1 < ntiles) issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
+  const uint8_t* pad_t = HAS_PAD ? pad_b + static_cast<size_t>(tile_u) * BS : nullptr;
+  const VOp<T> vo = load_v<T, BS, S>(kbase, lane);
+  const f32x16 s = scores<T, BS, S, HAS_PAD>(qop, pad_t, kbase, lane);
+  softmax_pv<T>(ws, s, vo);
 }
 
 __device__ __forceinline__ void store_row8(char* dst, const float* x, __bf16*) {
@@ -536,25 +524,21 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
   }
   ws.m = -__builtin_inff();
   ws.l = 0.0f;
-  Carry<T> cy0, cy1;
 
   // ---- tile loop: trips of 12 straight-line steps -----------------------------
-  // Step u reads the carry of tile u-1 and writes tile u's, alternating two
-  // register sets; step u == ntiles drains the last carry.  Units of the
-  // usual shapes have at most 11 tiles, so one trip covers them and the loop
-  // back edge -- where the compiler's LDS-DMA wait tracking turns
+  // Units of the usual shapes have at most 12 tiles, so one trip covers them
+  // and the loop back edge -- where the compiler's LDS-DMA wait tracking turns
   // conservative -- is not taken.  Tile ids are computed once per trip.
   constexpr int TRIP = 12;
-  static_assert(TRIP % 2 == 0, "trip must keep stage and parity aligned");
-  for (int u = 0; u <= ntiles; u += TRIP) {
+  static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
+  for (int u = 0; u < ntiles; u += TRIP) {
     int tid_[TRIP + 1];
 #pragma unroll
     for (int k = 0; k < TRIP + 1; ++k) tid_[k] = u + k < ntiles ? tile_at(tl, u + k) : 0;
 #define BB_STEP(k)                                                                               \
-  if (u + (k) <= ntiles)                                                                         \
-    step<T, BS, (k) % 2, HAS_PAD>(ws, (k) % 2 ? cy0 : cy1, (k) % 2 ? cy1 : cy0, qop, u + (k),      \
-                                  ntiles, tid_[k], tid_[(k) + 1], kbh, vbh, pad_b, wave, lane,     \
-                                  kbase);
+  if (u + (k) < ntiles)                                                                          \
+    step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k), ntiles, tid_[k], tid_[(k) + 1], kbh, vbh,      \
+                                  pad_b, wave, lane, kbase);
     BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
     BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
@@ -628,37 +612,58 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
 
 // Split-K merge of the two global query blocks of one (b, h): the partials of
 // the n_s key chunks (row max m_s, row sum l_s, unnormalised O_s) combine as
-// out = sum_s 2^((m_s - m)c) O_s / sum_s 2^((m_s - m)c) l_s, m = max_s m_s,
-// accumulated in chunk order with a running maximum (deterministic).  Runs as
-// its own launch after the global-row units, so their partials are complete
-// and visible without any in-kernel fence.  One thread per 4 output values;
-// a workgroup covers 16 query rows of one global block.
+// out = sum_s 2^((m_s - m)c) O_s / sum_s 2^((m_s - m)c) l_s, m = max_s m_s.
+// Runs as its own launch after the global-row units, so their partials are
+// complete and visible without any in-kernel fence.  A workgroup covers 4
+// query rows x 16 float4 columns; the chunks of each output are split over
+// kMergeSplit threads (strided), whose (m, l, O) are then combined through
+// LDS in a fixed order, so the result is deterministic.
+constexpr int kMergeSplit = 4;
+
 template <typename T, int BS>
 __global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
   constexpr int ROWB = kD * sizeof(T);
-  constexpr int SLICES = BS / 16;
+  constexpr int SLICES = BS / 4;
+  __shared__ float s_m[kMergeSplit][64], s_l[kMergeSplit][64];
+  __shared__ f32x4 s_o[kMergeSplit][64];
   const int slice = blockIdx.x % SLICES, gblk = blockIdx.x / SLICES;
   const int bh = gblk >> 1, gsel = gblk & 1;
   const int qb = gsel ? a.nb - 1 : 0;
-  const int ql = slice * 16 + (threadIdx.x >> 4), dq = threadIdx.x & 15;
+  const int sg = threadIdx.x >> 6, o = threadIdx.x & 63;      // chunk group, output slot
+  const int ql = slice * 4 + (o >> 4), dq = o & 15;
   const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.n_s;
-  float m = -__builtin_inff(), den = 0.0f;
+  float m = -__builtin_inff();
+  for (int s = sg; s < a.n_s; s += kMergeSplit) m = fmaxf(m, a.pm[(base + s) * BS + ql]);
+  float den = 0.0f;
   f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-  for (int s = 0; s < a.n_s; ++s) {
-    const size_t pi = (base + s) * BS + ql;
-    const float ms = a.pm[pi], ls = a.pl[pi];
-    const f32x4 os = *reinterpret_cast<const f32x4*>(a.po + pi * kD + dq * 4);
-    const float mn = fmaxf(m, ms);
-    const float wa = __builtin_amdgcn_exp2f((m - mn) * kScaleLog2);
-    const float wb = __builtin_amdgcn_exp2f((ms - mn) * kScaleLog2);
-    den = den * wa + ls * wb;
-    num = num * wa + os * wb;
-    m = mn;
+  if (m != -__builtin_inff()) {
+    for (int s = sg; s < a.n_s; s += kMergeSplit) {
+      const size_t pi = (base + s) * BS + ql;
+      const float w = __builtin_amdgcn_exp2f((a.pm[pi] - m) * kScaleLog2);
+      den += w * a.pl[pi];
+      num += w * *reinterpret_cast<const f32x4*>(a.po + pi * kD + dq * 4);
+    }
+  }
+  s_m[sg][o] = m;
+  s_l[sg][o] = den;
+  s_o[sg][o] = num;
+  __syncthreads();
+  if (sg != 0) return;
+  float mm = s_m[0][o];
+#pragma unroll
+  for (int g = 1; g < kMergeSplit; ++g) mm = fmaxf(mm, s_m[g][o]);
+  float dd = 0.0f;
+  f32x4 nn = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int g = 0; g < kMergeSplit; ++g) {
+    if (s_m[g][o] == -__builtin_inff()) continue;           // group had no chunk
+    const float w = __builtin_amdgcn_exp2f((s_m[g][o] - mm) * kScaleLog2);
+    dd += w * s_l[g][o];
+    nn += w * s_o[g][o];
   }
   store_f32x4(a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + ql) * ROWB +
                   dq * 4 * sizeof(T),
-              num * (1.0f / den), static_cast<T*>(nullptr));
+              nn * (1.0f / dd), static_cast<T*>(nullptr));
 }
 
 // Decode a work unit.  Per (b, h): the global units (block 0 chunks, then
@@ -763,7 +768,7 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   if (merge) {
-    bb_global_merge_kernel<T, BS><<<dim3(bhs * 2 * (BS / 16)), dim3(256), 0, stream>>>(a);
+    bb_global_merge_kernel<T, BS><<<dim3(bhs * 2 * (BS / 4)), dim3(256), 0, stream>>>(a);
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   return BB_OK;
