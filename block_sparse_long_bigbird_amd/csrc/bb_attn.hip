@@ -91,8 +91,7 @@ struct Cfg {
   static constexpr int MERGE_ML = (WK / 2) * WQ * 2 * 64 * 4;   // row max and row sum
   static_assert(DMA_MAT * 64 * NW == BS * CPR, "tile DMA must split evenly over waves");
   static_assert(CPR % 8 == 0, "swizzles act on groups of 8 chunks");
-  static_assert(MERGE_O <= 2 * TILE, "merge area must fit in one stage");
-  static_assert(MERGE_O + MERGE_ML <= 2 * TILE, "merge area (two stages)");
+  static_assert(MERGE_O <= TILE, "each half of the merged O must fit in one K or V tile");
 };
 
 struct Args {
@@ -137,14 +136,6 @@ __device__ __forceinline__ int perm_row(int i) {
   return 16 * (a >> 1) + 8 * gg + 4 * (a & 1) + c;
 }
 
-// XCD-aware work order: hardware hands consecutive workgroup ids to the 8 XCDs
-// round robin; remap so each XCD runs a contiguous range of work units (one
-// (batch, head) after another), which keeps that unit's K/V in its own L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int q = n >> 3, rem = n & 7, x = bid & 7, k = bid >> 3;
-  return x * q + (x < rem ? x : rem) + k;
-}
-
 __device__ __forceinline__ bool has_zero_byte(uint64_t x) {
   return ((x - 0x0101010101010101ull) & ~x & 0x8080808080808080ull) != 0;
 }
@@ -166,16 +157,45 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Copy key tile `tile` of K and V from HBM straight into LDS stage S.  Each DMA instruction moves 64 x 16 bytes; lane l of
-// instruction i fills physical chunk slot 64*i + l, so it fetches the logical
-// chunk that the swizzle places there.  Rows stay contiguous 128-byte runs.
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// accesses are complete (lgkmcnt = 0), vector-memory operations may stay in
+// flight.  (__syncthreads() would also drain them: its fence waits for vmcnt.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0); vmcnt, expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy key tile `tile` of K and V from HBM straight into LDS stage S.  Each
+// DMA instruction moves 64 x 16 bytes; lane l of instruction i fills physical
+// chunk slot 64*i + l, so it fetches the logical chunk that the swizzle places
+// there.  Rows stay contiguous 128-byte runs.
+//
+// The DMA instructions are written as asm: the compiler then does not know
+// that they write LDS and inserts none of its own (conservative) waits for
+// them before LDS accesses.  Every wait for them is explicit: the vmcnt(0) at
+// the start of each step, before the workgroup barrier that publishes the tile.
 typedef const __attribute__((address_space(1))) char* gchar_ptr;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
+}
+
+// One 64 x 16-byte DMA: lane offsets `voff` (32-bit) on the wave-uniform
+// global base `g`, into LDS at the wave-uniform address `m0` (+16 per lane).
+// The s_nop covers the one wait state an M0 write needs before an LDS DMA.
+__device__ __forceinline__ void dma16(gchar_ptr g, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(g), "{m0}"(m0) : "memory");
+}
 
 template <typename T, int BS, int S>
 __device__ __forceinline__ void issue_tile(gchar_ptr kbh, gchar_ptr vbh, int tile, int wave, int lane) {
   using C = Cfg<T, BS>;
   const gchar_ptr kt = kbh + static_cast<size_t>(tile) * C::TILE;
   const gchar_ptr vt = vbh + static_cast<size_t>(tile) * C::TILE;
+  const uint32_t lk = lds_addr(Stage<T, BS, S>::k()), lv = lds_addr(Stage<T, BS, S>::v());
 #pragma unroll
   for (int jj = 0; jj < C::DMA_MAT; ++jj) {
     const int ins = wave + C::NW * jj;
@@ -183,10 +203,8 @@ __device__ __forceinline__ void issue_tile(gchar_ptr kbh, gchar_ptr vbh, int til
     const int row = slot / C::CPR, p = slot % C::CPR;
     const uint32_t ko = row * C::ROWB + ((p ^ swz_k(row)) << 4);
     const uint32_t vo = row * C::ROWB + ((p ^ swz_v(row)) << 4);
-    __builtin_amdgcn_global_load_lds((const glb_void_t*)(kt + ko),
-                                     (lds_void_t*)(Stage<T, BS, S>::k() + ins * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const glb_void_t*)(vt + vo),
-                                     (lds_void_t*)(Stage<T, BS, S>::v() + ins * 1024), 16, 0, 0);
+    dma16(kt, ko, __builtin_amdgcn_readfirstlane(lk + ins * 1024));
+    dma16(vt, vo, __builtin_amdgcn_readfirstlane(lv + ins * 1024));
   }
 }
 
@@ -224,39 +242,67 @@ __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 acc, float*) 
 typedef const __attribute__((address_space(4))) uint64_t* const_u64_ptr;
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
-// S^T = K . Q^T (+ key bias) for this wave's 32-key subtile of stage S.
-template <typename T, int BS, int S, bool HAS_PAD>
-__device__ __forceinline__ f32x16 scores(const u32x4 (&qop)[Cfg<T, BS>::QC], const uint8_t* pad_t,
-                                         int kbase, int lane) {
+// S^T = K . Q^T for this wave's 32-key subtile of stage S (no bias yet).
+template <typename T, int BS, int S>
+__device__ __forceinline__ f32x16 scores(const u32x4 (&qop)[Cfg<T, BS>::QC], int kbase, int lane) {
   using C = Cfg<T, BS>;
   const int j = lane & 31, g = lane >> 5;
   const char* sk = Stage<T, BS, S>::k();
   const int row = kbase + perm_row(j);
   const int sw = swz_k(row);
   u32x4 a[C::QC];
+  if constexpr (C::QC == 4) {
+    // All four reads in flight before one wait (issued one by one, each
+    // would wait for its own LDS round trip).
+    uint32_t ad[4];
 #pragma unroll
-  for (int x = 0; x < C::QC; ++x)
-    a[x] = *reinterpret_cast<const u32x4*>(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
+    for (int x = 0; x < 4; ++x) ad[x] = lds_addr(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
+    asm volatile(
+        "ds_read_b128 %0, %4\n"
+        "ds_read_b128 %1, %5\n"
+        "ds_read_b128 %2, %6\n"
+        "ds_read_b128 %3, %7\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  } else {
+#pragma unroll
+    for (int x = 0; x < C::QC; ++x)
+      a[x] = *reinterpret_cast<const u32x4*>(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
+  }
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 #pragma unroll
   for (int x = 0; x < C::QC; ++x) acc = mfma_qk(a[x], qop[x], acc, static_cast<T*>(nullptr));
-  if constexpr (HAS_PAD) {
-    // The 32 pad bytes of this subtile, read with wave-uniform (scalar) loads;
-    // the -10000 offset (in q.k units) is added only where a key is padding.
-    const const_u64_ptr pw = (const_u64_ptr)(pad_t + kbase);
-    const uint64_t p0 = pw[0], p1 = pw[1], p2 = pw[2], p3 = pw[3];
-    if (has_zero_byte(p0) || has_zero_byte(p1) || has_zero_byte(p2) || has_zero_byte(p3)) {
-      const uint64_t w0 = g ? p1 : p0, w1 = g ? p3 : p2;
+  return acc;
+}
+
+// The 32 pad bytes of this wave's subtile (wave-uniform, scalar loads).
+struct PadWords {
+  uint64_t p[4];
+};
+__device__ __forceinline__ PadWords load_pad(const uint8_t* pad_t, int kbase) {
+  const const_u64_ptr pw = (const_u64_ptr)(pad_t + kbase);
+  PadWords w;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        acc[v] += ((w0 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
-        acc[8 + v] += ((w1 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
-      }
+  for (int i = 0; i < 4; ++i) w.p[i] = pw[i];
+  return w;
+}
+
+// Key bias: -10000 (in q.k units) on the logits of padded keys.  Taken only
+// when the subtile has a padded key.
+__device__ __forceinline__ void apply_pad(f32x16& acc, const PadWords& w, int lane) {
+  if (has_zero_byte(w.p[0]) || has_zero_byte(w.p[1]) || has_zero_byte(w.p[2]) || has_zero_byte(w.p[3])) {
+    const int g = lane >> 5;
+    const uint64_t w0 = g ? w.p[1] : w.p[0], w1 = g ? w.p[3] : w.p[2];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      acc[v] += ((w0 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
+      acc[8 + v] += ((w1 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
     }
   }
-  return acc;
 }
 
 // V^T operands of this wave's subtile of stage S.
@@ -321,39 +367,37 @@ __device__ __forceinline__ VOp<T> load_v(int kbase, int lane) {
   return vo;
 }
 
-// Online softmax of one score subtile (lane = query row, 16 of its 32 keys)
-// and O^T += V^T . P^T.  Registers only.
-template <typename T>
-__device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, const VOp<T>& vo) {
-  // P = 2^((s - m) c) against the running max m first; the tile's own max
-  // is reduced meanwhile, and only if it exceeds m by more than tau/c (rare)
-  // are O and l rescaled and P recomputed.  Keeps the exps off the critical
-  // path of the max reduction.
-  if (ws.m == -__builtin_inff()) {   // first tile: start the running max from it
-    float mm = acc[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mm = fmaxf(mm, acc[v]);
-    const auto sw0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mm), __float_as_uint(mm), false, false);
-    ws.m = fmaxf(__uint_as_float(sw0[0]), __uint_as_float(sw0[1]));
-  }
-  float mc = ws.m * kScaleLog2;
-  float p[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
+// Row max of this subtile's 16 scores per lane (and `m0`), over both lane
+// halves (the two 16-key halves of the query row).
+__device__ __forceinline__ float subtile_max(const f32x16& acc, float m0) {
   float m8[6];
   m8[0] = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
   m8[1] = fmaxf(fmaxf(acc[3], acc[4]), acc[5]);
   m8[2] = fmaxf(fmaxf(acc[6], acc[7]), acc[8]);
   m8[3] = fmaxf(fmaxf(acc[9], acc[10]), acc[11]);
   m8[4] = fmaxf(fmaxf(acc[12], acc[13]), acc[14]);
-  m8[5] = fmaxf(acc[15], ws.m);
-  float mloc = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), m8[2]), fmaxf(fmaxf(m8[3], m8[4]), m8[5]));
-  {
-    const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc),
-                                                      false, false);
-    mloc = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
-  }
-  if (__any((mloc - ws.m) * kScaleLog2 > kRescaleTau)) {
+  m8[5] = fmaxf(acc[15], m0);
+  float m = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), m8[2]), fmaxf(fmaxf(m8[3], m8[4]), m8[5]));
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Online softmax of one score subtile (lane = query row, 16 of its 32 keys)
+// and O^T += V^T . P^T.  Registers only.  `first`: the unit's first tile
+// (wave-uniform), whose max starts the running max.
+template <typename T>
+__device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, const VOp<T>& vo, bool first) {
+  // P = 2^((s - m) c) against the running max m first; the tile's own max
+  // is reduced meanwhile, and only if it exceeds m by more than tau/c (rare)
+  // are O and l rescaled and P recomputed.  Keeps the exps off the critical
+  // path of the max reduction.
+  if (first) ws.m = subtile_max(acc, acc[15]);
+  float p[16];
+  float mc = ws.m * kScaleLog2;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
+  const float mloc = subtile_max(acc, ws.m);
+  if (__any(mloc - ws.m > kRescaleTau / kScaleLog2)) {
     const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -403,11 +447,13 @@ __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, con
 }
 
 // Key tiles of a work unit, computed on the fly (all values wave-uniform).
+// (No bool members and no padding: these structs are copied around the unit
+// loop, and padding bytes would leave a small private object behind.)
 struct TileList {
   int first;             // global unit: first tile of its chunk; middle unit: band start
   int nwin;              // middle unit: band blocks inside 1..nb-2
   int nb;
-  bool global;
+  int global;            // 1: global unit, 0: middle unit
   const_i32_ptr rand;    // middle unit: its row of the random-block table
 };
 
@@ -420,23 +466,116 @@ __device__ __forceinline__ int tile_at(const TileList& tl, int u) {
   return e < 1 ? 1 : (e > tl.nb - 2 ? tl.nb - 2 : e);   // never read outside the sequence
 }
 
+// A decoded work unit (all values wave-uniform).  Per (b, h) the units are the
+// global units (block 0 chunks, then block nb-1 chunks; QSPLIT row slices
+// each) followed by the middle units (nb-2 blocks, QSPLIT row slices each).
+// `kind` selects which of them a grid covers: 0 = all, 1 = global units only,
+// 2 = middle units only.  A unit covers query rows [qb*BS + qh*64, +64) of
+// (b, h).  gsel < 0: middle query block qb, finalised in place.  gsel in
+// {0, 1}: global query block qb (0 or nb-1) against key chunk `chunk` of the
+// split-K, written as a partial for the merge kernel.
+struct Unit {
+  size_t off;            // byte offset of (b, h) in q, k, v and out: bh * L * ROWB
+  size_t pbase;          // global unit: partial row index of its first query row
+  int b, q0, gsel, ntiles;   // q0: first query row of the unit
+  TileList tl;
+};
+
+template <typename T, int BS, int kind>
+__device__ __forceinline__ Unit decode_unit(const Args& a, int unit) {
+  constexpr int QS = Cfg<T, BS>::QSPLIT;
+  const int n_g = kind == 2 ? 0 : 2 * a.n_s * QS;
+  const int n_m = kind == 1 ? 0 : (a.nb - 2) * QS;
+  const int per_bh = n_g + n_m;
+  const int bh = unit / per_bh, u = unit % per_bh;
+  const int nb = a.nb, h = bh % a.H;
+  Unit w;
+  w.off = static_cast<size_t>(bh) * a.L * Cfg<T, BS>::ROWB;
+  w.b = bh / a.H;
+  w.tl.nb = nb;
+  if (u < n_g) {
+    w.gsel = u / (a.n_s * QS);
+    const int rem = u % (a.n_s * QS);
+    const int chunk = rem / QS, qh = rem % QS;
+    w.q0 = (w.gsel ? nb - 1 : 0) * BS + qh * Cfg<T, BS>::QROWS;
+    w.pbase = ((static_cast<size_t>(bh) * 2 + w.gsel) * a.n_s + chunk) * BS + qh * Cfg<T, BS>::QROWS;
+    w.tl.global = 1;
+    w.tl.first = chunk * kChunkTiles;
+    w.tl.nwin = 0;
+    w.tl.rand = nullptr;
+    w.ntiles = nb - w.tl.first < kChunkTiles ? nb - w.tl.first : kChunkTiles;
+  } else {
+    w.gsel = -1;
+    const int qb = (u - n_g) / QS + 1, qh = (u - n_g) % QS;
+    w.q0 = qb * BS + qh * Cfg<T, BS>::QROWS;
+    w.pbase = 0;
+    const int lo = qb - 1 < 1 ? 1 : qb - 1;          // band without the global blocks
+    const int hi = qb + 1 > nb - 2 ? nb - 2 : qb + 1;
+    w.tl.global = 0;
+    w.tl.first = lo;
+    w.tl.nwin = hi - lo + 1;
+    w.tl.rand = (const_i32_ptr)(a.rand_idx + (static_cast<size_t>(h) * (nb - 2) + (qb - 1)) * a.r);
+    w.ntiles = 2 + w.tl.nwin + a.r;
+  }
+  return w;
+}
+
+// This wave's 32 query rows of unit w as the B operand of the score products.
+template <typename T, int BS>
+__device__ __forceinline__ void load_q(const Args& a, size_t off, int q0, int wq, int lane,
+                                       u32x4 (&qop)[Cfg<T, BS>::QC]) {
+  using C = Cfg<T, BS>;
+  const char* qrow = a.q + off + static_cast<size_t>(q0 + wq * 32 + (lane & 31)) * C::ROWB;
+#pragma unroll
+  for (int x = 0; x < C::QC; ++x)
+    qop[x] = *reinterpret_cast<const u32x4*>(qrow + (2 * x + (lane >> 5)) * 16);
+}
+
+// Where the next unit's first tile comes from, for the prefetch on the last
+// step of the current unit.
+struct NextUnit {
+  size_t off;            // its (b, h) byte offset
+  int q0;                // its first query row
+  int tile0;             // its first key tile
+  int pf;                // 1: prefetch (the current unit has an even tile count and a successor)
+  int unused;
+};
+
 // Step u of the tile loop: tile u sits in stage S = u % 2; tile_u and
-// tile_fill are the ids of tiles u and u+1.
+// tile_fill are the ids of tiles u and u+1.  On the last step
+// of a unit with an even tile count (S == 1) the next unit is prefetched: its
+// tile 0 into stage 0 and, once this step's score products have consumed Q,
+// its Q rows into qop.
 template <typename T, int BS, int S, bool HAS_PAD>
-__device__ __forceinline__ void step(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC], int u,
-                                     int ntiles, int tile_u, int tile_fill, gchar_ptr kbh,
-                                     gchar_ptr vbh, const uint8_t* pad_b, int wave, int lane,
-                                     int kbase) {
+__device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC], int u, int ntiles,
+                                     int tile_u, int tile_fill, gchar_ptr kbh, gchar_ptr vbh,
+                                     const uint8_t* pad_b, int wave, int lane, int kbase,
+                                     const NextUnit& nx, const Args& a, int wq) {
   // This wave's DMA of tile u has landed and its LDS reads of the previous
-  // step are complete (vmcnt = lgkmcnt = 0); after the barrier every wave's
+  // step are complete (vmcnt = lgkmcnt = 0; on a unit's first step this also
+  // covers the previous unit's output stores); after the barrier every wave's
   // part of tile u is visible and the stage of tile u-1 is free to refill.
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_waitcnt(7 << 4);
   ring_barrier();
-  if (u + 1 < ntiles) issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
-  const uint8_t* pad_t = HAS_PAD ? pad_b + static_cast<size_t>(tile_u) * BS : nullptr;
+  // Critical path first: K reads and the score products.  The V^T reads and
+  // the DMA of the next tile are issued while the products run.
+  PadWords pw;
+  if constexpr (HAS_PAD) pw = load_pad(pad_b + static_cast<size_t>(tile_u) * BS, kbase);
+  f32x16 s = scores<T, BS, S>(qop, kbase, lane);
   const VOp<T> vo = load_v<T, BS, S>(kbase, lane);
-  const f32x16 s = scores<T, BS, S, HAS_PAD>(qop, pad_t, kbase, lane);
-  softmax_pv<T>(ws, s, vo);
+  const bool last = u + 1 == ntiles;
+  if (!last)
+    issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
+  else if (S == 1 && nx.pf)
+    issue_tile<T, BS, 0>((gchar_ptr)(a.k) + nx.off, (gchar_ptr)(a.v) + nx.off, nx.tile0, wave, lane);
+  if constexpr (HAS_PAD) apply_pad(s, pw, lane);
+  if (S == 1 && last && nx.pf) {
+    // Q is dead after the score products: refill it for the next unit.  The
+    // empty asm ties the loads after those products.
+    asm volatile("" : "+v"(s) : : "memory");
+    load_q<T, BS>(a, nx.off, nx.q0, wq, lane, qop);
+  }
+  softmax_pv<T>(ws, s, vo, u == 0);
 }
 
 __device__ __forceinline__ void store_row8(char* dst, const float* x, __bf16*) {
@@ -451,9 +590,9 @@ __device__ __forceinline__ void store_row8(char* dst, const float* x, __bf16*) {
   *reinterpret_cast<bf16x8*>(dst) = o;
 }
 __device__ __forceinline__ void store_row8(char* dst, const float* x, float*) {
-  f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
-  reinterpret_cast<f32x4*>(dst)[0] = a;
-  reinterpret_cast<f32x4*>(dst)[1] = b;
+  f32x4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+  reinterpret_cast<f32x4*>(dst)[0] = lo;
+  reinterpret_cast<f32x4*>(dst)[1] = hi;
 }
 
 __device__ __forceinline__ void store_f32x4(char* dst, f32x4 x, __bf16*) {
@@ -466,91 +605,29 @@ __device__ __forceinline__ void store_f32x4(char* dst, f32x4 x, float*) {
   *reinterpret_cast<f32x4*>(dst) = x;
 }
 
-// One work unit on (b, h): query rows [qb*BS + qh*64, +64).  gsel < 0: middle
-// query block qb, finalised in place.  gsel in {0, 1}: global query block qb
-// (0 or nb-1), key chunk `chunk` of split-K, written as a partial for the
-// merge kernel.
-template <typename T, int BS, bool HAS_PAD>
-__device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, int qh, int gsel,
-                                         int chunk) {
+// Row max / row sum exchange area of the key-group merge.
+template <typename T, int BS>
+struct MergeML {
+  static __device__ __forceinline__ float* buf() {
+    __shared__ float b[Cfg<T, BS>::MERGE_ML / 4];
+    return b;
+  }
+};
+
+// End of a unit: merge the key groups of each query group (tree over LDS,
+// O through stage S -- the stage of the unit's last tile -- and (max, sum)
+// through MergeML), then write the output rows (middle unit) or the partial
+// (global unit).
+template <typename T, int BS, int S>
+__device__ __forceinline__ void finalize(WaveState& ws, const Args& a, const Unit& w, int wq, int wk,
+                                        int lane) {
   using C = Cfg<T, BS>;
-  constexpr int ROWB = C::ROWB;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wq = wave % C::WQ, wk = wave / C::WQ;
-  const int j = lane & 31, g = lane >> 5;
-  const int nb = a.nb, L = a.L;
-  const size_t bh = static_cast<size_t>(b) * a.H + h;
-  const char* qbh = a.q + bh * L * ROWB;
-  const gchar_ptr kbh = (gchar_ptr)(a.k) + bh * L * ROWB;
-  const gchar_ptr vbh = (gchar_ptr)(a.v) + bh * L * ROWB;
-  const uint8_t* pad_b = HAS_PAD ? a.pad + static_cast<size_t>(b) * L : nullptr;
-  const int kbase = wk * 32;             // this wave's 32 keys of every tile
-
-  // ---- key-tile list ----------------------------------------------------------
-  TileList tl;
-  tl.nb = nb;
-  tl.global = gsel >= 0;
-  int ntiles;
-  if (gsel < 0) {
-    const int lo = qb - 1 < 1 ? 1 : qb - 1;            // band without the global blocks
-    const int hi = qb + 1 > nb - 2 ? nb - 2 : qb + 1;
-    tl.first = lo;
-    tl.nwin = hi - lo + 1;
-    tl.rand = (const_i32_ptr)(a.rand_idx + (static_cast<size_t>(h) * (nb - 2) + (qb - 1)) * a.r);
-    ntiles = 2 + tl.nwin + a.r;
-  } else {
-    tl.first = chunk * kChunkTiles;
-    tl.nwin = 0;
-    tl.rand = nullptr;
-    ntiles = nb - tl.first < kChunkTiles ? nb - tl.first : kChunkTiles;
-  }
-
-  // ---- prologue: tile 0 in flight, Q into registers ----------------------------
-  issue_tile<T, BS, 0>(kbh, vbh, tile_at(tl, 0), wave, lane);
-  const int q0 = qb * BS + qh * C::QROWS + wq * 32;
-  u32x4 qop[C::QC];
-  {
-    const char* qrow = qbh + static_cast<size_t>(q0 + j) * ROWB;
-#pragma unroll
-    for (int x = 0; x < C::QC; ++x) qop[x] = *reinterpret_cast<const u32x4*>(qrow + (2 * x + g) * 16);
-  }
-  WaveState ws;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    ws.o[0][v] = 0.0f;
-    ws.o[1][v] = 0.0f;
-  }
-  ws.m = -__builtin_inff();
-  ws.l = 0.0f;
-
-  // ---- tile loop: trips of 12 straight-line steps -----------------------------
-  // Units of the usual shapes have at most 12 tiles, so one trip covers them
-  // and the loop back edge -- where the compiler's LDS-DMA wait tracking turns
-  // conservative -- is not taken.  Tile ids are computed once per trip.
-  constexpr int TRIP = 12;
-  static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
-  for (int u = 0; u < ntiles; u += TRIP) {
-    int tid_[TRIP + 1];
-#pragma unroll
-    for (int k = 0; k < TRIP + 1; ++k) tid_[k] = u + k < ntiles ? tile_at(tl, u + k) : 0;
-#define BB_STEP(k)                                                                               \
-  if (u + (k) < ntiles)                                                                          \
-    step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k), ntiles, tid_[k], tid_[(k) + 1], kbh, vbh,      \
-                                  pad_b, wave, lane, kbase);
-    BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
-    BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
-#undef BB_STEP
-  }
-
-  // ---- merge the key groups of each query group (tree over LDS) ------------
-  float* mo0 = reinterpret_cast<float*>(Stage<T, BS, 0>::buf());
-  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, 1>::buf());
-  float* mml = reinterpret_cast<float*>(Stage<T, BS, 1>::buf()) + C::MERGE_O / 4;
+  float* mo0 = reinterpret_cast<float*>(Stage<T, BS, S>::k());
+  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, S>::v());
+  float* mml = MergeML<T, BS>::buf();
 #pragma unroll
   for (int stride = C::WK / 2; stride >= 1; stride /= 2) {
-    __syncthreads();
+    lds_barrier();
     if (wk >= stride && wk < 2 * stride) {
       const int slot = (wk - stride) * C::WQ + wq;
 #pragma unroll
@@ -561,7 +638,7 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
       mml[(slot * 2) * 64 + lane] = ws.m;
       mml[(slot * 2 + 1) * 64 + lane] = ws.l;
     }
-    __syncthreads();
+    lds_barrier();
     if (wk < stride) {
       const int slot = wk * C::WQ + wq;
       const float m1 = mml[(slot * 2) * 64 + lane], l1 = mml[(slot * 2 + 1) * 64 + lane];
@@ -578,9 +655,10 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
     }
   }
   if (wk != 0) return;
-  float l = ws.l + __shfl_xor(ws.l, 32);
-  if (gsel < 0) {
-    char* orow = a.out + (bh * L + q0 + j) * ROWB;
+  const int j = lane & 31, g = lane >> 5;
+  const float l = ws.l + __shfl_xor(ws.l, 32);
+  if (w.gsel < 0) {
+    char* orow = a.out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
     const float inv = 1.0f / l;
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh)
@@ -591,22 +669,122 @@ __device__ __forceinline__ void run_unit(const Args& a, int b, int h, int qb, in
         for (int e = 0; e < 8; ++e) x[e] = ws.o[dh][8 * h8 + e] * inv;
         store_row8(orow + (dh * 32 + 16 * h8 + 8 * g) * C::ES, x, static_cast<T*>(nullptr));
       }
-  } else {
-    const size_t pidx = ((bh * 2 + gsel) * a.n_s + chunk) * BS + qh * C::QROWS + wq * 32 + j;
-    char* prow = reinterpret_cast<char*>(a.po + pidx * kD);
+    return;
+  }
+  const size_t pidx = w.pbase + wq * 32 + j;
+  char* prow = reinterpret_cast<char*>(a.po + pidx * kD);
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
+  for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        float x[8];
+    for (int h8 = 0; h8 < 2; ++h8) {
+      float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = ws.o[dh][8 * h8 + e];
-        store_row8(prow + (dh * 32 + 16 * h8 + 8 * g) * 4, x, static_cast<float*>(nullptr));
-      }
-    if (g == 0) {
-      a.pm[pidx] = ws.m;
-      a.pl[pidx] = l;
+      for (int e = 0; e < 8; ++e) x[e] = ws.o[dh][8 * h8 + e];
+      store_row8(prow + (dh * 32 + 16 * h8 + 8 * g) * 4, x, static_cast<float*>(nullptr));
     }
+  if (g == 0) {
+    a.pm[pidx] = ws.m;
+    a.pl[pidx] = l;
+  }
+}
+
+// A persistent workgroup: it runs a fixed sequence of work units back to back,
+// streaming their key tiles through the 2-stage LDS ring.  The sequence: the
+// hardware deals workgroup ids round robin to the 8 XCDs, so workgroup x runs
+// on XCD x % 8; each XCD owns a contiguous range of units (one (batch, head)
+// after another, which keeps their K/V in that XCD's L2) and its workgroups
+// take every (G/8)-th unit of it.  While the last tile of a unit is processed
+// the next unit's first tile and Q rows are already being fetched, so a unit
+// start waits for nothing but the stores of the previous one.
+template <typename T, int BS, int kind, bool HAS_PAD>
+__device__ __forceinline__ void run(const Args& a, int n_units) {
+  using C = Cfg<T, BS>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave % C::WQ, wk = wave / C::WQ;
+  const int kbase = wk * 32;             // this wave's 32 keys of every tile
+
+  int unit, stride, end;
+  {
+    const int G = gridDim.x, x = blockIdx.x;
+    if ((G & 7) == 0) {
+      const int X = x & 7;
+      unit = static_cast<int>((static_cast<long long>(n_units) * X) >> 3) + (x >> 3);
+      end = static_cast<int>((static_cast<long long>(n_units) * (X + 1)) >> 3);
+      stride = G >> 3;
+    } else {
+      unit = x;
+      end = n_units;
+      stride = G;
+    }
+  }
+  if (unit >= end) return;
+
+  Unit cu = decode_unit<T, BS, kind>(a, unit);
+  u32x4 qop[C::QC];
+  issue_tile<T, BS, 0>((gchar_ptr)(a.k) + cu.off, (gchar_ptr)(a.v) + cu.off, tile_at(cu.tl, 0), wave, lane);
+  load_q<T, BS>(a, cu.off, cu.q0, wq, lane, qop);
+  for (;;) {
+    // Per-lane address arithmetic is redone for every unit rather than kept
+    // live across the unit loop (register pressure).
+    int lane_u = lane;
+    asm volatile("" : "+v"(lane_u));
+    const int nunit = unit + stride;
+    const bool has_next = nunit < end;
+    const Unit nxu = decode_unit<T, BS, kind>(a, has_next ? nunit : unit);
+    NextUnit nx;
+    nx.off = nxu.off;
+    nx.q0 = nxu.q0;
+    nx.tile0 = tile_at(nxu.tl, 0);
+    nx.pf = has_next && (cu.ntiles & 1) == 0 ? 1 : 0;
+    nx.unused = 0;
+    const gchar_ptr kbh = (gchar_ptr)(a.k) + cu.off;
+    const gchar_ptr vbh = (gchar_ptr)(a.v) + cu.off;
+    const uint8_t* pad_b = HAS_PAD ? a.pad + static_cast<size_t>(cu.b) * a.L : nullptr;
+    const int ntiles = cu.ntiles;
+
+    WaveState ws;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      ws.o[0][v] = 0.0f;
+      ws.o[1][v] = 0.0f;
+    }
+    ws.m = -__builtin_inff();
+    ws.l = 0.0f;
+
+    // ---- tile loop: trips of 12 straight-line steps ---------------------------
+    // Units of the usual shapes have at most 12 tiles, so one trip covers them
+    // and the loop back edge -- where the compiler's LDS-DMA wait tracking
+    // turns conservative -- is not taken.  Tile ids are computed once per trip.
+    constexpr int TRIP = 12;
+    static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
+    for (int u = 0; u < ntiles; u += TRIP) {
+      int tid_[TRIP + 1];
+#pragma unroll
+      for (int k = 0; k < TRIP + 1; ++k) tid_[k] = u + k < ntiles ? tile_at(cu.tl, u + k) : 0;
+#define BB_STEP(k)                                                                                  \
+  if (u + (k) < ntiles)                                                                             \
+    step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k), ntiles, tid_[k], tid_[(k) + 1], kbh, vbh, pad_b,   \
+                                  wave, lane_u, kbase, nx, a, wq);
+      BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
+      BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
+#undef BB_STEP
+    }
+
+    if ((ntiles - 1) & 1)
+      finalize<T, BS, 1>(ws, a, cu, wq, wk, lane_u);
+    else
+      finalize<T, BS, 0>(ws, a, cu, wq, wk, lane_u);
+    if (!has_next) break;
+    if (!nx.pf) {
+      // odd tile count: the merge went through stage 0, which the next unit's
+      // first tile now refills once every wave is past the merge
+      lds_barrier();
+      issue_tile<T, BS, 0>((gchar_ptr)(a.k) + nx.off, (gchar_ptr)(a.v) + nx.off, nx.tile0, wave, lane_u);
+      load_q<T, BS>(a, nx.off, nx.q0, wq, lane_u, qop);
+    }
+    cu = nxu;
+    unit = nunit;
   }
 }
 
@@ -666,46 +844,17 @@ __global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
               nn * (1.0f / dd), static_cast<T*>(nullptr));
 }
 
-// Decode a work unit.  Per (b, h): the global units (block 0 chunks, then
-// block nb-1 chunks; QSPLIT row slices each) followed by the middle units
-// (nb-2 blocks, QSPLIT row slices each).  kind selects which of them this
-// grid covers: 0 = all, 1 = global units only, 2 = middle units only.
-template <typename T, int BS, int kind, bool HAS_PAD>
-__device__ __forceinline__ void dispatch(const Args& a) {
-  constexpr int QS = Cfg<T, BS>::QSPLIT;
-  const int n_g = kind == 2 ? 0 : 2 * a.n_s * QS;
-  const int n_m = kind == 1 ? 0 : (a.nb - 2) * QS;
-  const int per_bh = n_g + n_m;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = unit / per_bh, u = unit % per_bh;
-  const int b = bh / a.H, h = bh % a.H;
-  int qb, qh, gsel, chunk;
-  if (u < n_g) {
-    gsel = u / (a.n_s * QS);
-    const int rem = u % (a.n_s * QS);
-    chunk = rem / QS;
-    qh = rem % QS;
-    qb = gsel ? a.nb - 1 : 0;
-  } else {
-    gsel = -1;
-    chunk = 0;
-    qb = (u - n_g) / QS + 1;
-    qh = (u - n_g) % QS;
-  }
-  run_unit<T, BS, HAS_PAD>(a, b, h, qb, qh, gsel, chunk);
-}
-
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_fused_kernel(Args a) {
-  dispatch<T, BS, 0, HAS_PAD>(a);
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_fused_kernel(Args a, int n_units) {
+  run<T, BS, 0, HAS_PAD>(a, n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_global_rows_kernel(Args a) {
-  dispatch<T, BS, 1, HAS_PAD>(a);
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_global_rows_kernel(Args a, int n_units) {
+  run<T, BS, 1, HAS_PAD>(a, n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_middle_rows_kernel(Args a) {
-  dispatch<T, BS, 2, HAS_PAD>(a);
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_middle_rows_kernel(Args a, int n_units) {
+  run<T, BS, 2, HAS_PAD>(a, n_units);
 }
 
 // ---------------------------------------------------------------- host side --
@@ -750,25 +899,55 @@ bool overlap(const void* a, const void* b, size_t n) {
   return x < y + n && y < x + n;
 }
 
+// Persistent grid for a kernel: as many workgroups as the current device
+// holds at once, at most one per unit, rounded down to a multiple of 8 (the
+// XCD count) so that every XCD runs the same number.
+int persistent_grid(const void* kernel, int nt, long long n_units, unsigned* grid) {
+  int dev = 0, ncu = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BB_ERR_HIP;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return BB_ERR_HIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, nt, 0) != hipSuccess) return BB_ERR_HIP;
+  long long g = static_cast<long long>(ncu > 0 ? ncu : 1) * (occ > 0 ? occ : 1);
+  if (g > n_units) g = n_units;
+  if (g >= 8) g -= g % 8;
+  *grid = static_cast<unsigned>(g);
+  return BB_OK;
+}
+
 template <typename T, int BS, bool HAS_PAD>
 int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
   using C = Cfg<T, BS>;
-  const int per_g = 2 * a.n_s * C::QSPLIT, per_m = (a.nb - 2) * C::QSPLIT;
-  const unsigned bhs = static_cast<unsigned>(B) * static_cast<unsigned>(H);
+  const long long bhs = static_cast<long long>(B) * H;
+  const long long per_g = 2LL * a.n_s * C::QSPLIT, per_m = static_cast<long long>(a.nb - 2) * C::QSPLIT;
   const bool units = !(flags & BB_PHASE_MERGE) || (flags & BB_PHASE_UNITS);
   const bool merge = !(flags & BB_PHASE_UNITS) || (flags & BB_PHASE_MERGE);
+  unsigned grid = 0;
+  int st = BB_OK;
   if (units) {
     if (flags & BB_LAUNCH_SPLIT) {
-      bb_global_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_g), dim3(C::NT), 0, stream>>>(a);
+      st = persistent_grid(reinterpret_cast<const void*>(&bb_global_rows_kernel<T, BS, HAS_PAD>), C::NT,
+                           bhs * per_g, &grid);
+      if (st != BB_OK) return st;
+      bb_global_rows_kernel<T, BS, HAS_PAD><<<dim3(grid), dim3(C::NT), 0, stream>>>(
+          a, static_cast<int>(bhs * per_g));
       if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-      bb_middle_rows_kernel<T, BS, HAS_PAD><<<dim3(bhs * per_m), dim3(C::NT), 0, stream>>>(a);
+      st = persistent_grid(reinterpret_cast<const void*>(&bb_middle_rows_kernel<T, BS, HAS_PAD>), C::NT,
+                           bhs * per_m, &grid);
+      if (st != BB_OK) return st;
+      bb_middle_rows_kernel<T, BS, HAS_PAD><<<dim3(grid), dim3(C::NT), 0, stream>>>(
+          a, static_cast<int>(bhs * per_m));
     } else {
-      bb_fused_kernel<T, BS, HAS_PAD><<<dim3(bhs * (per_g + per_m)), dim3(C::NT), 0, stream>>>(a);
+      st = persistent_grid(reinterpret_cast<const void*>(&bb_fused_kernel<T, BS, HAS_PAD>), C::NT,
+                           bhs * (per_g + per_m), &grid);
+      if (st != BB_OK) return st;
+      bb_fused_kernel<T, BS, HAS_PAD><<<dim3(grid), dim3(C::NT), 0, stream>>>(
+          a, static_cast<int>(bhs * (per_g + per_m)));
     }
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   if (merge) {
-    bb_global_merge_kernel<T, BS><<<dim3(bhs * 2 * (BS / 4)), dim3(256), 0, stream>>>(a);
+    bb_global_merge_kernel<T, BS><<<dim3(static_cast<unsigned>(bhs) * 2 * (BS / 4)), dim3(256), 0, stream>>>(a);
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   return BB_OK;

@@ -117,7 +117,9 @@ size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block);
  *   out        DEVICE [B][H][L][d] in `dtype`, 16-byte aligned, fully
  *              overwritten; must not overlap q, k or v.
  *   dtype      BB_BF16 (fp32 accumulation, bf16 output rounded to nearest
- *              even) or BB_FP32.
+ *              even) or BB_FP32.  q, k and v must be finite: the kernels are
+ *              built without NaN semantics, so NaN or Inf inputs give
+ *              unspecified (but memory-safe) outputs.
  *   workspace  DEVICE buffer of at least bb_attn_workspace_bytes(...) bytes,
  *              256-byte aligned.  Its contents need no initialisation (every
  *              byte read is written earlier in the same call).  Calls that run
