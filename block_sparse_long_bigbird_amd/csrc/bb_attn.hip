@@ -185,9 +185,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // One 64 x 16-byte DMA: lane offsets `voff` (32-bit) on the wave-uniform
 // global base `g`, into LDS at the wave-uniform address `m0` (+16 per lane).
-// The s_nop covers the one wait state an M0 write needs before an LDS DMA.
+// The compiler cannot see that the asm reads `g` and M0 from a vector-memory
+// instruction, so it inserts no wait states for them: an SGPR written by a
+// VALU instruction (v_readlane, e.g. reloading a spilled base address) needs 5
+// before a vector-memory instruction reads it, an M0 write 1.  s_nop 4 gives
+// 5 whatever precedes the block.
 __device__ __forceinline__ void dma16(gchar_ptr g, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(g), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(g), "{m0}"(m0) : "memory");
 }
 
 template <typename T, int BS, int S>
@@ -291,17 +295,38 @@ __device__ __forceinline__ PadWords load_pad(const uint8_t* pad_t, int kbase) {
   return w;
 }
 
-// Key bias: -10000 (in q.k units) on the logits of padded keys.  Taken only
-// when the subtile has a padded key.
+// Bit k set iff byte k of w is zero (key padded).  Exact per byte: the high
+// bit of (w & 0x7f..) + 0x7f.. never carries across bytes, and the multiply
+// gathers the eight flag bits into the top byte (every product term lands on
+// a bit of its own, so there are no carries).
+__device__ __forceinline__ uint32_t zero_byte_mask(uint64_t w) {
+  const uint64_t lo7 = 0x7F7F7F7F7F7F7F7FULL;
+  const uint64_t t = ~(((w & lo7) + lo7) | w | lo7);
+  return static_cast<uint32_t>(((t >> 7) * 0x0102040810204080ULL) >> 56);
+}
+
+// Key bias: -10000 on the logits of padded keys (-80000 in q.k units), taken
+// only when the subtile has a padded key.  The bias enters through one more
+// product into the score accumulator: row i of A (key perm_row(i) of the
+// subtile) carries the key's bias in k-slot 0 (fp32) or in k-slots 0 and 1
+// (bf16: -79872 and -128, both exact, summing to -80000 exactly); B holds 1
+// in those slots for every query.
+template <typename T>
 __device__ __forceinline__ void apply_pad(f32x16& acc, const PadWords& w, int lane) {
-  if (has_zero_byte(w.p[0]) || has_zero_byte(w.p[1]) || has_zero_byte(w.p[2]) || has_zero_byte(w.p[3])) {
-    const int g = lane >> 5;
-    const uint64_t w0 = g ? w.p[1] : w.p[0], w1 = g ? w.p[3] : w.p[2];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      acc[v] += ((w0 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
-      acc[8 + v] += ((w1 >> (8 * v)) & 0xffu) ? 0.0f : kMaskRaw;
-    }
+  if (!(has_zero_byte(w.p[0]) || has_zero_byte(w.p[1]) || has_zero_byte(w.p[2]) || has_zero_byte(w.p[3])))
+    return;
+  const uint32_t m = zero_byte_mask(w.p[0]) | (zero_byte_mask(w.p[1]) << 8) |
+                     (zero_byte_mask(w.p[2]) << 16) | (zero_byte_mask(w.p[3]) << 24);
+  const int j = lane & 31;
+  const bool lo = lane < 32;                        // lanes holding k-slots 0..
+  const bool padded = (m >> perm_row(j)) & 1u;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 a = {lo && padded ? 0xC300C79Cu : 0u, 0u, 0u, 0u};
+    const u32x4 b = {lo ? 0x3F803F80u : 0u, 0u, 0u, 0u};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? 1.0f : 0.0f, acc, 0, 0, 0);
   }
 }
 
@@ -413,21 +438,16 @@ __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, con
   if constexpr (sizeof(T) == 2) {
     bf16x8 pb[2];
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         f32x2 pr = {p[8 * h + e], p[8 * h + e + 1]};
         const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
-        if (h == 0)
-          ls0 = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, ls0, false);   // row sum of bf16(P)
-        else
-          ls1 = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, ls1, false);
+        ws.l = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, ws.l, false);   // row sum of bf16(P)
         pb[h][e] = c2[0];
         pb[h][e + 1] = c2[1];
       }
-    ws.l += ls0 + ls1;
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
@@ -470,35 +490,87 @@ __device__ __forceinline__ int tile_at(const TileList& tl, int u) {
 // global units (block 0 chunks, then block nb-1 chunks; QSPLIT row slices
 // each) followed by the middle units (nb-2 blocks, QSPLIT row slices each).
 // `kind` selects which of them a grid covers: 0 = all, 1 = global units only,
-// 2 = middle units only.  A unit covers query rows [qb*BS + qh*64, +64) of
-// (b, h).  gsel < 0: middle query block qb, finalised in place.  gsel in
-// {0, 1}: global query block qb (0 or nb-1) against key chunk `chunk` of the
-// split-K, written as a partial for the merge kernel.
+// 2 = middle units only.  A unit covers query rows [q0, q0 + 64) of (b, h).
+// gsel < 0: a middle query block, finalised in place.  gsel in {0, 1}: global
+// query block 0 or nb-1 against one key chunk of the split-K, written as a
+// partial for the merge kernel.
 struct Unit {
   size_t off;            // byte offset of (b, h) in q, k, v and out: bh * L * ROWB
   size_t pbase;          // global unit: partial row index of its first query row
-  int b, q0, gsel, ntiles;   // q0: first query row of the unit
+  int b, q0, gsel, ntiles;
   TileList tl;
 };
 
+// Kernel arguments read straight from the kernel-argument segment where they
+// are used.  The empty asm makes the pointer opaque, so the loads are not
+// hoisted and the arguments do not occupy scalar registers across the tile
+// loop (they are needed only at unit boundaries).
+typedef const __attribute__((address_space(4))) Args* kargs_ptr;
+__device__ __forceinline__ kargs_ptr kargs() {
+  kargs_ptr p = (kargs_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 template <typename T, int BS, int kind>
-__device__ __forceinline__ Unit decode_unit(const Args& a, int unit) {
+__device__ __forceinline__ int units_per_bh(kargs_ptr a) {
   constexpr int QS = Cfg<T, BS>::QSPLIT;
-  const int n_g = kind == 2 ? 0 : 2 * a.n_s * QS;
-  const int n_m = kind == 1 ? 0 : (a.nb - 2) * QS;
-  const int per_bh = n_g + n_m;
-  const int bh = unit / per_bh, u = unit % per_bh;
-  const int nb = a.nb, h = bh % a.H;
+  return (kind == 2 ? 0 : 2 * a->n_s * QS) + (kind == 1 ? 0 : (a->nb - 2) * QS);
+}
+
+// Position of a unit, kept incrementally so that the unit loop does no
+// integer division: unit = bh * per_bh + u, bh = b * H + h.
+struct Cursor {
+  int unit, bh, u, b, h;
+};
+
+template <typename T, int BS, int kind>
+__device__ __forceinline__ Cursor cursor_at(kargs_ptr a, int unit) {
+  const int per_bh = units_per_bh<T, BS, kind>(a);
+  Cursor c;
+  c.unit = unit;
+  c.bh = unit / per_bh;
+  c.u = unit - c.bh * per_bh;
+  c.b = c.bh / a->H;
+  c.h = c.bh - c.b * a->H;
+  return c;
+}
+
+template <typename T, int BS, int kind>
+__device__ __forceinline__ Cursor cursor_advance(kargs_ptr a, Cursor c, int stride) {
+  const int per_bh = units_per_bh<T, BS, kind>(a), H = a->H;
+  c.unit += stride;
+  c.u += stride;
+  while (c.u >= per_bh) {
+    c.u -= per_bh;
+    ++c.bh;
+    if (++c.h == H) {
+      c.h = 0;
+      ++c.b;
+    }
+  }
+  return c;
+}
+
+template <typename T, int BS, int kind>
+__device__ __forceinline__ Unit decode_unit(kargs_ptr a, const Cursor& c) {
+  using C = Cfg<T, BS>;
+  constexpr int QS = C::QSPLIT;
+  constexpr int LQS = QS == 2 ? 1 : 0;
+  static_assert(QS == 1 || QS == 2, "row slices per query block");
+  const int nb = a->nb, n_s = a->n_s;
+  const int n_g = kind == 2 ? 0 : 2 * n_s * QS;
   Unit w;
-  w.off = static_cast<size_t>(bh) * a.L * Cfg<T, BS>::ROWB;
-  w.b = bh / a.H;
+  w.off = static_cast<size_t>(c.bh) * a->L * C::ROWB;
+  w.b = c.b;
   w.tl.nb = nb;
-  if (u < n_g) {
-    w.gsel = u / (a.n_s * QS);
-    const int rem = u % (a.n_s * QS);
-    const int chunk = rem / QS, qh = rem % QS;
-    w.q0 = (w.gsel ? nb - 1 : 0) * BS + qh * Cfg<T, BS>::QROWS;
-    w.pbase = ((static_cast<size_t>(bh) * 2 + w.gsel) * a.n_s + chunk) * BS + qh * Cfg<T, BS>::QROWS;
+  if (c.u < n_g) {
+    const int half = n_s * QS;
+    w.gsel = c.u >= half ? 1 : 0;
+    const int rem = c.u - (w.gsel ? half : 0);
+    const int chunk = rem >> LQS, qh = rem & (QS - 1);
+    w.q0 = (w.gsel ? nb - 1 : 0) * BS + qh * C::QROWS;
+    w.pbase = ((static_cast<size_t>(c.bh) * 2 + w.gsel) * n_s + chunk) * BS + qh * C::QROWS;
     w.tl.global = 1;
     w.tl.first = chunk * kChunkTiles;
     w.tl.nwin = 0;
@@ -506,51 +578,51 @@ __device__ __forceinline__ Unit decode_unit(const Args& a, int unit) {
     w.ntiles = nb - w.tl.first < kChunkTiles ? nb - w.tl.first : kChunkTiles;
   } else {
     w.gsel = -1;
-    const int qb = (u - n_g) / QS + 1, qh = (u - n_g) % QS;
-    w.q0 = qb * BS + qh * Cfg<T, BS>::QROWS;
+    const int v = c.u - n_g;
+    const int qb = (v >> LQS) + 1, qh = v & (QS - 1);
+    w.q0 = qb * BS + qh * C::QROWS;
     w.pbase = 0;
     const int lo = qb - 1 < 1 ? 1 : qb - 1;          // band without the global blocks
     const int hi = qb + 1 > nb - 2 ? nb - 2 : qb + 1;
     w.tl.global = 0;
     w.tl.first = lo;
     w.tl.nwin = hi - lo + 1;
-    w.tl.rand = (const_i32_ptr)(a.rand_idx + (static_cast<size_t>(h) * (nb - 2) + (qb - 1)) * a.r);
-    w.ntiles = 2 + w.tl.nwin + a.r;
+    const int r = a->r;
+    w.tl.rand = (const_i32_ptr)(a->rand_idx + (static_cast<size_t>(c.h) * (nb - 2) + (qb - 1)) * r);
+    w.ntiles = 2 + w.tl.nwin + r;
   }
   return w;
 }
 
-// This wave's 32 query rows of unit w as the B operand of the score products.
+// This wave's 32 query rows as the B operand of the score products; `qrow`
+// points at the unit's first query row.
 template <typename T, int BS>
-__device__ __forceinline__ void load_q(const Args& a, size_t off, int q0, int wq, int lane,
-                                       u32x4 (&qop)[Cfg<T, BS>::QC]) {
+__device__ __forceinline__ void load_q(const char* qrow0, int wq, int lane, u32x4 (&qop)[Cfg<T, BS>::QC]) {
   using C = Cfg<T, BS>;
-  const char* qrow = a.q + off + static_cast<size_t>(q0 + wq * 32 + (lane & 31)) * C::ROWB;
+  const char* qrow = qrow0 + static_cast<size_t>(wq * 32 + (lane & 31)) * C::ROWB;
 #pragma unroll
   for (int x = 0; x < C::QC; ++x)
     qop[x] = *reinterpret_cast<const u32x4*>(qrow + (2 * x + (lane >> 5)) * 16);
 }
 
-// Where the next unit's first tile comes from, for the prefetch on the last
-// step of the current unit.
+// What the last step of a unit needs to prefetch the next unit.
 struct NextUnit {
-  size_t off;            // its (b, h) byte offset
-  int q0;                // its first query row
+  gchar_ptr kbh, vbh;    // its K and V of (b, h)
+  const char* qrow0;     // its first query row
   int tile0;             // its first key tile
   int pf;                // 1: prefetch (the current unit has an even tile count and a successor)
-  int unused;
 };
 
 // Step u of the tile loop: tile u sits in stage S = u % 2; tile_u and
-// tile_fill are the ids of tiles u and u+1.  On the last step
-// of a unit with an even tile count (S == 1) the next unit is prefetched: its
-// tile 0 into stage 0 and, once this step's score products have consumed Q,
-// its Q rows into qop.
+// tile_fill are the ids of tiles u and u+1.  On the last step of a unit with
+// an even tile count (S == 1) the next unit is prefetched: its tile 0 into
+// stage 0 and, once this step's score products have consumed Q, its Q rows
+// into qop.
 template <typename T, int BS, int S, bool HAS_PAD>
 __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC], int u, int ntiles,
                                      int tile_u, int tile_fill, gchar_ptr kbh, gchar_ptr vbh,
                                      const uint8_t* pad_b, int wave, int lane, int kbase,
-                                     const NextUnit& nx, const Args& a, int wq) {
+                                     const NextUnit& nx, int wq) {
   // This wave's DMA of tile u has landed and its LDS reads of the previous
   // step are complete (vmcnt = lgkmcnt = 0; on a unit's first step this also
   // covers the previous unit's output stores); after the barrier every wave's
@@ -567,13 +639,13 @@ __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC]
   if (!last)
     issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
   else if (S == 1 && nx.pf)
-    issue_tile<T, BS, 0>((gchar_ptr)(a.k) + nx.off, (gchar_ptr)(a.v) + nx.off, nx.tile0, wave, lane);
-  if constexpr (HAS_PAD) apply_pad(s, pw, lane);
+    issue_tile<T, BS, 0>(nx.kbh, nx.vbh, nx.tile0, wave, lane);
+  if constexpr (HAS_PAD) apply_pad<T>(s, pw, lane);
   if (S == 1 && last && nx.pf) {
     // Q is dead after the score products: refill it for the next unit.  The
     // empty asm ties the loads after those products.
     asm volatile("" : "+v"(s) : : "memory");
-    load_q<T, BS>(a, nx.off, nx.q0, wq, lane, qop);
+    load_q<T, BS>(nx.qrow0, wq, lane, qop);
   }
   softmax_pv<T>(ws, s, vo, u == 0);
 }
@@ -617,16 +689,17 @@ struct MergeML {
 // End of a unit: merge the key groups of each query group (tree over LDS,
 // O through stage S -- the stage of the unit's last tile -- and (max, sum)
 // through MergeML), then write the output rows (middle unit) or the partial
-// (global unit).
+// (global unit).  Key group 0 finishes the last round; for a middle unit the
+// division by the row sum is folded into the two merge weights.
 template <typename T, int BS, int S>
-__device__ __forceinline__ void finalize(WaveState& ws, const Args& a, const Unit& w, int wq, int wk,
-                                        int lane) {
+__device__ __forceinline__ void finalize(WaveState& ws, const Unit& w, int wq, int wk, int lane) {
   using C = Cfg<T, BS>;
   float* mo0 = reinterpret_cast<float*>(Stage<T, BS, S>::k());
   float* mo1 = reinterpret_cast<float*>(Stage<T, BS, S>::v());
   float* mml = MergeML<T, BS>::buf();
+  // rounds with more than one receiving key group (4 key groups: 2,3 -> 0,1)
 #pragma unroll
-  for (int stride = C::WK / 2; stride >= 1; stride /= 2) {
+  for (int stride = C::WK / 2; stride >= 2; stride /= 2) {
     lds_barrier();
     if (wk >= stride && wk < 2 * stride) {
       const int slot = (wk - stride) * C::WQ + wq;
@@ -654,37 +727,68 @@ __device__ __forceinline__ void finalize(WaveState& ws, const Args& a, const Uni
       ws.m = mm;
     }
   }
+  // last round: key group 1 -> key group 0
+  lds_barrier();
+  if (wk == 1) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      mo0[(wq * 16 + v) * 64 + lane] = ws.o[0][v];
+      mo1[(wq * 16 + v) * 64 + lane] = ws.o[1][v];
+    }
+    mml[(wq * 2) * 64 + lane] = ws.m;
+    mml[(wq * 2 + 1) * 64 + lane] = ws.l;
+  }
+  lds_barrier();
   if (wk != 0) return;
   const int j = lane & 31, g = lane >> 5;
-  const float l = ws.l + __shfl_xor(ws.l, 32);
+  const float m1 = mml[(wq * 2) * 64 + lane], l1 = mml[(wq * 2 + 1) * 64 + lane];
+  const float mm = fmaxf(ws.m, m1);
+  float a0 = __builtin_amdgcn_exp2f((ws.m - mm) * kScaleLog2);
+  float a1 = __builtin_amdgcn_exp2f((m1 - mm) * kScaleLog2);
+  const float lh = ws.l * a0 + l1 * a1;             // this lane half's share of the row sum
+  const float l = lh + __shfl_xor(lh, 32);
+  char* dst;
+  float* pm = nullptr;
+  float* pl = nullptr;
+  size_t pidx = 0;
   if (w.gsel < 0) {
-    char* orow = a.out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
     const float inv = 1.0f / l;
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = ws.o[dh][8 * h8 + e] * inv;
-        store_row8(orow + (dh * 32 + 16 * h8 + 8 * g) * C::ES, x, static_cast<T*>(nullptr));
-      }
-    return;
+    a0 *= inv;
+    a1 *= inv;
+    dst = kargs()->out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
+  } else {
+    const kargs_ptr a = kargs();
+    pidx = w.pbase + wq * 32 + j;
+    dst = reinterpret_cast<char*>(a->po + pidx * kD);
+    pm = a->pm;
+    pl = a->pl;
   }
-  const size_t pidx = w.pbase + wq * 32 + j;
-  char* prow = reinterpret_cast<char*>(a.po + pidx * kD);
+  float x[2][2][8];
 #pragma unroll
   for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-    for (int h8 = 0; h8 < 2; ++h8) {
-      float x[8];
+    for (int h8 = 0; h8 < 2; ++h8)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ws.o[dh][8 * h8 + e];
-      store_row8(prow + (dh * 32 + 16 * h8 + 8 * g) * 4, x, static_cast<float*>(nullptr));
-    }
+      for (int e = 0; e < 8; ++e) {
+        const float* mo = dh ? mo1 : mo0;
+        x[dh][h8][e] = ws.o[dh][8 * h8 + e] * a0 + mo[(wq * 16 + 8 * h8 + e) * 64 + lane] * a1;
+      }
+  if (w.gsel < 0) {
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8)
+        store_row8(dst + (dh * 32 + 16 * h8 + 8 * g) * C::ES, x[dh][h8], static_cast<T*>(nullptr));
+    return;
+  }
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+      store_row8(dst + (dh * 32 + 16 * h8 + 8 * g) * 4, x[dh][h8], static_cast<float*>(nullptr));
   if (g == 0) {
-    a.pm[pidx] = ws.m;
-    a.pl[pidx] = l;
+    pm[pidx] = mm;
+    pl[pidx] = l;
   }
 }
 
@@ -697,50 +801,62 @@ __device__ __forceinline__ void finalize(WaveState& ws, const Args& a, const Uni
 // the next unit's first tile and Q rows are already being fetched, so a unit
 // start waits for nothing but the stores of the previous one.
 template <typename T, int BS, int kind, bool HAS_PAD>
-__device__ __forceinline__ void run(const Args& a, int n_units) {
+__device__ __forceinline__ void run(int n_units) {
   using C = Cfg<T, BS>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave % C::WQ, wk = wave / C::WQ;
   const int kbase = wk * 32;             // this wave's 32 keys of every tile
 
-  int unit, stride, end;
+  int first, stride, end;
   {
     const int G = gridDim.x, x = blockIdx.x;
     if ((G & 7) == 0) {
       const int X = x & 7;
-      unit = static_cast<int>((static_cast<long long>(n_units) * X) >> 3) + (x >> 3);
+      first = static_cast<int>((static_cast<long long>(n_units) * X) >> 3) + (x >> 3);
       end = static_cast<int>((static_cast<long long>(n_units) * (X + 1)) >> 3);
       stride = G >> 3;
     } else {
-      unit = x;
+      first = x;
       end = n_units;
       stride = G;
     }
   }
-  if (unit >= end) return;
+  if (first >= end) return;
 
-  Unit cu = decode_unit<T, BS, kind>(a, unit);
+  Cursor cur = cursor_at<T, BS, kind>(kargs(), first);
+  Unit cu = decode_unit<T, BS, kind>(kargs(), cur);
   u32x4 qop[C::QC];
-  issue_tile<T, BS, 0>((gchar_ptr)(a.k) + cu.off, (gchar_ptr)(a.v) + cu.off, tile_at(cu.tl, 0), wave, lane);
-  load_q<T, BS>(a, cu.off, cu.q0, wq, lane, qop);
+  {
+    const kargs_ptr a = kargs();
+    issue_tile<T, BS, 0>((gchar_ptr)(a->k) + cu.off, (gchar_ptr)(a->v) + cu.off, tile_at(cu.tl, 0), wave, lane);
+    load_q<T, BS>(a->q + cu.off + static_cast<size_t>(cu.q0) * C::ROWB, wq, lane, qop);
+  }
   for (;;) {
     // Per-lane address arithmetic is redone for every unit rather than kept
     // live across the unit loop (register pressure).
     int lane_u = lane;
     asm volatile("" : "+v"(lane_u));
-    const int nunit = unit + stride;
-    const bool has_next = nunit < end;
-    const Unit nxu = decode_unit<T, BS, kind>(a, has_next ? nunit : unit);
+    const Cursor nxt = cursor_advance<T, BS, kind>(kargs(), cur, stride);
+    const bool has_next = nxt.unit < end;
     NextUnit nx;
-    nx.off = nxu.off;
-    nx.q0 = nxu.q0;
-    nx.tile0 = tile_at(nxu.tl, 0);
-    nx.pf = has_next && (cu.ntiles & 1) == 0 ? 1 : 0;
-    nx.unused = 0;
-    const gchar_ptr kbh = (gchar_ptr)(a.k) + cu.off;
-    const gchar_ptr vbh = (gchar_ptr)(a.v) + cu.off;
-    const uint8_t* pad_b = HAS_PAD ? a.pad + static_cast<size_t>(cu.b) * a.L : nullptr;
+    {
+      const kargs_ptr a = kargs();
+      const Unit nu = decode_unit<T, BS, kind>(a, nxt);
+      nx.kbh = (gchar_ptr)(a->k) + nu.off;
+      nx.vbh = (gchar_ptr)(a->v) + nu.off;
+      nx.qrow0 = a->q + nu.off + static_cast<size_t>(nu.q0) * C::ROWB;
+      nx.tile0 = nu.tl.global ? nu.tl.first : 0;
+      nx.pf = has_next && (cu.ntiles & 1) == 0 ? 1 : 0;
+    }
+    gchar_ptr kbh, vbh;
+    const uint8_t* pad_b;
+    {
+      const kargs_ptr a = kargs();
+      kbh = (gchar_ptr)(a->k) + cu.off;
+      vbh = (gchar_ptr)(a->v) + cu.off;
+      pad_b = HAS_PAD ? a->pad + static_cast<size_t>(cu.b) * a->L : nullptr;
+    }
     const int ntiles = cu.ntiles;
 
     WaveState ws;
@@ -753,9 +869,8 @@ __device__ __forceinline__ void run(const Args& a, int n_units) {
     ws.l = 0.0f;
 
     // ---- tile loop: trips of 12 straight-line steps ---------------------------
-    // Units of the usual shapes have at most 12 tiles, so one trip covers them
-    // and the loop back edge -- where the compiler's LDS-DMA wait tracking
-    // turns conservative -- is not taken.  Tile ids are computed once per trip.
+    // Units of the usual shapes have at most 12 tiles, so one trip covers them.
+    // Tile ids are computed once per trip.
     constexpr int TRIP = 12;
     static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
     for (int u = 0; u < ntiles; u += TRIP) {
@@ -765,26 +880,26 @@ __device__ __forceinline__ void run(const Args& a, int n_units) {
 #define BB_STEP(k)                                                                                  \
   if (u + (k) < ntiles)                                                                             \
     step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k), ntiles, tid_[k], tid_[(k) + 1], kbh, vbh, pad_b,   \
-                                  wave, lane_u, kbase, nx, a, wq);
+                                  wave, lane_u, kbase, nx, wq);
       BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
       BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
     }
 
     if ((ntiles - 1) & 1)
-      finalize<T, BS, 1>(ws, a, cu, wq, wk, lane_u);
+      finalize<T, BS, 1>(ws, cu, wq, wk, lane_u);
     else
-      finalize<T, BS, 0>(ws, a, cu, wq, wk, lane_u);
+      finalize<T, BS, 0>(ws, cu, wq, wk, lane_u);
     if (!has_next) break;
     if (!nx.pf) {
       // odd tile count: the merge went through stage 0, which the next unit's
       // first tile now refills once every wave is past the merge
       lds_barrier();
-      issue_tile<T, BS, 0>((gchar_ptr)(a.k) + nx.off, (gchar_ptr)(a.v) + nx.off, nx.tile0, wave, lane_u);
-      load_q<T, BS>(a, nx.off, nx.q0, wq, lane_u, qop);
+      issue_tile<T, BS, 0>(nx.kbh, nx.vbh, nx.tile0, wave, lane_u);
+      load_q<T, BS>(nx.qrow0, wq, lane_u, qop);
     }
-    cu = nxu;
-    unit = nunit;
+    cur = nxt;
+    cu = decode_unit<T, BS, kind>(kargs(), cur);
   }
 }
 
@@ -845,16 +960,16 @@ __global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
 }
 
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_fused_kernel(Args a, int n_units) {
-  run<T, BS, 0, HAS_PAD>(a, n_units);
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_fused_kernel(Args, int n_units) {
+  run<T, BS, 0, HAS_PAD>(n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_global_rows_kernel(Args a, int n_units) {
-  run<T, BS, 1, HAS_PAD>(a, n_units);
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_global_rows_kernel(Args, int n_units) {
+  run<T, BS, 1, HAS_PAD>(n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_middle_rows_kernel(Args a, int n_units) {
-  run<T, BS, 2, HAS_PAD>(a, n_units);
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_middle_rows_kernel(Args, int n_units) {
+  run<T, BS, 2, HAS_PAD>(n_units);
 }
 
 // ---------------------------------------------------------------- host side --
