@@ -255,26 +255,9 @@ __device__ __forceinline__ f32x16 scores(const u32x4 (&qop)[Cfg<T, BS>::QC], int
   const int row = kbase + perm_row(j);
   const int sw = swz_k(row);
   u32x4 a[C::QC];
-  if constexpr (C::QC == 4) {
-    // All four reads in flight before one wait (issued one by one, each
-    // would wait for its own LDS round trip).
-    uint32_t ad[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) ad[x] = lds_addr(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
-    asm volatile(
-        "ds_read_b128 %0, %4\n"
-        "ds_read_b128 %1, %5\n"
-        "ds_read_b128 %2, %6\n"
-        "ds_read_b128 %3, %7\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-        : "memory");
-  } else {
-#pragma unroll
-    for (int x = 0; x < C::QC; ++x)
-      a[x] = *reinterpret_cast<const u32x4*>(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
-  }
+  for (int x = 0; x < C::QC; ++x)
+    a[x] = *reinterpret_cast<const u32x4*>(sk + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -307,27 +290,19 @@ __device__ __forceinline__ uint32_t zero_byte_mask(uint64_t w) {
 
 // Key bias: -10000 on the logits of padded keys (-80000 in q.k units), taken
 // only when the subtile has a padded key.  The bias enters through one more
-// product into the score accumulator: row i of A (key perm_row(i) of the
-// subtile) carries the key's bias in k-slot 0 (fp32) or in k-slots 0 and 1
-// (bf16: -79872 and -128, both exact, summing to -80000 exactly); B holds 1
-// in those slots for every query.
-template <typename T>
+// product into the score accumulator, an fp32 32x32x2 MFMA (one register per
+// operand): row i of A (key perm_row(i) of the subtile) carries the key's
+// bias in k-slot 0 (lanes 0..31), B holds 1 there for every query, k-slot 1
+// is zero.  -80000 * 1 is exact, so this is the fp32 add of the bias.
 __device__ __forceinline__ void apply_pad(f32x16& acc, const PadWords& w, int lane) {
   if (!(has_zero_byte(w.p[0]) || has_zero_byte(w.p[1]) || has_zero_byte(w.p[2]) || has_zero_byte(w.p[3])))
     return;
   const uint32_t m = zero_byte_mask(w.p[0]) | (zero_byte_mask(w.p[1]) << 8) |
                      (zero_byte_mask(w.p[2]) << 16) | (zero_byte_mask(w.p[3]) << 24);
   const int j = lane & 31;
-  const bool lo = lane < 32;                        // lanes holding k-slots 0..
+  const bool lo = lane < 32;                        // lanes holding k-slot 0
   const bool padded = (m >> perm_row(j)) & 1u;
-  if constexpr (sizeof(T) == 2) {
-    const u32x4 a = {lo && padded ? 0xC300C79Cu : 0u, 0u, 0u, 0u};
-    const u32x4 b = {lo ? 0x3F803F80u : 0u, 0u, 0u, 0u};
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-  } else {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? 1.0f : 0.0f, acc, 0, 0, 0);
-  }
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? 1.0f : 0.0f, acc, 0, 0, 0);
 }
 
 // V^T operands of this wave's subtile of stage S.
@@ -340,42 +315,21 @@ __device__ __forceinline__ VOp<T> load_v(int kbase, int lane) {
     // Transposing LDS reads (ds_read_b64_tr_b16): lane (dim, g) gets V[key][dim]
     // for 4 consecutive keys; lanes 4e+m of each 16-lane group address row
     // key0+e at dim quad m.  Rows key0 + {0, 4, 16, 20} share the swizzle
-    // (it depends on row % 4), so one address per dim half serves all four
-    // reads through immediate offsets.  The reads sit in one asm block that
-    // ends with its own lgkmcnt wait: issued through the intrinsic, the
-    // compiler cannot tell them from the K/V DMA still in flight and would
-    // drain all vector memory before each of them.
+    // (it depends on row % 4).
     const int g = lane >> 5, e4 = (lane >> 2) & 3;
     const int r0 = kbase + 8 * g + e4;
-    uint32_t addr[2];
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh) {
       const int dstart = dh * 32 + perm_row(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
       const int dchunk = dstart >> 3, dbyte = (dstart & 7) * 2;
-      addr[dh] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-          (const __attribute__((address_space(3))) char*)(sv + r0 * C::ROWB + ((dchunk ^ swz_v(r0)) << 4) + dbyte)));
+      const char* base = sv + r0 * C::ROWB + ((dchunk ^ swz_v(r0)) << 4) + dbyte;
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + 16 * mm * C::ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + (16 * mm + 4) * C::ROWB));
+        vo.a[dh][mm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     }
-    i16x4 t[2][4];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n"
-        "ds_read_b64_tr_b16 %1, %8 offset:%10\n"
-        "ds_read_b64_tr_b16 %2, %8 offset:%11\n"
-        "ds_read_b64_tr_b16 %3, %8 offset:%12\n"
-        "ds_read_b64_tr_b16 %4, %9\n"
-        "ds_read_b64_tr_b16 %5, %9 offset:%10\n"
-        "ds_read_b64_tr_b16 %6, %9 offset:%11\n"
-        "ds_read_b64_tr_b16 %7, %9 offset:%12\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[0][2]), "=&v"(t[0][3]),
-          "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[1][2]), "=&v"(t[1][3])
-        : "v"(addr[0]), "v"(addr[1]), "i"(4 * C::ROWB), "i"(16 * C::ROWB), "i"(20 * C::ROWB)
-        : "memory");
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-        vo.a[dh][mm] = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(t[dh][2 * mm], t[dh][2 * mm + 1], 0, 1, 2, 3, 4, 5, 6, 7));
   } else {
     const int j = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -605,12 +559,14 @@ __device__ __forceinline__ void load_q(const char* qrow0, int wq, int lane, u32x
     qop[x] = *reinterpret_cast<const u32x4*>(qrow + (2 * x + (lane >> 5)) * 16);
 }
 
-// What the last step of a unit needs to prefetch the next unit.
+// What the last step of a unit needs to prefetch the next unit (its K, V and
+// Q addresses are rebuilt from the kernel arguments there, once per unit).
 struct NextUnit {
-  gchar_ptr kbh, vbh;    // its K and V of (b, h)
-  const char* qrow0;     // its first query row
+  size_t off;            // its (b, h) byte offset
+  int q0;                // its first query row
   int tile0;             // its first key tile
   int pf;                // 1: prefetch (the current unit has an even tile count and a successor)
+  int unused;
 };
 
 // Step u of the tile loop: tile u sits in stage S = u % 2; tile_u and
@@ -636,16 +592,18 @@ __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC]
   f32x16 s = scores<T, BS, S>(qop, kbase, lane);
   const VOp<T> vo = load_v<T, BS, S>(kbase, lane);
   const bool last = u + 1 == ntiles;
-  if (!last)
+  if (!last) {
     issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
-  else if (S == 1 && nx.pf)
-    issue_tile<T, BS, 0>(nx.kbh, nx.vbh, nx.tile0, wave, lane);
-  if constexpr (HAS_PAD) apply_pad<T>(s, pw, lane);
+  } else if (S == 1 && nx.pf) {
+    const kargs_ptr a = kargs();
+    issue_tile<T, BS, 0>((gchar_ptr)(a->k) + nx.off, (gchar_ptr)(a->v) + nx.off, nx.tile0, wave, lane);
+  }
+  if constexpr (HAS_PAD) apply_pad(s, pw, lane);
   if (S == 1 && last && nx.pf) {
     // Q is dead after the score products: refill it for the next unit.  The
     // empty asm ties the loads after those products.
     asm volatile("" : "+v"(s) : : "memory");
-    load_q<T, BS>(nx.qrow0, wq, lane, qop);
+    load_q<T, BS>(kargs()->q + nx.off + static_cast<size_t>(nx.q0) * Cfg<T, BS>::ROWB, wq, lane, qop);
   }
   softmax_pv<T>(ws, s, vo, u == 0);
 }
@@ -841,13 +799,12 @@ __device__ __forceinline__ void run(int n_units) {
     const bool has_next = nxt.unit < end;
     NextUnit nx;
     {
-      const kargs_ptr a = kargs();
-      const Unit nu = decode_unit<T, BS, kind>(a, nxt);
-      nx.kbh = (gchar_ptr)(a->k) + nu.off;
-      nx.vbh = (gchar_ptr)(a->v) + nu.off;
-      nx.qrow0 = a->q + nu.off + static_cast<size_t>(nu.q0) * C::ROWB;
+      const Unit nu = decode_unit<T, BS, kind>(kargs(), nxt);
+      nx.off = nu.off;
+      nx.q0 = nu.q0;
       nx.tile0 = nu.tl.global ? nu.tl.first : 0;
       nx.pf = has_next && (cu.ntiles & 1) == 0 ? 1 : 0;
+      nx.unused = 0;
     }
     gchar_ptr kbh, vbh;
     const uint8_t* pad_b;
@@ -874,16 +831,23 @@ __device__ __forceinline__ void run(int n_units) {
     constexpr int TRIP = 12;
     static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
     for (int u = 0; u < ntiles; u += TRIP) {
-      int tid_[TRIP + 1];
+      // tile ids of the trip, two 16-bit ids per scalar register (nb < 65536)
+      uint32_t tp[(TRIP + 2) / 2];
 #pragma unroll
-      for (int k = 0; k < TRIP + 1; ++k) tid_[k] = u + k < ntiles ? tile_at(cu.tl, u + k) : 0;
+      for (int k = 0; k < (TRIP + 2) / 2; ++k) {
+        const uint32_t t0 = u + 2 * k < ntiles ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k)) : 0u;
+        const uint32_t t1 = u + 2 * k + 1 < ntiles ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k + 1)) : 0u;
+        tp[k] = t0 | (t1 << 16);
+      }
+#define BB_TILE(k) static_cast<int>((tp[(k) >> 1] >> (16 * ((k) & 1))) & 0xffffu)
 #define BB_STEP(k)                                                                                  \
   if (u + (k) < ntiles)                                                                             \
-    step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k), ntiles, tid_[k], tid_[(k) + 1], kbh, vbh, pad_b,   \
-                                  wave, lane_u, kbase, nx, wq);
+    step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k), ntiles, BB_TILE(k), BB_TILE((k) + 1), kbh, vbh,    \
+                                  pad_b, wave, lane_u, kbase, nx, wq);
       BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
       BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
+#undef BB_TILE
     }
 
     if ((ntiles - 1) & 1)
@@ -895,8 +859,9 @@ __device__ __forceinline__ void run(int n_units) {
       // odd tile count: the merge went through stage 0, which the next unit's
       // first tile now refills once every wave is past the merge
       lds_barrier();
-      issue_tile<T, BS, 0>(nx.kbh, nx.vbh, nx.tile0, wave, lane_u);
-      load_q<T, BS>(nx.qrow0, wq, lane_u, qop);
+      const kargs_ptr a = kargs();
+      issue_tile<T, BS, 0>((gchar_ptr)(a->k) + nx.off, (gchar_ptr)(a->v) + nx.off, nx.tile0, wave, lane_u);
+      load_q<T, BS>(a->q + nx.off + static_cast<size_t>(nx.q0) * C::ROWB, wq, lane_u, qop);
     }
     cur = nxt;
     cu = decode_unit<T, BS, kind>(kargs(), cur);
@@ -960,15 +925,15 @@ __global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
 }
 
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_fused_kernel(Args, int n_units) {
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(4))) bb_fused_kernel(Args, int n_units) {
   run<T, BS, 0, HAS_PAD>(n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_global_rows_kernel(Args, int n_units) {
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(4))) bb_global_rows_kernel(Args, int n_units) {
   run<T, BS, 1, HAS_PAD>(n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) bb_middle_rows_kernel(Args, int n_units) {
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(4))) bb_middle_rows_kernel(Args, int n_units) {
   run<T, BS, 2, HAS_PAD>(n_units);
 }
 
@@ -997,7 +962,7 @@ int check_shape(int B, int H, int L, int d, int block, int r, int* nb_out) {
   if (block != 64 && block != 128) return BB_ERR_SHAPE;
   if (L % block != 0) return BB_ERR_SHAPE;
   const int nb = L / block;
-  if (nb < 3) return BB_ERR_SHAPE;
+  if (nb < 3 || nb > 65535) return BB_ERR_SHAPE;
   const int r_max = nb - 5 > 0 ? nb - 5 : 0;
   if (r > r_max || r > kMaxR) return BB_ERR_SHAPE;
   const int n_s = (nb + kChunkTiles - 1) / kChunkTiles;
