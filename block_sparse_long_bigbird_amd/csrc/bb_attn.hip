@@ -874,8 +874,9 @@ __device__ __forceinline__ void run(int n_units) {
 // Runs as its own launch after the global-row units, so their partials are
 // complete and visible without any in-kernel fence.  A workgroup covers 4
 // query rows x 16 float4 columns; the chunks of each output are split over
-// kMergeSplit threads (strided), whose (m, l, O) are then combined through
-// LDS in a fixed order, so the result is deterministic.
+// kMergeSplit threads (strided, each a single online pass), whose (m, l, O)
+// are then combined through LDS in a fixed order, so the result is
+// deterministic.
 constexpr int kMergeSplit = 4;
 
 template <typename T, int BS>
@@ -890,17 +891,22 @@ __global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
   const int sg = threadIdx.x >> 6, o = threadIdx.x & 63;      // chunk group, output slot
   const int ql = slice * 4 + (o >> 4), dq = o & 15;
   const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.n_s;
+  // One pass, running max first (online rescaling), chunks in fixed order;
+  // unrolled by two so that two chunks' loads are in flight together.
   float m = -__builtin_inff();
-  for (int s = sg; s < a.n_s; s += kMergeSplit) m = fmaxf(m, a.pm[(base + s) * BS + ql]);
   float den = 0.0f;
   f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (m != -__builtin_inff()) {
-    for (int s = sg; s < a.n_s; s += kMergeSplit) {
-      const size_t pi = (base + s) * BS + ql;
-      const float w = __builtin_amdgcn_exp2f((a.pm[pi] - m) * kScaleLog2);
-      den += w * a.pl[pi];
-      num += w * *reinterpret_cast<const f32x4*>(a.po + pi * kD + dq * 4);
-    }
+#pragma unroll 2
+  for (int s = sg; s < a.n_s; s += kMergeSplit) {
+    const size_t pi = (base + s) * BS + ql;
+    const float ms = a.pm[pi], ls = a.pl[pi];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(a.po + pi * kD + dq * 4);
+    const float mn = fmaxf(m, ms);
+    const float c0 = __builtin_amdgcn_exp2f((m - mn) * kScaleLog2);   // 0 while m is -inf
+    const float c1 = __builtin_amdgcn_exp2f((ms - mn) * kScaleLog2);
+    den = den * c0 + ls * c1;
+    num = num * c0 + os * c1;
+    m = mn;
   }
   s_m[sg][o] = m;
   s_l[sg][o] = den;
