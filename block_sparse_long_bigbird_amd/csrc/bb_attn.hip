@@ -194,22 +194,42 @@ __device__ __forceinline__ void dma16(gchar_ptr g, uint32_t voff, uint32_t m0) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(g), "{m0}"(m0) : "memory");
 }
 
+// Two K and two V DMAs in one block: the leading s_nop 4 covers every input
+// (none is written inside), each M0 write gets its 1 wait state.
+__device__ __forceinline__ void dma16x4(gchar_ptr kt, gchar_ptr vt, uint32_t ko0, uint32_t vo0, uint32_t ko1,
+                                        uint32_t vo1, uint32_t mk0, uint32_t mv0, uint32_t mk1, uint32_t mv1) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %8\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %9\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %8\n\t"
+      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %9"
+      :
+      : "v"(ko0), "v"(vo0), "v"(ko1), "v"(vo1), "s"(mk0), "s"(mv0), "s"(mk1), "s"(mv1), "s"(kt), "s"(vt)
+      : "memory", "m0");
+}
+
 template <typename T, int BS, int S>
 __device__ __forceinline__ void issue_tile(gchar_ptr kbh, gchar_ptr vbh, int tile, int wave, int lane) {
   using C = Cfg<T, BS>;
   const gchar_ptr kt = kbh + static_cast<size_t>(tile) * C::TILE;
   const gchar_ptr vt = vbh + static_cast<size_t>(tile) * C::TILE;
   const uint32_t lk = lds_addr(Stage<T, BS, S>::k()), lv = lds_addr(Stage<T, BS, S>::v());
+  static_assert(C::DMA_MAT % 2 == 0, "DMA instructions go in blocks of two per matrix");
+  uint32_t ko[C::DMA_MAT], vo[C::DMA_MAT], mk[C::DMA_MAT], mv[C::DMA_MAT];
 #pragma unroll
   for (int jj = 0; jj < C::DMA_MAT; ++jj) {
     const int ins = wave + C::NW * jj;
     const int slot = ins * 64 + lane;
     const int row = slot / C::CPR, p = slot % C::CPR;
-    const uint32_t ko = row * C::ROWB + ((p ^ swz_k(row)) << 4);
-    const uint32_t vo = row * C::ROWB + ((p ^ swz_v(row)) << 4);
-    dma16(kt, ko, __builtin_amdgcn_readfirstlane(lk + ins * 1024));
-    dma16(vt, vo, __builtin_amdgcn_readfirstlane(lv + ins * 1024));
+    ko[jj] = row * C::ROWB + ((p ^ swz_k(row)) << 4);
+    vo[jj] = row * C::ROWB + ((p ^ swz_v(row)) << 4);
+    mk[jj] = __builtin_amdgcn_readfirstlane(lk + ins * 1024);
+    mv[jj] = __builtin_amdgcn_readfirstlane(lv + ins * 1024);
   }
+#pragma unroll
+  for (int jj = 0; jj < C::DMA_MAT; jj += 2)
+    dma16x4(kt, vt, ko[jj], vo[jj], ko[jj + 1], vo[jj + 1], mk[jj], mv[jj], mk[jj + 1], mv[jj + 1]);
 }
 
 // Per-wave online-softmax state for 32 query rows (one per lane pair).
@@ -346,9 +366,8 @@ __device__ __forceinline__ VOp<T> load_v(int kbase, int lane) {
   return vo;
 }
 
-// Row max of this subtile's 16 scores per lane (and `m0`), over both lane
-// halves (the two 16-key halves of the query row).
-__device__ __forceinline__ float subtile_max(const f32x16& acc, float m0) {
+// Max of this lane's 16 scores of the subtile and `m0`.
+__device__ __forceinline__ float lane_max(const f32x16& acc, float m0) {
   float m8[6];
   m8[0] = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
   m8[1] = fmaxf(fmaxf(acc[3], acc[4]), acc[5]);
@@ -356,7 +375,13 @@ __device__ __forceinline__ float subtile_max(const f32x16& acc, float m0) {
   m8[3] = fmaxf(fmaxf(acc[9], acc[10]), acc[11]);
   m8[4] = fmaxf(fmaxf(acc[12], acc[13]), acc[14]);
   m8[5] = fmaxf(acc[15], m0);
-  float m = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), m8[2]), fmaxf(fmaxf(m8[3], m8[4]), m8[5]));
+  return fmaxf(fmaxf(fmaxf(m8[0], m8[1]), m8[2]), fmaxf(fmaxf(m8[3], m8[4]), m8[5]));
+}
+
+// Row max of this subtile's 16 scores per lane (and `m0`), over both lane
+// halves (the two 16-key halves of the query row).
+__device__ __forceinline__ float subtile_max(const f32x16& acc, float m0) {
+  const float m = lane_max(acc, m0);
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
@@ -375,8 +400,10 @@ __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, con
   float mc = ws.m * kScaleLog2;
 #pragma unroll
   for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-  const float mloc = subtile_max(acc, ws.m);
-  if (__any(mloc - ws.m > kRescaleTau / kScaleLog2)) {
+  // Each lane tests its own 16 scores; only a rescale needs the row max over
+  // both lane halves.
+  if (__any(lane_max(acc, ws.m) > ws.m + kRescaleTau / kScaleLog2)) {
+    const float mloc = subtile_max(acc, ws.m);
     const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -710,7 +737,7 @@ __device__ __forceinline__ void finalize(WaveState& ws, const Unit& w, int wq, i
   float* pl = nullptr;
   size_t pidx = 0;
   if (w.gsel < 0) {
-    const float inv = 1.0f / l;
+    const float inv = __builtin_amdgcn_rcpf(l);   // 1 ulp
     a0 *= inv;
     a1 *= inv;
     dst = kargs()->out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
@@ -927,7 +954,7 @@ __global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
   }
   store_f32x4(a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + ql) * ROWB +
                   dq * 4 * sizeof(T),
-              nn * (1.0f / dd), static_cast<T*>(nullptr));
+              nn * __builtin_amdgcn_rcpf(dd), static_cast<T*>(nullptr));
 }
 
 template <typename T, int BS, bool HAS_PAD>
