@@ -19,8 +19,9 @@ last-level cache, so each call reads HBM.
 
 `roofline` is for the dominant kernel (the fused work-unit kernel, which does
 every useful FLOP): a second pass runs the same K steps through the two-phase
-form of the call with events between the phases, so the kernel's own launch
-duration is measured on its stream.  `traffic` is the HBM bytes per launch from
+form of the call, each kernel timestamped at its start and end by its own
+launch (hipExtLaunchKernel events on the launch stream), so the kernel's
+execution time is measured without enqueue gaps.  `traffic` is the HBM bytes per launch from
 the committed rocprofv3 counter summary, used only if that summary was taken
 on the current kernel source.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of (batch, head) units of the same workload on this host.
@@ -204,7 +205,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 500 calls (~30 ms of kernels): the engine clock ramps up over the first
+    # few milliseconds of load; with only 10 warm-up calls the timed region
+    # starts below full clock and reads ~15% low.
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="base_B4_H12_L4096_pad")
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--launch", choices=["fused", "split"], default="fused")
@@ -256,10 +260,10 @@ def main():
     ws = bb.alloc_workspace(w.B, w.H, w.L, w.d, w.block, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def call(i, flags):
+    def call(i, flags, events=None):
         a, b_, c, o = sets[i % n_sets]
         bb.bb_attn_forward(a, b_, c, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, o, ws,
-                           stream=stream.cuda_stream, flags=flags)
+                           stream=stream.cuda_stream, flags=flags, events=events)
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -278,19 +282,20 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # Pass 2 -- per-kernel durations: the same steps in two phases with events
-    # around the work-unit launch (the dominant kernel) and the merge.
-    e = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    # Pass 2 -- per-kernel durations: the same steps in two phases, each
+    # launch timestamped at its kernel's start and end by the launch itself
+    # (bb_attn_forward_timed), on the launch stream.
+    e = [(ev(), ev(), ev(), ev()) for _ in range(args.steps)]
+    for x in e:                  # create the HIP events behind them
+        for y in x:
+            y.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        e[i][0].record(stream)
-        call(i, launch | bb.BB_PHASE_UNITS)
-        e[i][1].record(stream)
-        call(i, launch | bb.BB_PHASE_MERGE)
-        e[i][2].record(stream)
+        call(i, launch | bb.BB_PHASE_UNITS, events=(e[i][0], e[i][1]))
+        call(i, launch | bb.BB_PHASE_MERGE, events=(e[i][2], e[i][3]))
     torch.cuda.synchronize()
-    units_ms = float(np.mean([a.elapsed_time(b_) for a, b_, _ in e]))
-    merge_ms = float(np.mean([b_.elapsed_time(c) for _, b_, c in e]))
+    units_ms = float(np.mean([x[0].elapsed_time(x[1]) for x in e]))
+    merge_ms = float(np.mean([x[2].elapsed_time(x[3]) for x in e]))
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)

@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "BB_OK", 1: "BB_ERR_NULL", 2: "BB_ERR_SHAPE", 3: "BB_ERR_DTYP
 
 # Every symbol include/bb_attn.h declares.
 EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_check",
-           "bb_attn_workspace_bytes", "bb_attn_forward", "bb_attn_forward_ex")
+           "bb_attn_workspace_bytes", "bb_attn_forward", "bb_attn_forward_ex",
+           "bb_attn_forward_timed")
 
 _lib = None
 
@@ -66,6 +67,8 @@ def lib():
     L.bb_attn_forward.argtypes = fwd
     L.bb_attn_forward_ex.restype = c_int
     L.bb_attn_forward_ex.argtypes = fwd + [ctypes.c_uint]
+    L.bb_attn_forward_timed.restype = c_int
+    L.bb_attn_forward_timed.argtypes = fwd + [ctypes.c_uint, vp, vp]
     _lib = L
     return L
 
@@ -136,20 +139,33 @@ def _check_device_tensor(name, t):
 
 
 def bb_attn_forward(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int,
-                    r: int, out, workspace, stream=None, flags: int = BB_LAUNCH_FUSED) -> None:
+                    r: int, out, workspace, stream=None, flags: int = BB_LAUNCH_FUSED,
+                    events=None) -> None:
     """Enqueue the forward on `stream` (default: torch's current stream).
 
     q, k, v, out: device tensors [B, H, L, d] (bf16 or fp32); pad_mask: uint8
     device tensor [B, L] or None; rand_idx: int32 device tensor [H, L/block-2, r]
     (or None when r == 0); workspace: uint8 device tensor from alloc_workspace.
+    events: optional (start, stop) pair of timing-enabled torch.cuda.Event that
+    the kernel launches themselves record (bb_attn_forward_timed); each must
+    have been recorded once before, so that its HIP event exists.
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("pad_mask", pad_mask),
                     ("rand_idx", rand_idx), ("workspace", workspace)):
         _check_device_tensor(name, t)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().bb_attn_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
-                                  B, H, L, d, block, r, _ptr(out), _dtype_code(q),
-                                  _ptr(workspace), ws_bytes, _stream_handle(q, stream), flags)
+    if events is None:
+        st = lib().bb_attn_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
+                                      B, H, L, d, block, r, _ptr(out), _dtype_code(q),
+                                      _ptr(workspace), ws_bytes, _stream_handle(q, stream), flags)
+    else:
+        e0, e1 = (int(e.cuda_event) for e in events)
+        if not e0 or not e1:
+            raise ValueError("events must have been recorded once (their HIP events do not exist yet)")
+        st = lib().bb_attn_forward_timed(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
+                                         B, H, L, d, block, r, _ptr(out), _dtype_code(q),
+                                         _ptr(workspace), ws_bytes, _stream_handle(q, stream), flags,
+                                         e0, e1)
     if st != BB_OK:
         raise BBError(st, "bb_attn_forward")
 

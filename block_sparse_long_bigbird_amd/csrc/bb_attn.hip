@@ -40,6 +40,7 @@
 //
 // fp32 inputs run the same code with fp32 MFMA (32x32x2) and fp32 P.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -400,10 +401,8 @@ __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, con
   float mc = ws.m * kScaleLog2;
 #pragma unroll
   for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-  // Each lane tests its own 16 scores; only a rescale needs the row max over
-  // both lane halves.
-  if (__any(lane_max(acc, ws.m) > ws.m + kRescaleTau / kScaleLog2)) {
-    const float mloc = subtile_max(acc, ws.m);
+  const float mloc = subtile_max(acc, ws.m);
+  if (__any(mloc - ws.m > kRescaleTau / kScaleLog2)) {
     const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -1028,8 +1027,12 @@ int persistent_grid(const void* kernel, int nt, long long n_units, unsigned* gri
   return BB_OK;
 }
 
+// Kernel launches of one call.  `ev0` / `ev1` (may be null): timestamps of
+// the start of the first and the end of the last kernel launched here (taken
+// by the launches themselves, hipExtLaunchKernelGGL, so they bracket the
+// kernels exactly).
 template <typename T, int BS, bool HAS_PAD>
-int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
+int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags, hipEvent_t ev0, hipEvent_t ev1) {
   using C = Cfg<T, BS>;
   const long long bhs = static_cast<long long>(B) * H;
   const long long per_g = 2LL * a.n_s * C::QSPLIT, per_m = static_cast<long long>(a.nb - 2) * C::QSPLIT;
@@ -1038,29 +1041,31 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags) {
   unsigned grid = 0;
   int st = BB_OK;
   if (units) {
+    hipEvent_t e1 = merge ? nullptr : ev1;
     if (flags & BB_LAUNCH_SPLIT) {
       st = persistent_grid(reinterpret_cast<const void*>(&bb_global_rows_kernel<T, BS, HAS_PAD>), C::NT,
                            bhs * per_g, &grid);
       if (st != BB_OK) return st;
-      bb_global_rows_kernel<T, BS, HAS_PAD><<<dim3(grid), dim3(C::NT), 0, stream>>>(
-          a, static_cast<int>(bhs * per_g));
+      hipExtLaunchKernelGGL(bb_global_rows_kernel<T, BS, HAS_PAD>, dim3(grid), dim3(C::NT), 0, stream, ev0,
+                            nullptr, 0, a, static_cast<int>(bhs * per_g));
       if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
       st = persistent_grid(reinterpret_cast<const void*>(&bb_middle_rows_kernel<T, BS, HAS_PAD>), C::NT,
                            bhs * per_m, &grid);
       if (st != BB_OK) return st;
-      bb_middle_rows_kernel<T, BS, HAS_PAD><<<dim3(grid), dim3(C::NT), 0, stream>>>(
-          a, static_cast<int>(bhs * per_m));
+      hipExtLaunchKernelGGL(bb_middle_rows_kernel<T, BS, HAS_PAD>, dim3(grid), dim3(C::NT), 0, stream, nullptr,
+                            e1, 0, a, static_cast<int>(bhs * per_m));
     } else {
       st = persistent_grid(reinterpret_cast<const void*>(&bb_fused_kernel<T, BS, HAS_PAD>), C::NT,
                            bhs * (per_g + per_m), &grid);
       if (st != BB_OK) return st;
-      bb_fused_kernel<T, BS, HAS_PAD><<<dim3(grid), dim3(C::NT), 0, stream>>>(
-          a, static_cast<int>(bhs * (per_g + per_m)));
+      hipExtLaunchKernelGGL(bb_fused_kernel<T, BS, HAS_PAD>, dim3(grid), dim3(C::NT), 0, stream, ev0, e1, 0, a,
+                            static_cast<int>(bhs * (per_g + per_m)));
     }
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   if (merge) {
-    bb_global_merge_kernel<T, BS><<<dim3(static_cast<unsigned>(bhs) * 2 * (BS / 4)), dim3(256), 0, stream>>>(a);
+    hipExtLaunchKernelGGL(bb_global_merge_kernel<T, BS>, dim3(static_cast<unsigned>(bhs) * 2 * (BS / 4)), dim3(256),
+                          0, stream, units ? nullptr : ev0, ev1, 0, a);
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   return BB_OK;
@@ -1093,10 +1098,10 @@ extern "C" size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block)
   return workspace_layout(B, H, nb, block).total;
 }
 
-extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
-                                  const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
-                                  void* out, int dtype, void* workspace, size_t workspace_bytes,
-                                  void* stream, unsigned flags) {
+extern "C" int bb_attn_forward_timed(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                     const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                                     void* out, int dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream, unsigned flags, void* start_event, void* stop_event) {
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
   if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE)) return BB_ERR_SHAPE;
   int nb = 0;
@@ -1132,13 +1137,24 @@ extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, c
   a.r = r;
   a.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
   const bool p = pad_mask != nullptr;
   if (dtype == BB_BF16) {
-    if (block == 64) return p ? launch<__bf16, 64, true>(a, B, H, s, flags) : launch<__bf16, 64, false>(a, B, H, s, flags);
-    return p ? launch<__bf16, 128, true>(a, B, H, s, flags) : launch<__bf16, 128, false>(a, B, H, s, flags);
+    if (block == 64)
+      return p ? launch<__bf16, 64, true>(a, B, H, s, flags, e0, e1) : launch<__bf16, 64, false>(a, B, H, s, flags, e0, e1);
+    return p ? launch<__bf16, 128, true>(a, B, H, s, flags, e0, e1) : launch<__bf16, 128, false>(a, B, H, s, flags, e0, e1);
   }
-  if (block == 64) return p ? launch<float, 64, true>(a, B, H, s, flags) : launch<float, 64, false>(a, B, H, s, flags);
-  return p ? launch<float, 128, true>(a, B, H, s, flags) : launch<float, 128, false>(a, B, H, s, flags);
+  if (block == 64)
+    return p ? launch<float, 64, true>(a, B, H, s, flags, e0, e1) : launch<float, 64, false>(a, B, H, s, flags, e0, e1);
+  return p ? launch<float, 128, true>(a, B, H, s, flags, e0, e1) : launch<float, 128, false>(a, B, H, s, flags, e0, e1);
+}
+
+extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                  const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                                  void* out, int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream, unsigned flags) {
+  return bb_attn_forward_timed(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace,
+                               workspace_bytes, stream, flags, nullptr, nullptr);
 }
 
 extern "C" int bb_attn_forward(const void* q, const void* k, const void* v, const uint8_t* pad_mask,

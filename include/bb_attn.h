@@ -142,6 +142,19 @@ int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_
                        void* out, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream, unsigned flags);
 
+/* bb_attn_forward_ex that also timestamps its kernels: start_event and
+ * stop_event (hipEvent_t created by the caller with timing enabled, or NULL)
+ * are recorded by the launches themselves at the start of the first and the
+ * end of the last kernel the call enqueues (with BB_PHASE_UNITS: exactly the
+ * work-unit launch), so hipEventElapsedTime between them is the kernels'
+ * execution time without enqueue gaps.  Same arguments, checks and errors as
+ * bb_attn_forward_ex; events are not touched when the call returns an error
+ * before launching. */
+int bb_attn_forward_timed(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                          const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                          void* out, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream, unsigned flags, void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,6 +165,36 @@ def test_two_phase_call_matches_single_call(dev, w):
         assert np.array_equal(out.float().cpu().numpy(), a)
 
 
+@pytest.mark.parametrize("w", [SMALL[6], SMALL[11]], ids=lambda w: w.name)
+def test_timed_entry_matches_and_times(dev, w):
+    """bb_attn_forward_timed: the same bits as the untimed call, for the whole call and
+    for each phase, and its launch-recorded events bracket a positive duration."""
+    say(f"case timed entry {w.name}")
+    inputs = make_inputs(w)
+    a, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_FUSED, inputs=inputs)
+    q, k, v, pad = inputs
+    ri = torch.from_numpy(bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)).to(dev)
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    dpad = None if pad is None else pad.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    for launch in (bb.BB_LAUNCH_FUSED, bb.BB_LAUNCH_SPLIT):
+        for phases in ((0,), (bb.BB_PHASE_UNITS, bb.BB_PHASE_MERGE)):
+            out = torch.full_like(dq, float("nan"))
+            ws = poisoned_workspace(w, dev)
+            evs = []
+            for phase in phases:
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for x in e:
+                    x.record(stream)
+                bb.bb_attn_forward(dq, dk, dv, dpad, ri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws,
+                                   flags=launch | phase, events=e)
+                evs.append(e)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.float().cpu().numpy(), a)
+            for e0, e1 in evs:
+                assert e0.elapsed_time(e1) > 0.0
+
+
 def test_deterministic_and_workspace_reuse(dev):
     """Same call twice gives identical bits; the workspace is ready for the next call,
     also for a different, smaller shape."""
