@@ -125,6 +125,11 @@ SMALL = [
     small("fp32_bs128_nb7_r2", B=1, H=2, L=7 * 128, block=128, r=2, dtype="fp32", data_seed=25),
     small("outliers_unscaled", B=1, H=2, L=16 * 64, block=64, r=3, outlier_frac=0.02,
           outlier_mult=8.0, data_seed=26),
+    # r at its maximum (16): middle units of 21 tiles run the tile loop in two
+    # trips (12 + 9 steps), with padding; and the same in fp32 with block 128
+    small("nb24_r16_pad_two_trips", B=2, H=2, L=24 * 64, block=64, r=16, pad="per_seq_blocks",
+          pad_lo_blocks=10, pad_hi_blocks=24, data_seed=27),
+    small("fp32_bs128_nb22_r16", B=1, H=1, L=22 * 128, block=128, r=16, dtype="fp32", data_seed=28),
 ]
 
 
