@@ -53,7 +53,6 @@ namespace {
 constexpr int kD = 64;                   // supported head dimension
 constexpr int kChunkTiles = 8;           // key tiles per global-row work unit
 constexpr int kMaxR = 16;                // random blocks per row, upper bound
-constexpr int kMaxTiles = 5 + kMaxR;     // longest tile list of a unit
 constexpr float kScaleLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
 constexpr float kMaskRaw = -10000.0f * 8.0f;  // -10000 on the logit, in q.k units
 constexpr float kRescaleTau = 8.0f;      // lazy rescale threshold (log2 units)
@@ -81,10 +80,8 @@ struct Cfg {
   static constexpr int NW = WQ * WK;                // waves per workgroup (4 or 8)
   static constexpr int NT = 64 * NW;                // threads per workgroup
   static constexpr int TILE = BS * ROWB;            // bytes of one K (or V) tile
-  // LDS ring depth.  Two stages: tile u+1 streams in while tile u is used.
-  // (A third stage lets two tiles fly, but the compiler's LDS-DMA wait
-  // tracking then drains the queue on one stage of every three.)
-  static constexpr int NSTAGE = 2;
+  // LDS ring: two stages (Stage<T, BS, 0/1>); tile u+1 streams in while tile
+  // u is used.
   static constexpr int DMA_MAT = BS * CPR / 64 / NW;  // DMA instructions per wave per matrix
   static constexpr int QC = CPR / 2;                // Q chunks per lane
   // key-group merge at the end: round with the most writers has WK/2 of them
@@ -184,19 +181,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
 }
 
-// One 64 x 16-byte DMA: lane offsets `voff` (32-bit) on the wave-uniform
-// global base `g`, into LDS at the wave-uniform address `m0` (+16 per lane).
-// The compiler cannot see that the asm reads `g` and M0 from a vector-memory
-// instruction, so it inserts no wait states for them: an SGPR written by a
-// VALU instruction (v_readlane, e.g. reloading a spilled base address) needs 5
-// before a vector-memory instruction reads it, an M0 write 1.  s_nop 4 gives
-// 5 whatever precedes the block.
-__device__ __forceinline__ void dma16(gchar_ptr g, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(g), "{m0}"(m0) : "memory");
-}
-
-// Two K and two V DMAs in one block: the leading s_nop 4 covers every input
-// (none is written inside), each M0 write gets its 1 wait state.
+// Two K and two V DMAs of 64 x 16 bytes each: lane offsets (32-bit) on the
+// wave-uniform global bases `kt` / `vt`, into LDS at the wave-uniform
+// addresses set in M0 (+16 per lane).  The compiler cannot see that the asm
+// reads the bases from a vector-memory instruction, so it inserts no wait
+// states for them: an SGPR written by a VALU instruction (v_readlane, e.g.
+// reloading a spilled base address) needs 5 before a vector-memory
+// instruction reads it.  The leading s_nop 4 gives 5 for every input (none is
+// written inside the block); each M0 write gets the 1 it needs.
 __device__ __forceinline__ void dma16x4(gchar_ptr kt, gchar_ptr vt, uint32_t ko0, uint32_t vo0, uint32_t ko1,
                                         uint32_t vo1, uint32_t mk0, uint32_t mv0, uint32_t mk1, uint32_t mv1) {
   asm volatile(
