@@ -227,7 +227,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}); (batch, head) units shard across GPUs with no "
               "communication, but no multi-GPU path is built here.", file=sys.stderr)
         sys.exit(2)
