@@ -134,10 +134,6 @@ __device__ __forceinline__ int perm_row(int i) {
   return 16 * (a >> 1) + 8 * gg + 4 * (a & 1) + c;
 }
 
-__device__ __forceinline__ bool has_zero_byte(uint64_t x) {
-  return ((x - 0x0101010101010101ull) & ~x & 0x8080808080808080ull) != 0;
-}
-
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -301,21 +297,35 @@ __device__ __forceinline__ uint32_t zero_byte_mask(uint64_t w) {
   return static_cast<uint32_t>(((t >> 7) * 0x0102040810204080ULL) >> 56);
 }
 
-// Key bias: -10000 on the logits of padded keys (-80000 in q.k units), taken
-// only when the subtile has a padded key.  The bias enters through one more
-// product into the score accumulator, an fp32 32x32x2 MFMA (one register per
-// operand): row i of A (key perm_row(i) of the subtile) carries the key's
-// bias in k-slot 0 (lanes 0..31), B holds 1 there for every query, k-slot 1
-// is zero.  -80000 * 1 is exact, so this is the fp32 add of the bias.
-__device__ __forceinline__ void apply_pad(f32x16& acc, const PadWords& w, int lane) {
-  if (!(has_zero_byte(w.p[0]) || has_zero_byte(w.p[1]) || has_zero_byte(w.p[2]) || has_zero_byte(w.p[3])))
-    return;
+// Key bias: -10000 on the logits of padded keys (-80000 in q.k units).  The
+// subtile's 32 pad bytes are classified on the scalar unit (wave-uniform):
+//   no padded key  -> bias 0, nothing to do (the common case);
+//   all 32 padded  -> one uniform bias, returned and folded by the softmax
+//                     into its max and exponent offset (no per-key work);
+//   mixed          -> the per-key bias enters the score accumulator through
+//                     one more product, an fp32 32x32x2 MFMA (one register
+//                     per operand): row i of A (key perm_row(i)) carries the
+//                     key's bias in k-slot 0 (lanes 0..31), B holds 1 there
+//                     for every query, k-slot 1 is zero; -80000 * 1 is exact,
+//                     so this is the fp32 add of the bias.  Returns 0.
+// The zero-byte test per word is exact: a byte b sets bit 7 of
+// (b - 1) & ~b only when b == 0, and a borrow leaves a byte only from a zero
+// byte, which is flagged already.
+__device__ __forceinline__ uint64_t zero_bytes_any(uint64_t x) {
+  return (x - 0x0101010101010101ull) & ~x & 0x8080808080808080ull;
+}
+
+__device__ __forceinline__ float apply_pad(f32x16& acc, const PadWords& w, int lane) {
+  if ((zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0)
+    return 0.0f;
+  if ((w.p[0] | w.p[1] | w.p[2] | w.p[3]) == 0) return kMaskRaw;
   const uint32_t m = zero_byte_mask(w.p[0]) | (zero_byte_mask(w.p[1]) << 8) |
                      (zero_byte_mask(w.p[2]) << 16) | (zero_byte_mask(w.p[3]) << 24);
   const int j = lane & 31;
   const bool lo = lane < 32;                        // lanes holding k-slot 0
   const bool padded = (m >> perm_row(j)) & 1u;
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? 1.0f : 0.0f, acc, 0, 0, 0);
+  return 0.0f;
 }
 
 // V^T operands of this wave's subtile of stage S.
@@ -381,19 +391,22 @@ __device__ __forceinline__ float subtile_max(const f32x16& acc, float m0) {
 
 // Online softmax of one score subtile (lane = query row, 16 of its 32 keys)
 // and O^T += V^T . P^T.  Registers only.  `first`: the unit's first tile
-// (wave-uniform), whose max starts the running max.
+// (wave-uniform), whose max starts the running max.  `bias` (wave-uniform, 0
+// or the padding bias): added to every score of the subtile, through the max
+// and the exponent offset rather than per score.
 template <typename T>
-__device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, const VOp<T>& vo, bool first) {
-  // P = 2^((s - m) c) against the running max m first; the tile's own max
-  // is reduced meanwhile, and only if it exceeds m by more than tau/c (rare)
-  // are O and l rescaled and P recomputed.  Keeps the exps off the critical
-  // path of the max reduction.
-  if (first) ws.m = subtile_max(acc, acc[15]);
+__device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, const VOp<T>& vo, bool first,
+                                           float bias) {
+  // P = 2^((s + bias - m) c) against the running max m first; the tile's own
+  // max is reduced meanwhile, and only if it exceeds m by more than tau/c
+  // (rare) are O and l rescaled and P recomputed.  Keeps the exps off the
+  // critical path of the max reduction.
+  if (first) ws.m = subtile_max(acc, acc[15]) + bias;
   float p[16];
-  float mc = ws.m * kScaleLog2;
+  float mc = (ws.m - bias) * kScaleLog2;
 #pragma unroll
   for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-  const float mloc = subtile_max(acc, ws.m);
+  const float mloc = fmaxf(subtile_max(acc, acc[15]) + bias, ws.m);
   if (__any(mloc - ws.m > kRescaleTau / kScaleLog2)) {
     const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
 #pragma unroll
@@ -403,7 +416,7 @@ __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, con
     }
     ws.l *= alpha;
     ws.m = mloc;
-    mc = ws.m * kScaleLog2;
+    mc = (ws.m - bias) * kScaleLog2;
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
   }
@@ -616,14 +629,15 @@ __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC]
     const kargs_ptr a = kargs();
     issue_tile<T, BS, 0>((gchar_ptr)(a->k) + nx.off, (gchar_ptr)(a->v) + nx.off, nx.tile0, wave, lane);
   }
-  if constexpr (HAS_PAD) apply_pad(s, pw, lane);
+  float pbias = 0.0f;
+  if constexpr (HAS_PAD) pbias = apply_pad(s, pw, lane);
   if (S == 1 && last && nx.pf) {
     // Q is dead after the score products: refill it for the next unit.  The
     // empty asm ties the loads after those products.
     asm volatile("" : "+v"(s) : : "memory");
     load_q<T, BS>(kargs()->q + nx.off + static_cast<size_t>(nx.q0) * Cfg<T, BS>::ROWB, wq, lane, qop);
   }
-  softmax_pv<T>(ws, s, vo, u == 0);
+  softmax_pv<T>(ws, s, vo, u == 0, pbias);
 }
 
 __device__ __forceinline__ void store_row8(char* dst, const float* x, __bf16*) {
