@@ -614,12 +614,19 @@ __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC]
   // step are complete (vmcnt = lgkmcnt = 0; on a unit's first step this also
   // covers the previous unit's output stores); after the barrier every wave's
   // part of tile u is visible and the stage of tile u-1 is free to refill.
+  // The pad bytes of tile u are loaded first, so that their scalar load
+  // completes under this wait and the barrier: scalar and LDS loads share one
+  // counter and scalar loads may return out of order, so an outstanding one
+  // would turn every later LDS wait of the step into a full drain.
+  PadWords pw;
+  if constexpr (HAS_PAD) {
+    pw = load_pad(pad_b + static_cast<size_t>(tile_u) * BS, kbase);
+    asm volatile("" ::: "memory");
+  }
   __builtin_amdgcn_s_waitcnt(7 << 4);
   ring_barrier();
   // Critical path first: K reads and the score products.  The V^T reads and
   // the DMA of the next tile are issued while the products run.
-  PadWords pw;
-  if constexpr (HAS_PAD) pw = load_pad(pad_b + static_cast<size_t>(tile_u) * BS, kbase);
   f32x16 s = scores<T, BS, S>(qop, kbase, lane);
   const VOp<T> vo = load_v<T, BS, S>(kbase, lane);
   const bool last = u + 1 == ntiles;
