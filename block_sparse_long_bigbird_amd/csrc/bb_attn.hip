@@ -203,7 +203,9 @@ __device__ __forceinline__ void issue_tile(gchar_ptr kbh, gchar_ptr vbh, int til
   using C = Cfg<T, BS>;
   const gchar_ptr kt = kbh + static_cast<size_t>(tile) * C::TILE;
   const gchar_ptr vt = vbh + static_cast<size_t>(tile) * C::TILE;
-  const uint32_t lk = lds_addr(Stage<T, BS, S>::k()), lv = lds_addr(Stage<T, BS, S>::v());
+  // (V's address as K's plus the tile size: converting a second generic
+  // pointer would cost a null check per DMA group)
+  const uint32_t lk = lds_addr(Stage<T, BS, S>::k()), lv = lk + C::TILE;
   static_assert(C::DMA_MAT % 2 == 0, "DMA instructions go in blocks of two per matrix");
   uint32_t ko[C::DMA_MAT], vo[C::DMA_MAT], mk[C::DMA_MAT], mv[C::DMA_MAT];
 #pragma unroll
