@@ -608,7 +608,7 @@ struct NextUnit {
 // stage 0 and, once this step's score products have consumed Q, its Q rows
 // into qop.
 template <typename T, int BS, int S, bool HAS_PAD>
-__device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC], int u, int ntiles,
+__device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC], bool first, bool last,
                                      int tile_u, int tile_fill, gchar_ptr kbh, gchar_ptr vbh,
                                      const uint8_t* pad_b, int wave, int lane, int kbase,
                                      const NextUnit& nx, int wq) {
@@ -631,7 +631,6 @@ __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC]
   // the DMA of the next tile are issued while the products run.
   f32x16 s = scores<T, BS, S>(qop, kbase, lane);
   const VOp<T> vo = load_v<T, BS, S>(kbase, lane);
-  const bool last = u + 1 == ntiles;
   if (!last) {
     issue_tile<T, BS, S ^ 1>(kbh, vbh, tile_fill, wave, lane);
   } else if (S == 1 && nx.pf) {
@@ -646,7 +645,7 @@ __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC]
     asm volatile("" : "+v"(s) : : "memory");
     load_q<T, BS>(kargs()->q + nx.off + static_cast<size_t>(nx.q0) * Cfg<T, BS>::ROWB, wq, lane, qop);
   }
-  softmax_pv<T>(ws, s, vo, u == 0, pbias);
+  softmax_pv<T>(ws, s, vo, first, pbias);
 }
 
 __device__ __forceinline__ void store_row8(char* dst, const float* x, __bf16*) {
@@ -745,7 +744,8 @@ __device__ __forceinline__ void finalize(WaveState& ws, const Unit& w, int wq, i
   float a0 = __builtin_amdgcn_exp2f((ws.m - mm) * kScaleLog2);
   float a1 = __builtin_amdgcn_exp2f((m1 - mm) * kScaleLog2);
   const float lh = ws.l * a0 + l1 * a1;             // this lane half's share of the row sum
-  const float l = lh + __shfl_xor(lh, 32);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lh), __float_as_uint(lh), false, false);
+  const float l = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);   // both lane halves of the row
   char* dst;
   float* pm = nullptr;
   float* pl = nullptr;
@@ -834,7 +834,9 @@ __device__ __forceinline__ void run(int n_units) {
   for (;;) {
     // Per-lane address arithmetic is redone for every unit rather than kept
     // live across the unit loop (register pressure).
-    int lane_u = lane;
+    // (The lane id is rebuilt from the exec mask rather than kept in a
+    // register: kept, it was spilled, and reloading it drained the prefetch.)
+    int lane_u = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
     asm volatile("" : "+v"(lane_u));
     const Cursor nxt = cursor_advance<T, BS, kind>(kargs(), cur, stride);
     const bool has_next = nxt.unit < end;
@@ -872,19 +874,24 @@ __device__ __forceinline__ void run(int n_units) {
     constexpr int TRIP = 12;
     static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
     for (int u = 0; u < ntiles; u += TRIP) {
+      // Tiles left from u.  Opaque, so that the step guards and the last-step
+      // test compare it with immediates rather than with one precomputed
+      // ntiles - k per step (scalar registers that would spill).
+      int rem = ntiles - u;
+      asm volatile("" : "+s"(rem));
       // tile ids of the trip, two 16-bit ids per scalar register (nb < 65536)
       uint32_t tp[(TRIP + 2) / 2];
 #pragma unroll
       for (int k = 0; k < (TRIP + 2) / 2; ++k) {
-        const uint32_t t0 = u + 2 * k < ntiles ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k)) : 0u;
-        const uint32_t t1 = u + 2 * k + 1 < ntiles ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k + 1)) : 0u;
+        const uint32_t t0 = 2 * k < rem ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k)) : 0u;
+        const uint32_t t1 = 2 * k + 1 < rem ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k + 1)) : 0u;
         tp[k] = t0 | (t1 << 16);
       }
 #define BB_TILE(k) static_cast<int>((tp[(k) >> 1] >> (16 * ((k) & 1))) & 0xffffu)
 #define BB_STEP(k)                                                                                  \
-  if (u + (k) < ntiles)                                                                             \
-    step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k), ntiles, BB_TILE(k), BB_TILE((k) + 1), kbh, vbh,    \
-                                  pad_b, wave, lane_u, kbase, nx, wq);
+  if ((k) < rem)                                                                                    \
+    step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k) == 0, (k) + 1 == rem, BB_TILE(k), BB_TILE((k) + 1),  \
+                                  kbh, vbh, pad_b, wave, lane_u, kbase, nx, wq);
       BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
       BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
