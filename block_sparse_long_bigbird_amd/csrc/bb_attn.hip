@@ -408,8 +408,12 @@ __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, con
   float mc = (ws.m - bias) * kScaleLog2;
 #pragma unroll
   for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-  const float mloc = fmaxf(subtile_max(acc, acc[15]) + bias, ws.m);
-  if (__any(mloc - ws.m > kRescaleTau / kScaleLog2)) {
+  // Each lane tests its own 16 scores; only a rescale needs the row max over
+  // both lane halves.
+  const float lm = lane_max(acc, acc[15]) + bias;
+  if (__any(lm - ws.m > kRescaleTau / kScaleLog2)) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+    const float mloc = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), ws.m);
     const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
