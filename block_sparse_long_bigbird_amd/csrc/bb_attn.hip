@@ -86,7 +86,9 @@ struct Cfg {
   static constexpr int QC = CPR / 2;                // Q chunks per lane
   // key-group merge at the end: round with the most writers has WK/2 of them
   static constexpr int MERGE_O = (WK / 2) * WQ * 16 * 64 * 4;   // 16 O registers per lane
-  static constexpr int MERGE_ML = (WK / 2) * WQ * 2 * 64 * 4;   // row max and row sum
+  // row max and row sum: WK/2 writers per query group in the wide rounds,
+  // both key groups 0 and 1 in the last one
+  static constexpr int MERGE_ML = (WK / 2 > 2 ? WK / 2 : 2) * WQ * 2 * 64 * 4;
   static_assert(DMA_MAT * 64 * NW == BS * CPR, "tile DMA must split evenly over waves");
   static_assert(CPR % 8 == 0, "swizzles act on groups of 8 chunks");
   static_assert(MERGE_O <= TILE, "each half of the merged O must fit in one K or V tile");
@@ -688,11 +690,73 @@ struct MergeML {
   }
 };
 
+// Last merge round for key group KEEP (0 or 1) of one query group: see
+// finalize().
+template <typename T, int BS, int KEEP>
+__device__ __forceinline__ void finalize_half(WaveState& ws, const Unit& w, int wq, int lane, float* mo0, float* mo1,
+                                              float* mml) {
+  using C = Cfg<T, BS>;
+  constexpr int GIVE = KEEP ^ 1;
+  {
+    float* mo_give = GIVE ? mo1 : mo0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mo_give[(wq * 16 + v) * 64 + lane] = ws.o[GIVE][v];
+    mml[((wq * 2 + KEEP) * 2) * 64 + lane] = ws.m;
+    mml[((wq * 2 + KEEP) * 2 + 1) * 64 + lane] = ws.l;
+  }
+  lds_barrier();
+  const int j = lane & 31, g = lane >> 5;
+  const float m1 = mml[((wq * 2 + GIVE) * 2) * 64 + lane], l1 = mml[((wq * 2 + GIVE) * 2 + 1) * 64 + lane];
+  const float mm = fmaxf(ws.m, m1);
+  float a0 = __builtin_amdgcn_exp2f((ws.m - mm) * kScaleLog2);
+  float a1 = __builtin_amdgcn_exp2f((m1 - mm) * kScaleLog2);
+  const float lh = ws.l * a0 + l1 * a1;             // this lane half's share of the row sum
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lh), __float_as_uint(lh), false, false);
+  const float l = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);   // both lane halves of the row
+  char* dst;
+  float* pm = nullptr;
+  float* pl = nullptr;
+  size_t pidx = 0;
+  if (w.gsel < 0) {
+    const float inv = __builtin_amdgcn_rcpf(l);   // 1 ulp
+    a0 *= inv;
+    a1 *= inv;
+    dst = kargs()->out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
+  } else {
+    const kargs_ptr a = kargs();
+    pidx = w.pbase + wq * 32 + j;
+    dst = reinterpret_cast<char*>(a->po + pidx * kD);
+    pm = a->pm;
+    pl = a->pl;
+  }
+  const float* mo_keep = KEEP ? mo1 : mo0;
+  float x[2][8];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      x[h8][e] = ws.o[KEEP][8 * h8 + e] * a0 + mo_keep[(wq * 16 + 8 * h8 + e) * 64 + lane] * a1;
+  if (w.gsel < 0) {
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+      store_row8(dst + (KEEP * 32 + 16 * h8 + 8 * g) * C::ES, x[h8], static_cast<T*>(nullptr));
+    return;
+  }
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+    store_row8(dst + (KEEP * 32 + 16 * h8 + 8 * g) * 4, x[h8], static_cast<float*>(nullptr));
+  if (KEEP == 0 && g == 0) {
+    pm[pidx] = mm;
+    pl[pidx] = l;
+  }
+}
+
 // End of a unit: merge the key groups of each query group (tree over LDS,
 // O through stage S -- the stage of the unit's last tile -- and (max, sum)
 // through MergeML), then write the output rows (middle unit) or the partial
-// (global unit).  Key group 0 finishes the last round; for a middle unit the
-// division by the row sum is folded into the two merge weights.
+// (global unit).  Key groups 0 and 1 finish the last round together, each
+// on half of the head dims; for a middle unit the division by the row sum is
+// folded into the two merge weights.
 template <typename T, int BS, int S>
 __device__ __forceinline__ void finalize(WaveState& ws, const Unit& w, int wq, int wk, int lane) {
   using C = Cfg<T, BS>;
@@ -729,70 +793,19 @@ __device__ __forceinline__ void finalize(WaveState& ws, const Unit& w, int wq, i
       ws.m = mm;
     }
   }
-  // last round: key group 1 -> key group 0
+  // Last round, between key groups 0 and 1, split by head dims: wave wk
+  // keeps dims [32 wk, 32 wk + 32) (its o[wk]) and hands the other half to
+  // its partner through stage S (o[0] halves in the K part, o[1] halves in
+  // the V part); both publish (max, sum).  Each then merges and writes its
+  // half, so the two waves finish together.  (Wave-uniform branch on wk, so
+  // the register arrays are indexed by constants only.)
   lds_barrier();
-  if (wk == 1) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      mo0[(wq * 16 + v) * 64 + lane] = ws.o[0][v];
-      mo1[(wq * 16 + v) * 64 + lane] = ws.o[1][v];
-    }
-    mml[(wq * 2) * 64 + lane] = ws.m;
-    mml[(wq * 2 + 1) * 64 + lane] = ws.l;
-  }
-  lds_barrier();
-  if (wk != 0) return;
-  const int j = lane & 31, g = lane >> 5;
-  const float m1 = mml[(wq * 2) * 64 + lane], l1 = mml[(wq * 2 + 1) * 64 + lane];
-  const float mm = fmaxf(ws.m, m1);
-  float a0 = __builtin_amdgcn_exp2f((ws.m - mm) * kScaleLog2);
-  float a1 = __builtin_amdgcn_exp2f((m1 - mm) * kScaleLog2);
-  const float lh = ws.l * a0 + l1 * a1;             // this lane half's share of the row sum
-  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lh), __float_as_uint(lh), false, false);
-  const float l = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);   // both lane halves of the row
-  char* dst;
-  float* pm = nullptr;
-  float* pl = nullptr;
-  size_t pidx = 0;
-  if (w.gsel < 0) {
-    const float inv = __builtin_amdgcn_rcpf(l);   // 1 ulp
-    a0 *= inv;
-    a1 *= inv;
-    dst = kargs()->out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
-  } else {
-    const kargs_ptr a = kargs();
-    pidx = w.pbase + wq * 32 + j;
-    dst = reinterpret_cast<char*>(a->po + pidx * kD);
-    pm = a->pm;
-    pl = a->pl;
-  }
-  float x[2][2][8];
-#pragma unroll
-  for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-    for (int h8 = 0; h8 < 2; ++h8)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float* mo = dh ? mo1 : mo0;
-        x[dh][h8][e] = ws.o[dh][8 * h8 + e] * a0 + mo[(wq * 16 + 8 * h8 + e) * 64 + lane] * a1;
-      }
-  if (w.gsel < 0) {
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8)
-        store_row8(dst + (dh * 32 + 16 * h8 + 8 * g) * C::ES, x[dh][h8], static_cast<T*>(nullptr));
-    return;
-  }
-#pragma unroll
-  for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-    for (int h8 = 0; h8 < 2; ++h8)
-      store_row8(dst + (dh * 32 + 16 * h8 + 8 * g) * 4, x[dh][h8], static_cast<float*>(nullptr));
-  if (g == 0) {
-    pm[pidx] = mm;
-    pl[pidx] = l;
-  }
+  if (wk == 0)
+    finalize_half<T, BS, 0>(ws, w, wq, lane, mo0, mo1, mml);
+  else if (wk == 1)
+    finalize_half<T, BS, 1>(ws, w, wq, lane, mo0, mo1, mml);
+  else
+    lds_barrier();   // key groups 2 and 3 (block 128) are merged already: the round's second barrier
 }
 
 // A persistent workgroup: it runs a fixed sequence of work units back to back,
