@@ -103,7 +103,8 @@ struct Args {
   char* out;
   float* pm;       // [B*H][2][n_s][BS] partial row max (q.k units)
   float* pl;       // [B*H][2][n_s][BS] partial row sum
-  float* po;       // [B*H][2][n_s][BS][kD] partial unnormalised output
+  float* po;       // [B*H][2][n_s][BS][kD] partial unnormalised output; each 64-row unit
+                   // block is stored lane-major (partial_slot())
   int H, L, nb, r, n_s;
 };
 
@@ -690,6 +691,14 @@ struct MergeML {
   }
 };
 
+// Float offset, inside a 64-row x 64-dim partial block of a global unit, of
+// the 4 dims [32 keep + 16 (q / 2) + 8 g + 4 (q % 2), +4) of row 32 wq + j,
+// where lane = j + 32 g: blocks of 64 lanes x 4 floats per (wq, keep, q), so
+// that a wave's store of one q is 1 KB contiguous.
+__device__ __forceinline__ int partial_slot(int wq, int keep, int q, int lane) {
+  return ((wq * 2 + keep) * 4 + q) * 256 + lane * 4;
+}
+
 // Last merge round for key group KEEP (0 or 1) of one query group: see
 // finalize().
 template <typename T, int BS, int KEEP>
@@ -742,9 +751,16 @@ __device__ __forceinline__ void finalize_half(WaveState& ws, const Unit& w, int 
       store_row8(dst + (KEEP * 32 + 16 * h8 + 8 * g) * C::ES, x[h8], static_cast<T*>(nullptr));
     return;
   }
+  // Partial O, lane-major inside the unit's 64 x 64 block: every store writes
+  // 1 KB contiguous (layout in partial_slot()).
+  float* blk = reinterpret_cast<float*>(dst) - static_cast<size_t>(wq * 32 + j) * kD;
 #pragma unroll
   for (int h8 = 0; h8 < 2; ++h8)
-    store_row8(dst + (KEEP * 32 + 16 * h8 + 8 * g) * 4, x[h8], static_cast<float*>(nullptr));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 v4 = {x[h8][4 * hf], x[h8][4 * hf + 1], x[h8][4 * hf + 2], x[h8][4 * hf + 3]};
+      *reinterpret_cast<f32x4*>(blk + partial_slot(wq, KEEP, 2 * h8 + hf, lane)) = v4;
+    }
   if (KEEP == 0 && g == 0) {
     pm[pidx] = mm;
     pl[pidx] = l;
@@ -937,62 +953,76 @@ __device__ __forceinline__ void run(int n_units) {
 // the n_s key chunks (row max m_s, row sum l_s, unnormalised O_s) combine as
 // out = sum_s 2^((m_s - m)c) O_s / sum_s 2^((m_s - m)c) l_s, m = max_s m_s.
 // Runs as its own launch after the global-row units, so their partials are
-// complete and visible without any in-kernel fence.  A workgroup covers 4
-// query rows x 16 float4 columns; the chunks of each output are split over
-// kMergeSplit threads (strided, each a single online pass), whose (m, l, O)
-// are then combined through LDS in a fixed order, so the result is
-// deterministic.
+// complete and visible without any in-kernel fence.  A workgroup covers 8
+// rows of one query group of one 64-row unit block, all 64 dims: thread
+// (cs, q, g, jj) takes the 4-dim groups (keep 0 and 1, q) of row 8 rb + jj
+// for lane half g (so each chunk's loads are 128-byte runs of the partial
+// layout), over the chunks s = cs, cs + kMergeSplit, ... in one online pass;
+// the kMergeSplit chunk groups are then combined through LDS in a fixed
+// order, so the result is deterministic.
 constexpr int kMergeSplit = 4;
 
 template <typename T, int BS>
-__global__ void __launch_bounds__(256) bb_global_merge_kernel(Args a) {
+__global__ void __launch_bounds__(64 * kMergeSplit) bb_global_merge_kernel(Args a) {
   constexpr int ROWB = kD * sizeof(T);
-  constexpr int SLICES = BS / 4;
+  constexpr int UB = BS / 64;                                 // 64-row unit blocks per query block
   __shared__ float s_m[kMergeSplit][64], s_l[kMergeSplit][64];
-  __shared__ f32x4 s_o[kMergeSplit][64];
-  const int slice = blockIdx.x % SLICES, gblk = blockIdx.x / SLICES;
+  __shared__ f32x4 s_o[kMergeSplit][2][64];
+  const int rb = blockIdx.x & 3;                              // 8-row slice of the query group
+  const int wq = (blockIdx.x >> 2) & 1;
+  const int rest = blockIdx.x >> 3;
+  const int qh = rest % UB, gblk = rest / UB;
   const int bh = gblk >> 1, gsel = gblk & 1;
   const int qb = gsel ? a.nb - 1 : 0;
-  const int sg = threadIdx.x >> 6, o = threadIdx.x & 63;      // chunk group, output slot
-  const int ql = slice * 4 + (o >> 4), dq = o & 15;
+  const int cs = threadIdx.x >> 6, t = threadIdx.x & 63;
+  const int q = t >> 4, g = (t >> 3) & 1, j = rb * 8 + (t & 7);
+  const int lane = j + 32 * g;
+  const int row = qh * 64 + wq * 32 + j;                      // row inside the query block
   const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.n_s;
-  // One pass, running max first (online rescaling), chunks in fixed order;
-  // unrolled by two so that two chunks' loads are in flight together.
   float m = -__builtin_inff();
   float den = 0.0f;
-  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 num[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll 2
-  for (int s = sg; s < a.n_s; s += kMergeSplit) {
-    const size_t pi = (base + s) * BS + ql;
+  for (int s = cs; s < a.n_s; s += kMergeSplit) {
+    const size_t pi = (base + s) * BS + row;
+    const float* blk = a.po + ((base + s) * BS + qh * 64) * kD;
     const float ms = a.pm[pi], ls = a.pl[pi];
-    const f32x4 os = *reinterpret_cast<const f32x4*>(a.po + pi * kD + dq * 4);
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(blk + partial_slot(wq, 0, q, lane));
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(blk + partial_slot(wq, 1, q, lane));
     const float mn = fmaxf(m, ms);
     const float c0 = __builtin_amdgcn_exp2f((m - mn) * kScaleLog2);   // 0 while m is -inf
     const float c1 = __builtin_amdgcn_exp2f((ms - mn) * kScaleLog2);
     den = den * c0 + ls * c1;
-    num = num * c0 + os * c1;
+    num[0] = num[0] * c0 + o0 * c1;
+    num[1] = num[1] * c0 + o1 * c1;
     m = mn;
   }
-  s_m[sg][o] = m;
-  s_l[sg][o] = den;
-  s_o[sg][o] = num;
+  s_m[cs][t] = m;
+  s_l[cs][t] = den;
+  s_o[cs][0][t] = num[0];
+  s_o[cs][1][t] = num[1];
   __syncthreads();
-  if (sg != 0) return;
-  float mm = s_m[0][o];
+  if (cs != 0) return;
+  float mm = s_m[0][t];
 #pragma unroll
-  for (int g = 1; g < kMergeSplit; ++g) mm = fmaxf(mm, s_m[g][o]);
+  for (int c = 1; c < kMergeSplit; ++c) mm = fmaxf(mm, s_m[c][t]);
   float dd = 0.0f;
-  f32x4 nn = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 nn[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-  for (int g = 0; g < kMergeSplit; ++g) {
-    if (s_m[g][o] == -__builtin_inff()) continue;           // group had no chunk
-    const float w = __builtin_amdgcn_exp2f((s_m[g][o] - mm) * kScaleLog2);
-    dd += w * s_l[g][o];
-    nn += w * s_o[g][o];
+  for (int c = 0; c < kMergeSplit; ++c) {
+    if (s_m[c][t] == -__builtin_inff()) continue;             // group had no chunk
+    const float w = __builtin_amdgcn_exp2f((s_m[c][t] - mm) * kScaleLog2);
+    dd += w * s_l[c][t];
+    nn[0] += w * s_o[c][0][t];
+    nn[1] += w * s_o[c][1][t];
   }
-  store_f32x4(a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + ql) * ROWB +
-                  dq * 4 * sizeof(T),
-              nn * __builtin_amdgcn_rcpf(dd), static_cast<T*>(nullptr));
+  const float inv = __builtin_amdgcn_rcpf(dd);
+  char* orow = a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + row) * ROWB;
+#pragma unroll
+  for (int keep = 0; keep < 2; ++keep) {
+    const int d0 = 32 * keep + 16 * (q >> 1) + 8 * g + 4 * (q & 1);
+    store_f32x4(orow + d0 * sizeof(T), nn[keep] * inv, static_cast<T*>(nullptr));
+  }
 }
 
 template <typename T, int BS, bool HAS_PAD>
@@ -1103,7 +1133,7 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags, hipE
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   if (merge) {
-    hipExtLaunchKernelGGL(bb_global_merge_kernel<T, BS>, dim3(static_cast<unsigned>(bhs) * 2 * (BS / 4)), dim3(256),
+    hipExtLaunchKernelGGL(bb_global_merge_kernel<T, BS>, dim3(static_cast<unsigned>(bhs) * 2 * (BS / 64) * 2 * 4), dim3(64 * kMergeSplit),
                           0, stream, units ? nullptr : ev0, ev1, 0, a);
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
