@@ -6,7 +6,9 @@ never does.
 """
 from .bigbird_oracle import (  # noqa: F401
     MASK_OFFSET,
+    attention_backward,
     attention_forward,
+    attention_lse,
     attention_probs,
     attention_rows,
     block_adjacency,

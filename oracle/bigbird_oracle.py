@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for BigBird block-sparse self-attention (forward).
+"""Plain fp64 CPU oracle for BigBird block-sparse self-attention (forward and backward).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this module: only the test suite, the smoke check and the CPU-baseline
@@ -33,9 +33,21 @@ attention.  Rows may be evaluated in groups (each row's softmax is
 independent), which bounds host memory at long L; nothing else is blocked,
 fused or reordered.
 
+Backward (the gradient of the same function; the pages train this layer with
+recomputation of the forward, [P2-pattern] page, section on the encoder's
+recompute layer): with P the softmax above, O = P V, an upstream gradient dO
+and s the scaled, biased logits,
+  dV = P^T dO,  dP = dO V^T,  D_t = sum_d dO[t] O[t],
+  dS = P * (dP - D),  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d);
+the pad offset is a constant and has no gradient.  The row log-sum-exp
+LSE_t = log sum_u exp(s_tu) over the allowed keys is what a backward pass
+needs from the forward to rebuild P.
+
 Pins: see the test suite (brute force on tiny inputs, a hand-derived golden
 fixture, closed-form allowed-key counts, dense/global special cases against
-torch's scaled_dot_product_attention, invariants).
+torch's scaled_dot_product_attention, invariants; for the backward, central
+finite differences of the forward, float64 autograd of an independently
+written dense masked attention, and exact invariants).
 """
 
 from __future__ import annotations
@@ -181,3 +193,85 @@ def attention_forward(q, k, v, pad_mask, rand_idx, block: int,
             out[b, h, rows] = attention_rows(q[b, h], k[b, h], v[b, h], pad_b,
                                              adjs[h], block, rows)
     return out
+
+
+def _logits_rows(q, k, pad_b, adj, block: int, rows) -> np.ndarray:
+    """Scaled, biased logits of rows `rows`, -inf off the pattern: fp64 [len(rows), L]."""
+    L, d = k.shape
+    s = (q[rows] @ k.T) / math.sqrt(d)
+    if pad_b is not None:
+        s = s + MASK_OFFSET * (np.asarray(pad_b) == 0).astype(np.float64)[None, :]
+    return np.where(_mask_rows(adj, block, rows), s, -np.inf)
+
+
+def attention_lse(q, k, pad_mask, rand_idx, block: int, units=None) -> np.ndarray:
+    """Row log-sum-exp of the logits over the allowed keys: fp64 [B, H, L].
+
+    LSE_t = log sum_u exp(s_tu), natural log, s as in the forward.
+    units: optional (b, h) pairs to evaluate; other units are NaN.
+    """
+    B, H, L, d = np.shape(q)
+    nb = num_blocks(L, block)
+    rand_idx = np.asarray(rand_idx)
+    r = rand_idx.shape[2] if rand_idx.ndim == 3 else 0
+    check_rand_idx(rand_idx, H, L, block, r)
+    out = np.full((B, H, L), np.nan, dtype=np.float64)
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(H)]
+    for b, h in units:
+        adj = block_adjacency(rand_idx[h], nb)
+        pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
+        s = _logits_rows(np.asarray(q[b, h], np.float64), np.asarray(k[b, h], np.float64),
+                         pad_b, adj, block, np.arange(L))
+        m = s.max(axis=1, keepdims=True)
+        out[b, h] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+    return out
+
+
+def attention_backward(q, k, v, pad_mask, rand_idx, block: int, dout, units=None,
+                       row_group: int = 4096):
+    """Gradients (dq, dk, dv) of sum(out * dout) for the forward above, fp64.
+
+    q, k, v, dout: [B, H, L, d]; pad_mask [B, L] or None; rand_idx [H, nb-2, r].
+    Follows the formulas in the module docstring, one (b, h) at a time; rows
+    may be taken in groups (dK and dV are sums over rows, added group by group).
+    units: optional (b, h) pairs to evaluate; other units are NaN.
+    Returns three fp64 [B, H, L, d] arrays.
+    """
+    B, H, L, d = np.shape(q)
+    nb = num_blocks(L, block)
+    rand_idx = np.asarray(rand_idx)
+    r = rand_idx.shape[2] if rand_idx.ndim == 3 else 0
+    check_rand_idx(rand_idx, H, L, block, r)
+    dq = np.full((B, H, L, d), np.nan, dtype=np.float64)
+    dk = np.full((B, H, L, d), np.nan, dtype=np.float64)
+    dv = np.full((B, H, L, d), np.nan, dtype=np.float64)
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(H)]
+    scale = 1.0 / math.sqrt(d)
+    for b, h in units:
+        adj = block_adjacency(rand_idx[h], nb)
+        pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
+        qb = np.asarray(q[b, h], np.float64)
+        kb = np.asarray(k[b, h], np.float64)
+        vb = np.asarray(v[b, h], np.float64)
+        gb = np.asarray(dout[b, h], np.float64)
+        dk_acc = np.zeros((L, d))
+        dv_acc = np.zeros((L, d))
+        for r0 in range(0, L, row_group):
+            rows = np.arange(r0, min(L, r0 + row_group))
+            s = _logits_rows(qb, kb, pad_b, adj, block, rows)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)          # P, rows of the softmax
+            o = p @ vb                                     # O
+            g = gb[rows]                                   # dO
+            dv_acc += p.T @ g                              # dV = P^T dO
+            dp = g @ vb.T                                  # dP = dO V^T
+            dsum = (g * o).sum(axis=1, keepdims=True)      # D = rowsum(dO * O)
+            ds = p * (dp - dsum)                           # dS = P (dP - D)
+            dq[b, h, rows] = (ds @ kb) * scale             # dQ = dS K / sqrt(d)
+            dk_acc += (ds.T @ qb[rows]) * scale            # dK = dS^T Q / sqrt(d)
+        dk[b, h] = dk_acc
+        dv[b, h] = dv_acc
+    return dq, dk, dv
