@@ -31,7 +31,8 @@ STATUS_NAMES = {0: "BB_OK", 1: "BB_ERR_NULL", 2: "BB_ERR_SHAPE", 3: "BB_ERR_DTYP
 # Every symbol include/bb_attn.h declares.
 EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_check",
            "bb_attn_workspace_bytes", "bb_attn_forward", "bb_attn_forward_ex",
-           "bb_attn_forward_timed")
+           "bb_attn_forward_timed", "bb_attn_forward_lse", "bb_rand_idx_invert",
+           "bb_attn_backward_workspace_bytes", "bb_attn_backward")
 
 _lib = None
 
@@ -69,6 +70,15 @@ def lib():
     L.bb_attn_forward_ex.argtypes = fwd + [ctypes.c_uint]
     L.bb_attn_forward_timed.restype = c_int
     L.bb_attn_forward_timed.argtypes = fwd + [ctypes.c_uint, vp, vp]
+    L.bb_attn_forward_lse.restype = c_int
+    L.bb_attn_forward_lse.argtypes = fwd + [vp]
+    L.bb_rand_idx_invert.restype = c_int
+    L.bb_rand_idx_invert.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp]
+    L.bb_attn_backward_workspace_bytes.restype = c_size
+    L.bb_attn_backward_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    L.bb_attn_backward.restype = c_int
+    L.bb_attn_backward.argtypes = ([vp, vp, vp, vp, vp, vp, vp] + [c_int] * 6 +
+                                   [vp, vp, vp, vp, vp, vp, c_int, vp, c_size, vp])
     _lib = L
     return L
 
@@ -183,3 +193,56 @@ def forward(q, k, v, rand_idx, pad_mask=None, block: int = 64, out=None, workspa
     bb_attn_forward(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, workspace,
                     stream=stream, flags=flags)
     return out
+
+
+def bb_attn_forward_lse(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int,
+                        r: int, out, workspace, lse, stream=None) -> None:
+    """The forward that also writes the row log-sum-exp: lse is a float32
+    device tensor [B, H, L] (natural log)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("pad_mask", pad_mask),
+                    ("rand_idx", rand_idx), ("workspace", workspace), ("lse", lse)):
+        _check_device_tensor(name, t)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().bb_attn_forward_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
+                                   B, H, L, d, block, r, _ptr(out), _dtype_code(q),
+                                   _ptr(workspace), ws_bytes, _stream_handle(q, stream), _ptr(lse))
+    if st != BB_OK:
+        raise BBError(st, "bb_attn_forward_lse")
+
+
+def bb_rand_idx_invert(rand_idx, H: int, L: int, block: int, r: int):
+    """Host inverse of a random-block table: (inv_off int32 [H, nb+1],
+    inv_rows int32 [H * (nb-2) * r])."""
+    nb = L // block if block > 0 else 0
+    a = np.ascontiguousarray(np.asarray(rand_idx), dtype=np.int32)
+    off = np.zeros((max(H, 0), max(nb + 1, 0)), dtype=np.int32)
+    rows = np.zeros(max(H * max(nb - 2, 0) * max(r, 0), 0), dtype=np.int32)
+    st = lib().bb_rand_idx_invert(a.ctypes.data if a.size else None, H, L, block, r,
+                                  off.ctypes.data if off.size else None,
+                                  rows.ctypes.data if rows.size else None)
+    if st != BB_OK:
+        raise BBError(st, "bb_rand_idx_invert")
+    return off, rows
+
+
+def bb_attn_backward_workspace_bytes(B: int, H: int, L: int, d: int, block: int) -> int:
+    return int(lib().bb_attn_backward_workspace_bytes(B, H, L, d, block))
+
+
+def bb_attn_backward(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B: int, H: int, L: int,
+                     d: int, block: int, r: int, out, dout, lse, dq, dk, dv, workspace,
+                     stream=None) -> None:
+    """Enqueue the backward on `stream` (default: torch's current stream).
+    inv_off / inv_rows: int32 device tensors from bb_rand_idx_invert."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("pad_mask", pad_mask), ("rand_idx", rand_idx),
+                    ("inv_off", inv_off), ("inv_rows", inv_rows), ("out", out), ("dout", dout),
+                    ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv), ("workspace", workspace)):
+        _check_device_tensor(name, t)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().bb_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
+                                _ptr(inv_off), _ptr(inv_rows), B, H, L, d, block, r, _ptr(out),
+                                _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _dtype_code(q), _ptr(workspace), ws_bytes,
+                                _stream_handle(q, stream))
+    if st != BB_OK:
+        raise BBError(st, "bb_attn_backward")

@@ -117,3 +117,29 @@ extern "C" int bb_rand_idx_check(const int32_t* rand_idx, int H, int L, int bloc
   }
   return BB_OK;
 }
+
+extern "C" int bb_rand_idx_invert(const int32_t* rand_idx, int H, int L, int block, int r, int32_t* inv_off,
+                                  int32_t* inv_rows) {
+  const int st = bb_rand_idx_check(rand_idx, H, L, block, r);
+  if (st != BB_OK) return st;
+  const int nb = L / block;
+  if (H == 0) return BB_OK;
+  if (inv_off == nullptr || (r > 0 && inv_rows == nullptr)) return BB_ERR_NULL;
+  const size_t per_head = static_cast<size_t>(nb - 2) * r;
+  for (int h = 0; h < H; ++h) {
+    int32_t* off = inv_off + static_cast<size_t>(h) * (nb + 1);
+    for (int j = 0; j <= nb; ++j) off[j] = 0;
+    // counts per key block, then exclusive prefix sums (absolute offsets)
+    for (size_t e = 0; e < per_head; ++e) ++off[rand_idx[h * per_head + e] + 1];
+    off[0] = static_cast<int32_t>(h * per_head);
+    for (int j = 1; j <= nb; ++j) off[j] += off[j - 1];
+    // fill in increasing row order: rows come out ascending within each key block
+    std::vector<int32_t> cursor(off, off + nb);
+    for (int i = 1; i <= nb - 2; ++i)
+      for (int t = 0; t < r; ++t) {
+        const int j = rand_idx[h * per_head + static_cast<size_t>(i - 1) * r + t];
+        inv_rows[cursor[j]++] = i;
+      }
+  }
+  return BB_OK;
+}

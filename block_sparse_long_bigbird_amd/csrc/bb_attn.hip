@@ -56,6 +56,7 @@ constexpr int kMaxR = 16;                // random blocks per row, upper bound
 constexpr float kScaleLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
 constexpr float kMaskRaw = -10000.0f * 8.0f;  // -10000 on the logit, in q.k units
 constexpr float kRescaleTau = 8.0f;      // lazy rescale threshold (log2 units)
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -105,6 +106,7 @@ struct Args {
   float* pl;       // [B*H][2][n_s][BS] partial row sum
   float* po;       // [B*H][2][n_s][BS][kD] partial unnormalised output; each 64-row unit
                    // block is stored lane-major (partial_slot())
+  float* lse;      // [B*H][L] natural-log row log-sum-exp of the logits, or null (not written)
   int H, L, nb, r, n_s;
 };
 
@@ -731,6 +733,9 @@ __device__ __forceinline__ void finalize_half(WaveState& ws, const Unit& w, int 
     a0 *= inv;
     a1 *= inv;
     dst = kargs()->out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
+    float* lse = kargs()->lse;
+    if (KEEP == 0 && g == 0 && lse != nullptr)   // LSE = m / sqrt(d) + ln(l)
+      lse[w.off / C::ROWB + w.q0 + wq * 32 + j] = (mm * kScaleLog2 + __builtin_amdgcn_logf(l)) * kLn2;
   } else {
     const kargs_ptr a = kargs();
     pidx = w.pbase + wq * 32 + j;
@@ -1018,6 +1023,9 @@ __global__ void __launch_bounds__(64 * kMergeSplit) bb_global_merge_kernel(Args 
   }
   const float inv = __builtin_amdgcn_rcpf(dd);
   char* orow = a.out + (static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + row) * ROWB;
+  if (a.lse != nullptr && q == 0 && g == 0)
+    a.lse[static_cast<size_t>(bh) * a.L + static_cast<size_t>(qb) * BS + row] =
+        (mm * kScaleLog2 + __builtin_amdgcn_logf(dd)) * kLn2;
 #pragma unroll
   for (int keep = 0; keep < 2; ++keep) {
     const int d0 = 32 * keep + 16 * (q >> 1) + 8 * g + 4 * (q & 1);
@@ -1036,6 +1044,593 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
 template <typename T, int BS, bool HAS_PAD>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(4))) bb_middle_rows_kernel(Args, int n_units) {
   run<T, BS, 2, HAS_PAD>(n_units);
+}
+
+// ================================================================ backward ==
+// Gradients of the same attention (dQ, dK, dV of sum(out * dO)), the
+// textbook softmax-attention backward restricted to the block pattern:
+//   P = 2^(s c + bias c - LSE2) rebuilt from the forward's row log-sum-exp
+//   (LSE2 = LSE log2(e), c = log2(e)/sqrt(d)), D_t = sum_d dO[t] O[t],
+//   dS = P (dP - D) with dP = dO V^T,
+//   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO.
+// Three passes over the pattern plus two small kernels:
+//   bb_bwd_pre_kernel    D and LSE2 per row;
+//   bb_bwd_dq_kernel     query-stationary (the forward's work units): per key
+//                        tile S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
+//                        the two global query blocks as split-K chunks;
+//   bb_bwd_dkdv_kernel   key-stationary: a middle key block j is seen by the
+//                        global query blocks, the band rows {j-1, j, j+1} and
+//                        the middle rows whose random list holds j (the
+//                        inverted table); per query tile S = Q K^T, dP = dO V^T,
+//                        dV^T += dO^T P, dK^T += Q^T dS; the two global key
+//                        blocks (seen by every query block) as split-K chunks;
+//   bb_bwd_reduce_kernel sums the split-K partials of those four blocks.
+// Every pass stages its streamed tiles through the same two-stage LDS ring
+// as the forward; a tile that is read both as rows and transposed is read
+// one of the two ways through the other matrix's swizzle (correct, with
+// some bank conflicts).
+
+struct BwdArgs {
+  Args f;                   // q, k, v, pad, rand_idx and the sizes (first member: kargs() reads it)
+  const char* o;            // forward output O [B*H][L][d]
+  const char* dout;         // dO [B*H][L][d]
+  const float* lse;         // forward row log-sum-exp (natural log) [B*H][L]
+  const int32_t* inv_off;   // [H][nb+1] ranges of inv_rows per (head, key block)
+  const int32_t* inv_rows;  // middle query blocks holding each key block in their random list
+  float* lse2;              // workspace [B*H][L]: LSE * log2(e)
+  float* dsum;              // workspace [B*H][L]: D
+  float* dq_part;           // workspace [B*H][2][n_s][BS][d], lane-major 64 x 64 blocks
+  float* dk_part;
+  float* dv_part;
+  char* dq;
+  char* dk;
+  char* dv;
+};
+
+typedef const __attribute__((address_space(4))) BwdArgs* bargs_ptr;
+__device__ __forceinline__ bargs_ptr bargs() {
+  bargs_ptr p = (bargs_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
+// D and LSE2 of every row: 4 threads per row, 16 dims each.
+template <typename T>
+__global__ void __launch_bounds__(256) bb_bwd_pre_kernel(BwdArgs a, int rows) {
+  static_assert(sizeof(T) == 2, "bf16 rows");
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int row = t >> 2, part = t & 3;
+  float acc = 0.0f;
+  if (row < rows) {
+    const size_t off = static_cast<size_t>(row) * kD * sizeof(T) + part * 16 * sizeof(T);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(a.o + off + 16 * h);
+      const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(a.dout + off + 16 * h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += static_cast<float>(o8[e]) * static_cast<float>(g8[e]);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (row < rows && part == 0) {
+    a.dsum[row] = acc;
+    a.lse2[row] = a.lse[row] * 1.4426950408889634f;
+  }
+}
+
+// 32 rows of stage S's K slot (SLOT 0, K swizzle) or V slot (SLOT 1, V
+// swizzle), permuted as in scores(), times the B operand bop: the 32 x 32
+// product rows x bop-columns.
+template <typename T, int BS, int S, int SLOT>
+__device__ __forceinline__ f32x16 rows_times(const u32x4 (&bop)[Cfg<T, BS>::QC], int rbase, int lane) {
+  using C = Cfg<T, BS>;
+  const int j = lane & 31, g = lane >> 5;
+  const char* sb = SLOT ? Stage<T, BS, S>::v() : Stage<T, BS, S>::k();
+  const int row = rbase + perm_row(j);
+  const int sw = SLOT ? swz_v(row) : swz_k(row);
+  u32x4 a[C::QC];
+#pragma unroll
+  for (int x = 0; x < C::QC; ++x)
+    a[x] = *reinterpret_cast<const u32x4*>(sb + row * C::ROWB + (((2 * x + g) ^ sw) << 4));
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int x = 0; x < C::QC; ++x) acc = mfma_qk(a[x], bop[x], acc, static_cast<T*>(nullptr));
+  return acc;
+}
+
+// The transposed operand of 32 rows [rbase, rbase + 32) of a slot (the
+// forward's load_v, for either slot and its swizzle; both swizzles keep rows
+// r, r+4, r+16 and r+20 on one pattern).
+template <typename T, int BS, int S, int SLOT>
+__device__ __forceinline__ VOp<T> cols_op(int rbase, int lane) {
+  static_assert(sizeof(T) == 2, "bf16 operands");
+  using C = Cfg<T, BS>;
+  const char* sb = SLOT ? Stage<T, BS, S>::v() : Stage<T, BS, S>::k();
+  VOp<T> vo;
+  const int g = lane >> 5, e4 = (lane >> 2) & 3;
+  const int r0 = rbase + 8 * g + e4;
+  const int sw = SLOT ? swz_v(r0) : swz_k(r0);
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh) {
+    const int dstart = dh * 32 + perm_row(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    const int dchunk = dstart >> 3, dbyte = (dstart & 7) * 2;
+    const char* base = sb + r0 * C::ROWB + ((dchunk ^ sw) << 4) + dbyte;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + 16 * mm * C::ROWB));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + (16 * mm + 4) * C::ROWB));
+      vo.a[dh][mm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+  return vo;
+}
+
+// Two bf16 pairs per 4 fp32 values, in the PV operand layout.
+__device__ __forceinline__ void pack_pairs(const float (&x)[16], bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      f32x2 pr = {x[8 * h + e], x[8 * h + e + 1]};
+      const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
+      pb[h][e] = c2[0];
+      pb[h][e + 1] = c2[1];
+    }
+}
+
+// ---- dQ pass ----------------------------------------------------------------
+// Stage layout: V in the K slot (its rows feed dP^T = V dO^T), K in the V
+// slot (its transposed operand feeds dQ^T += K^T dS^T; its rows, read
+// through the V swizzle, feed S^T = K Q^T).
+template <typename T, int BS, int S, bool HAS_PAD>
+__device__ __forceinline__ void step_dq(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC],
+                                        const u32x4 (&dop)[Cfg<T, BS>::QC], float lse2, float dsum, bool last,
+                                        int tile_u, int tile_fill, gchar_ptr vbh, gchar_ptr kbh,
+                                        const uint8_t* pad_b, int wave, int lane, int kbase) {
+  PadWords pw;
+  if constexpr (HAS_PAD) {
+    pw = load_pad(pad_b + static_cast<size_t>(tile_u) * BS, kbase);
+    asm volatile("" ::: "memory");
+  }
+  __builtin_amdgcn_s_waitcnt(7 << 4);
+  ring_barrier();
+  f32x16 s = rows_times<T, BS, S, 1>(qop, kbase, lane);    // S^T = K Q^T
+  const f32x16 dp = rows_times<T, BS, S, 0>(dop, kbase, lane);   // dP^T = V dO^T
+  const VOp<T> kt = cols_op<T, BS, S, 1>(kbase, lane);       // K^T
+  if (!last) issue_tile<T, BS, S ^ 1>(vbh, kbh, tile_fill, wave, lane);
+  float pbias = 0.0f;
+  if constexpr (HAS_PAD) pbias = apply_pad(s, pw, lane);
+  const float off = lse2 - pbias * kScaleLog2;
+  float ds[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], kScaleLog2, -off));
+    ds[v] = p * (dp[v] - dsum);
+  }
+  bf16x8 db[2];
+  pack_pairs(ds, db);
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+      ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt.a[dh][mm], db[mm], ws.o[dh], 0, 0, 0);
+}
+
+// Sum of the two key groups' dQ^T halves (exchanged through stage S), scaled
+// by 1/sqrt(d); a middle unit writes its rows, a global unit its partial.
+template <typename T, int BS, int S, int KEEP>
+__device__ __forceinline__ void finalize_dq_half(WaveState& ws, const Unit& w, int wq, int lane) {
+  using C = Cfg<T, BS>;
+  constexpr int GIVE = KEEP ^ 1;
+  float* mo0 = reinterpret_cast<float*>(Stage<T, BS, S>::k());
+  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, S>::v());
+  float* mo_give = GIVE ? mo1 : mo0;
+  const float* mo_keep = KEEP ? mo1 : mo0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mo_give[(wq * 16 + v) * 64 + lane] = ws.o[GIVE][v];
+  lds_barrier();
+  const int j = lane & 31, g = lane >> 5;
+  float x[2][8];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[h8][e] = ws.o[KEEP][8 * h8 + e] + mo_keep[(wq * 16 + 8 * h8 + e) * 64 + lane];
+  const bargs_ptr b = bargs();
+  if (w.gsel < 0) {
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[h8][e] *= 0.125f;   // 1/sqrt(64)
+    char* dst = b->dq + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * C::ROWB;
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+      store_row8(dst + (KEEP * 32 + 16 * h8 + 8 * g) * C::ES, x[h8], static_cast<T*>(nullptr));
+    return;
+  }
+  float* blk = b->dq_part + w.pbase * kD;
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 v4 = {x[h8][4 * hf], x[h8][4 * hf + 1], x[h8][4 * hf + 2], x[h8][4 * hf + 3]};
+      *reinterpret_cast<f32x4*>(blk + partial_slot(wq, KEEP, 2 * h8 + hf, lane)) = v4;
+    }
+}
+
+template <typename T, int BS, bool HAS_PAD>
+__device__ __forceinline__ void run_dq(int n_units) {
+  using C = Cfg<T, BS>;
+  static_assert(sizeof(T) == 2 && BS == 64, "backward: bf16, block 64");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave % C::WQ, wk = wave / C::WQ;
+  const int kbase = wk * 32;
+  int first, stride, end;
+  {
+    const int G = gridDim.x, x = blockIdx.x;
+    if ((G & 7) == 0) {
+      const int X = x & 7;
+      first = static_cast<int>((static_cast<long long>(n_units) * X) >> 3) + (x >> 3);
+      end = static_cast<int>((static_cast<long long>(n_units) * (X + 1)) >> 3);
+      stride = G >> 3;
+    } else {
+      first = x;
+      end = n_units;
+      stride = G;
+    }
+  }
+  if (first >= end) return;
+  Cursor cur = cursor_at<T, BS, 0>(kargs(), first);
+  for (;;) {
+    const Unit cu = decode_unit<T, BS, 0>(kargs(), cur);
+    const bargs_ptr b = bargs();
+    const size_t row = cu.off / C::ROWB + cu.q0 + wq * 32 + (lane & 31);
+    const float lse2 = b->lse2[row], dsum = b->dsum[row];
+    u32x4 qop[C::QC], dop[C::QC];
+    load_q<T, BS>(b->f.q + cu.off + static_cast<size_t>(cu.q0) * C::ROWB, wq, lane, qop);
+    load_q<T, BS>(b->dout + cu.off + static_cast<size_t>(cu.q0) * C::ROWB, wq, lane, dop);
+    const gchar_ptr vbh = (gchar_ptr)(b->f.v) + cu.off, kbh = (gchar_ptr)(b->f.k) + cu.off;
+    const uint8_t* pad_b = HAS_PAD ? b->f.pad + static_cast<size_t>(cu.b) * b->f.L : nullptr;
+    issue_tile<T, BS, 0>(vbh, kbh, tile_at(cu.tl, 0), wave, lane);
+    WaveState ws;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      ws.o[0][v] = 0.0f;
+      ws.o[1][v] = 0.0f;
+    }
+    ws.m = 0.0f;
+    ws.l = 0.0f;
+    const int ntiles = cu.ntiles;
+    constexpr int TRIP = 12;
+    for (int u = 0; u < ntiles; u += TRIP) {
+      int rem = ntiles - u;
+      asm volatile("" : "+s"(rem));
+      uint32_t tp[(TRIP + 2) / 2];
+#pragma unroll
+      for (int k = 0; k < (TRIP + 2) / 2; ++k) {
+        const uint32_t t0 = 2 * k < rem ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k)) : 0u;
+        const uint32_t t1 = 2 * k + 1 < rem ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k + 1)) : 0u;
+        tp[k] = t0 | (t1 << 16);
+      }
+#define BB_TILE(k) static_cast<int>((tp[(k) >> 1] >> (16 * ((k) & 1))) & 0xffffu)
+#define BB_STEP(k)                                                                                    \
+  if ((k) < rem)                                                                                      \
+    step_dq<T, BS, (k) % 2, HAS_PAD>(ws, qop, dop, lse2, dsum, (k) + 1 == rem, BB_TILE(k),            \
+                                     BB_TILE((k) + 1), vbh, kbh, pad_b, wave, lane, kbase);
+      BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
+      BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
+#undef BB_STEP
+#undef BB_TILE
+    }
+    lds_barrier();   // every wave is past its last LDS read of the unit
+    if ((ntiles - 1) & 1) {
+      if (wk == 0) finalize_dq_half<T, BS, 1, 0>(ws, cu, wq, lane);
+      else finalize_dq_half<T, BS, 1, 1>(ws, cu, wq, lane);
+    } else {
+      if (wk == 0) finalize_dq_half<T, BS, 0, 0>(ws, cu, wq, lane);
+      else finalize_dq_half<T, BS, 0, 1>(ws, cu, wq, lane);
+    }
+    lds_barrier();   // the exchange area is read before the next unit's first tile lands there
+    cur = cursor_advance<T, BS, 0>(kargs(), cur, stride);
+    if (cur.unit >= end) break;
+  }
+}
+
+// ---- dK/dV pass ---------------------------------------------------------------
+// Work units per (b, h): the two global key blocks in n_s query chunks each
+// (partials), then the nb-2 middle key blocks.  Query tiles of a middle key
+// block j: 0, nb-1, the band rows max(1, j-1)..min(nb-2, j+1), then the rows
+// of the inverted random table.  Stage layout: Q in the K slot, dO in the V slot.
+struct KvTiles {
+  int first;             // global key unit: first query tile of its chunk; middle: band start
+  int nwin;              // middle: band rows inside 1..nb-2
+  int nb;
+  int global;
+  const_i32_ptr inv;     // middle: its inverted-table rows
+};
+
+__device__ __forceinline__ int kv_tile_at(const KvTiles& tl, int u) {
+  if (tl.global) return tl.first + u;
+  if (u == 0) return 0;
+  if (u == 1) return tl.nb - 1;
+  if (u < 2 + tl.nwin) return tl.first + u - 2;
+  const int e = tl.inv[u - 2 - tl.nwin];
+  return e < 1 ? 1 : (e > tl.nb - 2 ? tl.nb - 2 : e);   // never read outside the sequence
+}
+
+struct KvUnit {
+  size_t off;            // (b, h) byte offset
+  size_t pbase;          // global key unit: partial row index of its first key row
+  size_t bh;
+  int b, k0, gsel, ntiles;
+  KvTiles tl;
+};
+
+__device__ __forceinline__ KvUnit decode_kv_unit(bargs_ptr a, const Cursor& c) {
+  const int nb = a->f.nb, n_s = a->f.n_s;
+  const int n_g = 2 * n_s;
+  KvUnit w;
+  w.bh = static_cast<size_t>(c.bh);
+  w.off = static_cast<size_t>(c.bh) * a->f.L * (kD * 2);
+  w.b = c.b;
+  w.tl.nb = nb;
+  if (c.u < n_g) {
+    w.gsel = c.u >= n_s ? 1 : 0;
+    const int chunk = c.u - (w.gsel ? n_s : 0);
+    w.k0 = (w.gsel ? nb - 1 : 0) * 64;
+    w.pbase = ((static_cast<size_t>(c.bh) * 2 + w.gsel) * n_s + chunk) * 64;
+    w.tl.global = 1;
+    w.tl.first = chunk * kChunkTiles;
+    w.tl.nwin = 0;
+    w.tl.inv = nullptr;
+    w.ntiles = nb - w.tl.first < kChunkTiles ? nb - w.tl.first : kChunkTiles;
+  } else {
+    w.gsel = -1;
+    const int j = c.u - n_g + 1;
+    w.k0 = j * 64;
+    w.pbase = 0;
+    const int lo = j - 1 < 1 ? 1 : j - 1;
+    const int hi = j + 1 > nb - 2 ? nb - 2 : j + 1;
+    w.tl.global = 0;
+    w.tl.first = lo;
+    w.tl.nwin = hi - lo + 1;
+    const int32_t* offs = a->inv_off + static_cast<size_t>(c.h) * (nb + 1);
+    // offsets clamped into the table, so a corrupted one cannot read outside it
+    const int total = a->f.H * (nb - 2) * a->f.r;
+    const int o0 = offs[j], o1 = offs[j + 1];
+    const int i0 = o0 < 0 ? 0 : (o0 > total ? total : o0);
+    const int i1 = o1 < i0 ? i0 : (o1 > total ? total : o1);
+    w.tl.inv = (const_i32_ptr)(a->inv_rows + i0);
+    w.ntiles = 2 + w.tl.nwin + (i1 - i0);
+  }
+  return w;
+}
+
+struct KvState {
+  f32x16 dk[2];   // dK^T, dims [0,32) and [32,64), 32 keys
+  f32x16 dv[2];   // dV^T
+};
+
+// One query tile: this wave's 32 keys x its 32 queries of the tile.
+template <typename T, int BS, int S>
+__device__ __forceinline__ void step_kv(KvState& st, const u32x4 (&kop)[Cfg<T, BS>::QC],
+                                        const u32x4 (&vop)[Cfg<T, BS>::QC], float kbias_c, bool last,
+                                        int tile_u, int tile_fill, gchar_ptr qbh, gchar_ptr gbh,
+                                        const float* lse2_bh, const float* dsum_bh, int wave, int lane, int wq) {
+  const int qb = wq * 32, g = lane >> 5;
+  __builtin_amdgcn_s_waitcnt(7 << 4);
+  ring_barrier();
+  // LSE2 and D of this lane's 16 accumulator rows: two runs of 8 queries
+  const size_t r0 = static_cast<size_t>(tile_u) * BS + qb + 8 * g;
+  f32x4 l4[4], d4[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      l4[2 * h + x] = *reinterpret_cast<const f32x4*>(lse2_bh + r0 + 16 * h + 4 * x);
+      d4[2 * h + x] = *reinterpret_cast<const f32x4*>(dsum_bh + r0 + 16 * h + 4 * x);
+    }
+  const f32x16 s = rows_times<T, BS, S, 0>(kop, qb, lane);    // S = Q K^T (rows = queries)
+  const f32x16 dp = rows_times<T, BS, S, 1>(vop, qb, lane);   // dP = dO V^T
+  const VOp<T> got = cols_op<T, BS, S, 1>(qb, lane);         // dO^T
+  const VOp<T> qt = cols_op<T, BS, S, 0>(qb, lane);          // Q^T
+  // P and dS before the next tile's DMA is issued: the compiler's own wait
+  // for the LSE2 / D loads then drains nothing but them.
+  float p[16], ds[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float l2 = l4[v >> 2][v & 3], dd = d4[v >> 2][v & 3];
+    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], kScaleLog2, kbias_c - l2));
+    ds[v] = p[v] * (dp[v] - dd);
+  }
+  bf16x8 pb[2], db[2];
+  pack_pairs(p, pb);
+  pack_pairs(ds, db);
+  asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(db[0]), "+v"(db[1]));
+  if (!last) issue_tile<T, BS, S ^ 1>(qbh, gbh, tile_fill, wave, lane);
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) {
+      st.dv[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(got.a[dh][mm], pb[mm], st.dv[dh], 0, 0, 0);
+      st.dk[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt.a[dh][mm], db[mm], st.dk[dh], 0, 0, 0);
+    }
+}
+
+// Sum of the two query groups' dK^T and dV^T (wave wq keeps dims
+// [32 wq, 32 wq + 32)), exchanged through both stages; dK scaled by 1/sqrt(d).
+template <typename T, int BS, int KEEP>
+__device__ __forceinline__ void finalize_kv_half(KvState& st, const KvUnit& w, int wk, int lane) {
+  using C = Cfg<T, BS>;
+  constexpr int GIVE = KEEP ^ 1;
+  float* xv = reinterpret_cast<float*>(Stage<T, BS, 0>::k());   // 16 KB: dV halves
+  float* xk = reinterpret_cast<float*>(Stage<T, BS, 1>::k());   // 16 KB: dK halves
+  const int mine = (wk * 2 + KEEP) * 16, theirs = (wk * 2 + GIVE) * 16;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    xv[(mine + v) * 64 + lane] = st.dv[GIVE][v];
+    xk[(mine + v) * 64 + lane] = st.dk[GIVE][v];
+  }
+  lds_barrier();
+  const int j = lane & 31, g = lane >> 5;
+  float yv[2][8], yk[2][8];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      yv[h8][e] = st.dv[KEEP][8 * h8 + e] + xv[(theirs + 8 * h8 + e) * 64 + lane];
+      yk[h8][e] = (st.dk[KEEP][8 * h8 + e] + xk[(theirs + 8 * h8 + e) * 64 + lane]);
+    }
+  const bargs_ptr b = bargs();
+  if (w.gsel < 0) {
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yk[h8][e] *= 0.125f;   // 1/sqrt(64)
+    const size_t ro = w.off + static_cast<size_t>(w.k0 + wk * 32 + j) * C::ROWB;
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      store_row8(b->dv + ro + (KEEP * 32 + 16 * h8 + 8 * g) * C::ES, yv[h8], static_cast<T*>(nullptr));
+      store_row8(b->dk + ro + (KEEP * 32 + 16 * h8 + 8 * g) * C::ES, yk[h8], static_cast<T*>(nullptr));
+    }
+    return;
+  }
+  float* bv = b->dv_part + w.pbase * kD;
+  float* bk = b->dk_part + w.pbase * kD;
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 v4 = {yv[h8][4 * hf], yv[h8][4 * hf + 1], yv[h8][4 * hf + 2], yv[h8][4 * hf + 3]};
+      const f32x4 k4 = {yk[h8][4 * hf], yk[h8][4 * hf + 1], yk[h8][4 * hf + 2], yk[h8][4 * hf + 3]};
+      *reinterpret_cast<f32x4*>(bv + partial_slot(wk, KEEP, 2 * h8 + hf, lane)) = v4;
+      *reinterpret_cast<f32x4*>(bk + partial_slot(wk, KEEP, 2 * h8 + hf, lane)) = k4;
+    }
+}
+
+template <typename T, int BS, bool HAS_PAD>
+__device__ __forceinline__ void run_dkdv(int n_units) {
+  using C = Cfg<T, BS>;
+  static_assert(sizeof(T) == 2 && BS == 64, "backward: bf16, block 64");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave % C::WQ, wk = wave / C::WQ;
+  int first, stride, end;
+  {
+    const int G = gridDim.x, x = blockIdx.x;
+    if ((G & 7) == 0) {
+      const int X = x & 7;
+      first = static_cast<int>((static_cast<long long>(n_units) * X) >> 3) + (x >> 3);
+      end = static_cast<int>((static_cast<long long>(n_units) * (X + 1)) >> 3);
+      stride = G >> 3;
+    } else {
+      first = x;
+      end = n_units;
+      stride = G;
+    }
+  }
+  if (first >= end) return;
+  Cursor cur = cursor_at<T, BS, 0>(kargs(), first);
+  for (;;) {
+    const bargs_ptr b = bargs();
+    const KvUnit cu = decode_kv_unit(b, cur);
+    // K^T and V^T of this wave's 32 keys as B operands (lane j: key k0 + 32 wk + j)
+    u32x4 kop[C::QC], vop[C::QC];
+    load_q<T, BS>(b->f.k + cu.off + static_cast<size_t>(cu.k0) * C::ROWB, wk, lane, kop);
+    load_q<T, BS>(b->f.v + cu.off + static_cast<size_t>(cu.k0) * C::ROWB, wk, lane, vop);
+    float kbias_c = 0.0f;
+    if constexpr (HAS_PAD) {
+      const uint8_t pv = b->f.pad[static_cast<size_t>(cu.b) * b->f.L + cu.k0 + wk * 32 + (lane & 31)];
+      kbias_c = pv == 0 ? kMaskRaw * kScaleLog2 : 0.0f;
+    }
+    const gchar_ptr qbh = (gchar_ptr)(b->f.q) + cu.off, gbh = (gchar_ptr)(b->dout) + cu.off;
+    const float* lse2_bh = b->lse2 + cu.bh * b->f.L;
+    const float* dsum_bh = b->dsum + cu.bh * b->f.L;
+    issue_tile<T, BS, 0>(qbh, gbh, kv_tile_at(cu.tl, 0), wave, lane);
+    KvState st;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      st.dk[0][v] = 0.0f;
+      st.dk[1][v] = 0.0f;
+      st.dv[0][v] = 0.0f;
+      st.dv[1][v] = 0.0f;
+    }
+    const int ntiles = cu.ntiles;
+    constexpr int TRIP = 12;
+    for (int u = 0; u < ntiles; u += TRIP) {
+      int rem = ntiles - u;
+      asm volatile("" : "+s"(rem));
+      uint32_t tp[(TRIP + 2) / 2];
+#pragma unroll
+      for (int k = 0; k < (TRIP + 2) / 2; ++k) {
+        const uint32_t t0 = 2 * k < rem ? static_cast<uint32_t>(kv_tile_at(cu.tl, u + 2 * k)) : 0u;
+        const uint32_t t1 = 2 * k + 1 < rem ? static_cast<uint32_t>(kv_tile_at(cu.tl, u + 2 * k + 1)) : 0u;
+        tp[k] = t0 | (t1 << 16);
+      }
+#define BB_TILE(k) static_cast<int>((tp[(k) >> 1] >> (16 * ((k) & 1))) & 0xffffu)
+#define BB_STEP(k)                                                                                    \
+  if ((k) < rem)                                                                                      \
+    step_kv<T, BS, (k) % 2>(st, kop, vop, kbias_c, (k) + 1 == rem, BB_TILE(k), BB_TILE((k) + 1), qbh,   \
+                            gbh, lse2_bh, dsum_bh, wave, lane, wq);
+      BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
+      BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
+#undef BB_STEP
+#undef BB_TILE
+    }
+    lds_barrier();   // every wave is past its last LDS read of the unit
+    if (wq == 0) finalize_kv_half<T, BS, 0>(st, cu, wk, lane);
+    else finalize_kv_half<T, BS, 1>(st, cu, wk, lane);
+    lds_barrier();
+    cur = cursor_advance<T, BS, 0>(kargs(), cur, stride);
+    if (cur.unit >= end) break;
+  }
+}
+
+// Sums of the split-K partials: dQ rows of query blocks 0 and nb-1, dK and dV
+// rows of key blocks 0 and nb-1.  Workgroup: 8 rows x 64 dims of one 32-row
+// group of one block of one matrix; thread (q, g, jj) as in the forward's
+// merge; chunks summed in order.
+template <typename T, int BS>
+__global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
+  constexpr int ROWB = kD * sizeof(T);
+  const int rb = blockIdx.x & 3;
+  const int grp = (blockIdx.x >> 2) & 1;
+  const int rest = blockIdx.x >> 3;
+  const int mat = rest % 3, gblk = rest / 3;
+  const int bh = gblk >> 1, gsel = gblk & 1;
+  const int blkid = gsel ? a.f.nb - 1 : 0;
+  const int t = threadIdx.x;
+  const int q = t >> 4, g = (t >> 3) & 1, j = rb * 8 + (t & 7);
+  const int lane = j + 32 * g;
+  const int row = grp * 32 + j;
+  const float* part = mat == 0 ? a.dq_part : (mat == 1 ? a.dk_part : a.dv_part);
+  char* dst = mat == 0 ? a.dq : (mat == 1 ? a.dk : a.dv);
+  const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.f.n_s;
+  f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int s = 0; s < a.f.n_s; ++s) {
+    const float* blk = part + (base + s) * BS * kD;
+    acc[0] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 0, q, lane));
+    acc[1] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 1, q, lane));
+  }
+  const float sc = mat == 2 ? 1.0f : 0.125f;   // dQ and dK carry 1/sqrt(64)
+  char* orow = dst + (static_cast<size_t>(bh) * a.f.L + static_cast<size_t>(blkid) * BS + row) * ROWB;
+#pragma unroll
+  for (int keep = 0; keep < 2; ++keep) {
+    const int d0 = 32 * keep + 16 * (q >> 1) + 8 * g + 4 * (q & 1);
+    store_f32x4(orow + d0 * sizeof(T), acc[keep] * sc, static_cast<T*>(nullptr));
+  }
+}
+
+template <typename T, int BS, bool HAS_PAD>
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(3))) bb_bwd_dq_kernel(BwdArgs, int n_units) {
+  run_dq<T, BS, HAS_PAD>(n_units);
+}
+template <typename T, int BS, bool HAS_PAD>
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(2))) bb_bwd_dkdv_kernel(BwdArgs, int n_units) {
+  run_dkdv<T, BS, HAS_PAD>(n_units);
 }
 
 // ---------------------------------------------------------------- host side --
@@ -1167,10 +1762,12 @@ extern "C" size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block)
   return workspace_layout(B, H, nb, block).total;
 }
 
-extern "C" int bb_attn_forward_timed(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
-                                     const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
-                                     void* out, int dtype, void* workspace, size_t workspace_bytes,
-                                     void* stream, unsigned flags, void* start_event, void* stop_event) {
+namespace {
+
+int forward_impl(const void* q, const void* k, const void* v, const uint8_t* pad_mask, const int32_t* rand_idx,
+                 int B, int H, int L, int d, int block, int r, void* out, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream, unsigned flags, void* start_event, void* stop_event,
+                 float* lse) {
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
   if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE)) return BB_ERR_SHAPE;
   int nb = 0;
@@ -1200,6 +1797,7 @@ extern "C" int bb_attn_forward_timed(const void* q, const void* k, const void* v
   a.pm = reinterpret_cast<float*>(ws + w.pm);
   a.pl = reinterpret_cast<float*>(ws + w.pl);
   a.po = reinterpret_cast<float*>(ws + w.po);
+  a.lse = lse;
   a.H = H;
   a.L = L;
   a.nb = nb;
@@ -1218,6 +1816,26 @@ extern "C" int bb_attn_forward_timed(const void* q, const void* k, const void* v
   return p ? launch<float, 128, true>(a, B, H, s, flags, e0, e1) : launch<float, 128, false>(a, B, H, s, flags, e0, e1);
 }
 
+}  // namespace
+
+extern "C" int bb_attn_forward_timed(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                     const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                                     void* out, int dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream, unsigned flags, void* start_event, void* stop_event) {
+  return forward_impl(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace, workspace_bytes,
+                      stream, flags, start_event, stop_event, nullptr);
+}
+
+extern "C" int bb_attn_forward_lse(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                   const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                                   void* out, int dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream, float* lse) {
+  if (B > 0 && H > 0 && lse == nullptr) return BB_ERR_NULL;
+  if (lse != nullptr && !aligned(lse, 4)) return BB_ERR_ALIGN;
+  return forward_impl(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace, workspace_bytes,
+                      stream, BB_LAUNCH_FUSED, nullptr, nullptr, lse);
+}
+
 extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
                                   const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
                                   void* out, int dtype, void* workspace, size_t workspace_bytes,
@@ -1232,4 +1850,122 @@ extern "C" int bb_attn_forward(const void* q, const void* k, const void* v, cons
                                void* stream) {
   return bb_attn_forward_ex(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace,
                             workspace_bytes, stream, BB_LAUNCH_FUSED);
+}
+
+// ------------------------------------------------------------ backward host --
+
+namespace {
+
+struct BwdLayout {
+  size_t lse2, dsum, dq, dk, dv, total;
+};
+
+BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
+  const size_t rows = static_cast<size_t>(B) * H * L;
+  const size_t n_s = static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
+  const size_t part = static_cast<size_t>(B) * H * 2 * n_s * block * kD * sizeof(float);
+  BwdLayout w;
+  w.lse2 = 0;
+  w.dsum = w.lse2 + align256(rows * sizeof(float));
+  w.dq = w.dsum + align256(rows * sizeof(float));
+  w.dk = w.dq + align256(part);
+  w.dv = w.dk + align256(part);
+  w.total = w.dv + part;
+  return w;
+}
+
+template <bool HAS_PAD>
+int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
+  using T = __bf16;
+  constexpr int BS = 64;
+  using C = Cfg<T, BS>;
+  const long long bhs = static_cast<long long>(B) * H;
+  const long long rows = bhs * a.f.L;
+  const long long n_units = bhs * (2LL * a.f.n_s + a.f.nb - 2);
+  hipLaunchKernelGGL(bb_bwd_pre_kernel<T>, dim3(static_cast<unsigned>((rows * 4 + 255) / 256)), dim3(256), 0,
+                     stream, a, static_cast<int>(rows));
+  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  unsigned grid = 0;
+  int st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dq_kernel<T, BS, HAS_PAD>), C::NT, n_units, &grid);
+  if (st != BB_OK) return st;
+  hipLaunchKernelGGL((bb_bwd_dq_kernel<T, BS, HAS_PAD>), dim3(grid), dim3(C::NT), 0, stream, a,
+                     static_cast<int>(n_units));
+  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dkdv_kernel<T, BS, HAS_PAD>), C::NT, n_units, &grid);
+  if (st != BB_OK) return st;
+  hipLaunchKernelGGL((bb_bwd_dkdv_kernel<T, BS, HAS_PAD>), dim3(grid), dim3(C::NT), 0, stream, a,
+                     static_cast<int>(n_units));
+  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  hipLaunchKernelGGL((bb_bwd_reduce_kernel<T, BS>), dim3(static_cast<unsigned>(bhs) * 2 * 3 * 8), dim3(64), 0,
+                     stream, a);
+  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  return BB_OK;
+}
+
+}  // namespace
+
+extern "C" size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, int block) {
+  int nb = 0;
+  if (check_shape(B, H, L, d, block, 0, &nb) != BB_OK || block != 64) return 0;
+  if (B == 0 || H == 0) return 0;
+  return bwd_layout(B, H, L, nb, block).total;
+}
+
+extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                const int32_t* rand_idx, const int32_t* inv_off, const int32_t* inv_rows,
+                                int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
+  if (dtype != BB_BF16) return BB_ERR_DTYPE;
+  int nb = 0;
+  const int st = check_shape(B, H, L, d, block, r, &nb);
+  if (st != BB_OK) return st;
+  if (block != 64) return BB_ERR_SHAPE;
+  if (B == 0 || H == 0) return BB_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace || !inv_off) return BB_ERR_NULL;
+  if (r > 0 && (!rand_idx || !inv_rows)) return BB_ERR_NULL;
+  const void* a16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return BB_ERR_ALIGN;
+  if ((pad_mask && !aligned(pad_mask, 8)) || !aligned(workspace, 256) || !aligned(lse, 4) ||
+      !aligned(inv_off, 4) || (rand_idx && !aligned(rand_idx, 4)) || (inv_rows && !aligned(inv_rows, 4)))
+    return BB_ERR_ALIGN;
+  const size_t bytes = static_cast<size_t>(B) * H * L * d * 2;
+  const void* ins[] = {q, k, v, out, dout};
+  for (void* g : {dq, dk, dv}) {
+    for (const void* x : ins)
+      if (overlap(g, x, bytes)) return BB_ERR_ALIAS;
+  }
+  if (overlap(dq, dk, bytes) || overlap(dq, dv, bytes) || overlap(dk, dv, bytes)) return BB_ERR_ALIAS;
+  const BwdLayout w = bwd_layout(B, H, L, nb, block);
+  if (workspace_bytes < w.total) return BB_ERR_WORKSPACE;
+
+  BwdArgs a{};
+  a.f.q = static_cast<const char*>(q);
+  a.f.k = static_cast<const char*>(k);
+  a.f.v = static_cast<const char*>(v);
+  a.f.pad = pad_mask;
+  a.f.rand_idx = rand_idx;
+  a.f.H = H;
+  a.f.L = L;
+  a.f.nb = nb;
+  a.f.r = r;
+  a.f.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
+  a.o = static_cast<const char*>(out);
+  a.dout = static_cast<const char*>(dout);
+  a.lse = lse;
+  a.inv_off = inv_off;
+  a.inv_rows = inv_rows;
+  char* ws = static_cast<char*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  a.dsum = reinterpret_cast<float*>(ws + w.dsum);
+  a.dq_part = reinterpret_cast<float*>(ws + w.dq);
+  a.dk_part = reinterpret_cast<float*>(ws + w.dk);
+  a.dv_part = reinterpret_cast<float*>(ws + w.dv);
+  a.dq = static_cast<char*>(dq);
+  a.dk = static_cast<char*>(dk);
+  a.dv = static_cast<char*>(dv);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return pad_mask ? launch_bwd<true>(a, B, H, s) : launch_bwd<false>(a, B, H, s);
 }

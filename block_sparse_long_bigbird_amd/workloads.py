@@ -157,3 +157,13 @@ def small(name: str, B: int, H: int, L: int, block: int, r: int, dtype: str = "b
                     pad_lo_blocks=pad_lo_blocks, pad_hi_blocks=pad_hi_blocks,
                     outlier_frac=outlier_frac, outlier_mult=outlier_mult,
                     data_seed=data_seed, rand_seed=rand_seed)
+
+
+def make_dout(w: Workload):
+    """Upstream gradient for a backward pass: N(0,1) draws of shape [B, H, L, d]
+    from its own stream (PCG64 seeded with data_seed + 1000), rounded to the
+    workload's dtype, as a CPU torch tensor."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(w.data_seed + 1000))
+    g = rng.standard_normal((w.B, w.H, w.L, w.d), dtype=np.float32)
+    return torch.from_numpy(g).to(torch_dtype(w.dtype))

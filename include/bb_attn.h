@@ -155,6 +155,72 @@ int bb_attn_forward_timed(const void* q, const void* k, const void* v, const uin
                           void* out, int dtype, void* workspace, size_t workspace_bytes,
                           void* stream, unsigned flags, void* start_event, void* stop_event);
 
+/*
+ * bb_attn_forward that also writes the row log-sum-exp a backward pass needs.
+ * Source: the softmax of page "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的完整实践",
+ * section "BigBird：从二次方注意力到线性稀疏注意力"; the same page's encoder section
+ * trains the layer with the forward recomputed in the backward pass.
+ *   lse   DEVICE float [B][H][L], 4-byte aligned, caller-allocated: for every
+ *         query row t, log(sum_u exp(s_tu)) (natural log) over its allowed keys,
+ *         s_tu = q.k/sqrt(d) - 10000 [key u padded], the logits of the softmax.
+ *         For bf16 the row sum is that of the bf16-rounded probabilities the
+ *         output is formed from.  Must not be NULL when B*H > 0.
+ * Everything else as bb_attn_forward (the fused launch).
+ */
+int bb_attn_forward_lse(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                        const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                        void* out, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream, float* lse);
+
+/*
+ * Invert a HOST random-block table for the backward pass: for every head h
+ * and key block j, the middle query blocks i (ascending) whose row
+ * rand_idx[h][i-1][:] holds j.
+ *   inv_off   HOST int32 [H][nb+1], caller-allocated: rows of (h, j) are
+ *             inv_rows[inv_off[h][j] .. inv_off[h][j+1]) (absolute offsets).
+ *   inv_rows  HOST int32 [H * (nb-2) * r], caller-allocated (may be NULL when r == 0).
+ * The table is validated first (bb_rand_idx_check's errors).  Copy both
+ * arrays to the device for bb_attn_backward.
+ */
+int bb_rand_idx_invert(const int32_t* rand_idx, int H, int L, int block, int r, int32_t* inv_off,
+                       int32_t* inv_rows);
+
+/* Bytes of device workspace bb_attn_backward needs (0 for empty or
+ * unsupported sizes: the backward supports block 64). */
+size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, int block);
+
+/*
+ * Backward pass of the same attention: the gradients of sum(out * dout)
+ * with respect to q, k and v (the pad offset is a constant).  The gradient
+ * of softmax attention restricted to the block pattern of bb_attn_forward:
+ * P rebuilt from lse, D_t = dout_t . out_t, dS = P (dout V^T - D),
+ * dq = dS K / sqrt(d), dk = dS^T Q / sqrt(d), dv = P^T dout.
+ *   q, k, v, pad_mask, rand_idx, B, H, L, d, block, r
+ *              as passed to the forward that produced out and lse.
+ *   inv_off, inv_rows
+ *              DEVICE copies of bb_rand_idx_invert's output for rand_idx
+ *              (inv_rows may be NULL when r == 0).  Offsets are clamped
+ *              into the table and entries into 1..nb-2, so a wrong table
+ *              cannot read out of bounds (its result is then undefined).
+ *   out, lse   DEVICE forward output [B][H][L][d] and bb_attn_forward_lse's lse.
+ *   dout       DEVICE upstream gradient [B][H][L][d].
+ *   dq, dk, dv DEVICE [B][H][L][d], fully overwritten; must not overlap each
+ *              other or any input.
+ *   dtype      BB_BF16 only (fp32 accumulation, bf16 results rounded to
+ *              nearest even); BB_FP32 returns BB_ERR_DTYPE.
+ *   block      64 only (128: BB_ERR_SHAPE).
+ *   workspace  DEVICE, >= bb_attn_backward_workspace_bytes(), 256-byte aligned,
+ *              no initialisation needed; concurrent calls need distinct ones.
+ * Alignment: q, k, v, out, dout, dq, dk, dv 16 bytes; pad_mask 8; lse,
+ * inv_off, inv_rows, rand_idx 4.  Asynchronous on `stream`, like the forward;
+ * nothing is launched when a check fails.
+ */
+int bb_attn_backward(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                     const int32_t* rand_idx, const int32_t* inv_off, const int32_t* inv_rows,
+                     int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,171 @@
+"""GPU parity of the training entry points, through the C ABI, against the
+fp64 oracle: the forward's row log-sum-exp (bb_attn_forward_lse) and the
+backward pass (bb_attn_backward).
+
+Tolerances:
+  - LSE: 1e-5 (fp32 inputs); 5e-3 (bf16): the row sum is that of bf16-rounded
+    probabilities (relative rounding <= 2^-9 each), so ln(l) moves by at most
+    about 2^-9.
+  - gradients (bf16 only): max |gpu - oracle| <= 2e-2 * max |oracle| per
+    tensor.  Each product term carries bf16 operands (P, dS, dO, Q, K, V,
+    relative rounding 2^-9 each, with fp32 accumulation) and the result is
+    rounded to bf16 (2^-9); D is formed from the bf16 forward output.
+Outputs and the workspace are poisoned (NaN / 0xFF) before every call, and
+every output is scanned for NaN.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_bigbird_amd import binding as bb
+from block_sparse_long_bigbird_amd.workloads import WORKLOADS, make_dout, make_inputs, small
+from oracle import attention_backward, attention_forward, attention_lse
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"fp32": 1e-5, "bf16": 5e-3}
+GRAD_REL = 2e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    bb.lib()
+    return torch.device("cuda:0")
+
+
+def f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def forward_lse(w, dev, inputs, ri):
+    q, k, v, pad = inputs
+    dq_, dk_, dv_ = q.to(dev), k.to(dev), v.to(dev)
+    dpad = None if pad is None else pad.to(dev)
+    dri = torch.from_numpy(ri).to(dev) if w.r > 0 else None
+    out = torch.full_like(dq_, float("nan"))
+    lse = torch.full((w.B, w.H, w.L), float("nan"), dtype=torch.float32, device=dev)
+    n = bb.bb_attn_workspace_bytes(w.B, w.H, w.L, w.d, w.block)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
+    say(f"  forward_lse {w.name} B={w.B} H={w.H} L={w.L} block={w.block} r={w.r} {w.dtype}")
+    bb.bb_attn_forward_lse(dq_, dk_, dv_, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws, lse)
+    torch.cuda.synchronize()
+    return (dq_, dk_, dv_, dpad, dri), out, lse
+
+
+LSE_CASES = [
+    small("lse_nb5", B=2, H=2, L=5 * 64, block=64, r=0, data_seed=41),
+    small("lse_nb12_r3_pad", B=3, H=2, L=12 * 64, block=64, r=3, pad="per_seq_blocks",
+          pad_lo_blocks=4, pad_hi_blocks=12, data_seed=42),
+    small("lse_nb17_r3", B=1, H=2, L=17 * 64, block=64, r=3, data_seed=43),
+    small("lse_bs128_nb11_r4_pad", B=1, H=2, L=11 * 128, block=128, r=4, pad="fixed",
+          valid_len=11 * 128 - 200, data_seed=44),
+    small("lse_fp32_nb9_r3_pad", B=2, H=2, L=9 * 64, block=64, r=3, dtype="fp32", pad="fixed",
+          valid_len=9 * 64 - 70, data_seed=45),
+    small("lse_outliers_unscaled", B=1, H=2, L=16 * 64, block=64, r=3, outlier_frac=0.02,
+          outlier_mult=8.0, data_seed=46),
+]
+
+
+@pytest.mark.parametrize("w", LSE_CASES, ids=[w.name for w in LSE_CASES])
+def test_forward_lse_matches_oracle(dev, w):
+    inputs = make_inputs(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    _, out, lse = forward_lse(w, dev, inputs, ri)
+    q, k, v, pad = inputs
+    pn = None if pad is None else pad.numpy()
+    exp_out = attention_forward(f64(q), f64(k), f64(v), pn, ri, w.block)
+    exp_lse = attention_lse(f64(q), f64(k), pn, ri, w.block)
+    got_out = out.float().cpu().numpy()
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert not np.isnan(got_lse).any() and not np.isnan(got_out).any()
+    e_out, e_lse = np.abs(got_out - exp_out).max(), np.abs(got_lse - exp_lse).max()
+    say(f"  out err {e_out:.3e}  lse err {e_lse:.3e}")
+    assert e_out <= {"fp32": 1e-5, "bf16": 2e-2}[w.dtype]
+    assert e_lse <= LSE_TOL[w.dtype]
+
+
+BWD_CASES = [
+    small("bwd_nb3_dense", B=2, H=2, L=3 * 64, block=64, r=0, data_seed=51),
+    small("bwd_nb5", B=1, H=2, L=5 * 64, block=64, r=0, data_seed=52),
+    small("bwd_nb6_r1", B=1, H=3, L=6 * 64, block=64, r=1, data_seed=53),
+    small("bwd_nb9_r4_two_chunks", B=2, H=2, L=9 * 64, block=64, r=4, data_seed=54),
+    small("bwd_nb17_r3_ragged_chunk", B=1, H=2, L=17 * 64, block=64, r=3, data_seed=55),
+    small("bwd_nb12_r3_pad", B=3, H=2, L=12 * 64, block=64, r=3, pad="per_seq_blocks",
+          pad_lo_blocks=4, pad_hi_blocks=12, data_seed=56),
+    small("bwd_nb10_r2_pad_ragged", B=1, H=2, L=10 * 64, block=64, r=2, pad="fixed",
+          valid_len=10 * 64 - 37, data_seed=57),
+    small("bwd_nb20_r5_scale_small", B=1, H=2, L=20 * 64, block=64, r=5, value_scale=0.125,
+          data_seed=58),
+    small("bwd_nb24_r16_pad_two_trips", B=2, H=2, L=24 * 64, block=64, r=16, pad="per_seq_blocks",
+          pad_lo_blocks=10, pad_hi_blocks=24, data_seed=59),
+    small("bwd_outliers_unscaled", B=1, H=2, L=16 * 64, block=64, r=3, outlier_frac=0.02,
+          outlier_mult=8.0, data_seed=60),
+]
+
+
+def run_backward(w, dev, inputs, ri, dout):
+    (dq_, dk_, dv_, dpad, dri), out, lse = forward_lse(w, dev, inputs, ri)
+    off, rows = bb.bb_rand_idx_invert(ri, w.H, w.L, w.block, w.r)
+    doff = torch.from_numpy(off).to(dev)
+    drows = torch.from_numpy(rows).to(dev) if rows.size else None
+    g = dout.to(dev)
+    gq, gk, gv = (torch.full_like(dq_, float("nan")) for _ in range(3))
+    n = bb.bb_attn_backward_workspace_bytes(w.B, w.H, w.L, w.d, w.block)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
+    say(f"  backward {w.name}")
+    bb.bb_attn_backward(dq_, dk_, dv_, dpad, dri, doff, drows, w.B, w.H, w.L, w.d, w.block, w.r,
+                        out, g, lse, gq, gk, gv, ws)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy() for t in (gq, gk, gv)]
+
+
+def check_grads(got, exp, units=None):
+    worst = 0.0
+    for name, a, b in zip(("dq", "dk", "dv"), got, exp):
+        if units is not None:
+            a = np.stack([a[bb_, h] for bb_, h in units])
+            b = np.stack([b[bb_, h] for bb_, h in units])
+        assert not np.isnan(a).any(), f"unwritten (NaN) {name}"
+        scale = np.abs(b).max()
+        err = np.abs(a - b).max()
+        say(f"  {name}: max err {err:.3e}  max |ref| {scale:.3e}  rel {err / scale:.3e}")
+        assert err <= GRAD_REL * scale, name
+        worst = max(worst, err / scale)
+    return worst
+
+
+@pytest.mark.parametrize("w", BWD_CASES, ids=[w.name for w in BWD_CASES])
+def test_backward_matches_oracle(dev, w):
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    got = run_backward(w, dev, inputs, ri, dout)
+    q, k, v, pad = inputs
+    exp = attention_backward(f64(q), f64(k), f64(v), None if pad is None else pad.numpy(), ri,
+                             w.block, f64(dout))
+    check_grads(got, exp)
+
+
+def test_backward_full_size_sampled_units(dev):
+    """The benchmark shape (4 x 12 x 4096, padded): every output scanned for
+    NaN, three (batch, head) units compared in full with the oracle."""
+    w = WORKLOADS["base_B4_H12_L4096_pad"]
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    got = run_backward(w, dev, inputs, ri, dout)
+    for a in got:
+        assert not np.isnan(a).any()
+    units = [(0, 0), (1, 7), (3, 11)]
+    q, k, v, pad = inputs
+    exp = attention_backward(f64(q), f64(k), f64(v), pad.numpy(), ri, w.block, f64(dout), units=units)
+    check_grads(got, exp, units=units)

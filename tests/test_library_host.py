@@ -205,3 +205,89 @@ def test_workspace_size_formula(lib):
         exp = 2 * a256(units * n_s * block * 4) + units * n_s * block * 64 * 4
         assert lib.bb_attn_workspace_bytes(B, H, L, 64, block) == exp
     assert lib.bb_attn_workspace_bytes(1, 1, 1000, 64, 64) == 0   # unsupported -> 0
+
+
+# ------------------------------------------------------ backward (host side) ---
+
+def numpy_invert(ri, nb):
+    """Inverse of a table written with plain loops: key block -> sorted rows."""
+    H = ri.shape[0]
+    out = {}
+    for h in range(H):
+        for j in range(nb):
+            out[(h, j)] = sorted(i for i in range(1, nb - 1) if j in set(ri[h, i - 1].tolist()))
+    return out
+
+
+@pytest.mark.parametrize("H,nb,r", [(1, 6, 1), (3, 12, 3), (2, 40, 16), (2, 5, 0)])
+def test_rand_idx_invert_matches_loops(lib, H, nb, r):
+    block = 64
+    ri = bb.bb_rand_idx_build(7 + nb, H, nb * block, block, r)
+    off, rows = bb.bb_rand_idx_invert(ri, H, nb * block, block, r)
+    assert off.shape == (H, nb + 1)
+    ref = numpy_invert(ri, nb)
+    for h in range(H):
+        assert off[h, 0] == h * (nb - 2) * r and off[h, nb] == (h + 1) * (nb - 2) * r
+        for j in range(nb):
+            assert rows[off[h, j]:off[h, j + 1]].tolist() == ref[(h, j)]
+    # nothing points at the global blocks
+    assert all((off[:, 1] - off[:, 0]) == 0) and all((off[:, nb] - off[:, nb - 1]) == 0)
+
+
+def test_rand_idx_invert_rejects_bad_table(lib):
+    ri = bb.bb_rand_idx_build(1, 2, 64 * 10, 64, 2)
+    ri[1, 3, 0] = 4       # block 4 is inside row 4's window
+    with pytest.raises(bb.BBError):
+        bb.bb_rand_idx_invert(ri, 2, 64 * 10, 64, 2)
+
+
+def bwd(lib, q=FAKE, k=2 * FAKE, v=3 * FAKE, pad=0, rand=4 * FAKE, inv_off=10 * FAKE, inv_rows=11 * FAKE,
+        B=2, H=3, L=1024, d=64, block=64, r=3, out=5 * FAKE, dout=6 * FAKE, lse=7 * FAKE, dq=12 * FAKE,
+        dk=13 * FAKE, dv=14 * FAKE, dtype=1, ws=15 * FAKE, ws_bytes=1 << 30):
+    P = ctypes.c_void_p
+    return lib.bb_attn_backward(P(q), P(k), P(v), P(pad), P(rand), P(inv_off), P(inv_rows), B, H, L, d,
+                                block, r, P(out), P(dout), P(lse), P(dq), P(dk), P(dv), dtype, P(ws),
+                                ws_bytes, None)
+
+
+def test_backward_validation_errors(lib):
+    assert bwd(lib, dtype=0) == 3                       # fp32: BB_ERR_DTYPE
+    assert bwd(lib, dtype=9) == 3
+    assert bwd(lib, block=128, L=2048) == 2             # block 64 only
+    assert bwd(lib, d=32) == 2
+    assert bwd(lib, r=12) == 2
+    for name in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "ws", "inv_off", "rand", "inv_rows"):
+        assert bwd(lib, **{name: 0}) == 1, name         # BB_ERR_NULL
+    assert bwd(lib, r=0, rand=0, inv_rows=0) != 1       # r == 0 needs no table
+    assert bwd(lib, dq=12 * FAKE + 8) == 8              # BB_ERR_ALIGN
+    assert bwd(lib, lse=7 * FAKE + 2) == 8
+    assert bwd(lib, dq=FAKE) == 7                       # dq == q
+    assert bwd(lib, dk=12 * FAKE) == 7                  # dk == dq
+    assert bwd(lib, dv=6 * FAKE + 4096) == 7            # dv inside dout
+    need = lib.bb_attn_backward_workspace_bytes(2, 3, 1024, 64, 64)
+    assert need > 0
+    assert bwd(lib, ws_bytes=need - 1) == 5
+    assert bwd(lib, B=0, q=0, k=0, v=0, out=0, ws=0) == 0
+    assert lib.bb_attn_backward_workspace_bytes(1, 2, 2048, 64, 128) == 0
+
+
+def test_backward_workspace_size_formula(lib):
+    for B, H, L in [(4, 12, 4096), (1, 8, 16384), (1, 2, 192)]:
+        nb = L // 64
+        n_s = -(-nb // 8)
+        def a256(x):
+            return (x + 255) // 256 * 256
+        rows = B * H * L
+        part = B * H * 2 * n_s * 64 * 64 * 4
+        exp = 2 * a256(rows * 4) + 2 * a256(part) + part
+        assert lib.bb_attn_backward_workspace_bytes(B, H, L, 64, 64) == exp
+
+
+def test_forward_lse_needs_a_buffer(lib):
+    P = ctypes.c_void_p
+    st = lib.bb_attn_forward_lse(P(FAKE), P(2 * FAKE), P(3 * FAKE), None, P(4 * FAKE), 2, 3, 1024, 64, 64,
+                                 3, P(5 * FAKE), 1, P(6 * FAKE), 1 << 30, None, None)
+    assert st == 1
+    st = lib.bb_attn_forward_lse(P(FAKE), P(2 * FAKE), P(3 * FAKE), None, P(4 * FAKE), 2, 3, 1024, 64, 64,
+                                 3, P(5 * FAKE), 1, P(6 * FAKE), 1 << 30, None, P(7 * FAKE + 2))
+    assert st == 8
