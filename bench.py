@@ -2,7 +2,15 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode cold|warm]
                     [--launch fused|split] [--no-cpu-baseline] [--copy-calibration]
+    python bench.py --pass backward [--steps K] [--warmup W] [--workload NAME] [--mode cold|warm]
     python bench.py --pmc-summary FETCH_CSV WRITE_CSV --workload NAME --command "..."
+
+`--pass backward` times bb_attn_backward instead (the default is the forward,
+the headline): one step = one backward call over the whole batch (D and
+LSE2, the dQ pass, the dK/dV pass, the split-K reduce), its inputs (q, k, v,
+out, dout, lse from one forward) resident in HBM.  Useful backward FLOPs are
+10*d per attended pair -- the five products of the recompute-based backward
+(S, dP, dV, dK, dQ); the kernels execute 14*d (S and dP in both passes).
 
 One step = one bb_attn_forward call over the whole batch: key pad bias, tile
 lists, HBM->LDS staging, QK^T, online softmax, PV, the split-K global rows and
@@ -201,6 +209,115 @@ def cpu_baseline(w, inputs, ri, budget_s: float):
     }
 
 
+def cpu_baseline_backward(w, inputs, dout, ri, budget_s: float):
+    """Time the fp64 oracle's backward on (b, h) units until `budget_s` is spent."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_backward
+    q, k, v, pad = inputs
+    qd, kd, vd, gd = (t.double().numpy() for t in (q, k, v, dout))
+    pd = None if pad is None else pad.numpy()
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for bh in units:
+        attention_backward(qd, kd, vd, pd, ri, w.block, gd, units=[bh])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    frac = done / len(units)
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {
+        "value": round(2.5 * useful_flops(w) * frac / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(units)} (batch, head) units of {w.name}, backward of all {w.L} rows "
+                  f"each, fp64 numpy, {el:.1f} s",
+    }
+
+
+def bench_backward(args, w, dev):
+    """One JSON line for bb_attn_backward (see the module docstring)."""
+    import torch
+
+    from block_sparse_long_bigbird_amd import binding as bb
+    from block_sparse_long_bigbird_amd.workloads import make_dout, make_inputs
+
+    if w.dtype != "bf16" or w.block != 64:
+        raise SystemExit("the backward supports bf16 with block 64")
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    off, rows = bb.bb_rand_idx_invert(ri, w.H, w.L, w.block, w.r)
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    q, k, v, pad = inputs
+    dpad = None if pad is None else pad.to(dev)
+    dri = torch.from_numpy(ri).to(dev) if w.r > 0 else None
+    doff = torch.from_numpy(off).to(dev)
+    drows = torch.from_numpy(rows).to(dev) if rows.size else None
+    fws = bb.alloc_workspace(w.B, w.H, w.L, w.d, w.block, dev)
+    dq0, dk0, dv0, dg0 = q.to(dev), k.to(dev), v.to(dev), dout.to(dev)
+    out0 = torch.empty_like(dq0)
+    lse0 = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+    bb.bb_attn_forward_lse(dq0, dk0, dv0, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, out0, fws, lse0)
+    # cold mode: rotate among copies of the inputs (q, k, v, out, dout: 5 x 25 MB on the
+    # headline shape) and outputs so that each call reads HBM
+    footprint = 8 * dq0.numel() * dq0.element_size()
+    n_sets = 1 if args.mode == "warm" else max(2, math.ceil(2.1 * LLC_BYTES / footprint))
+    sets = []
+    for i in range(n_sets):
+        c = (lambda t: t) if i == 0 else (lambda t: t.clone())
+        sets.append((c(dq0), c(dk0), c(dv0), c(out0), c(dg0), c(lse0),
+                     torch.empty_like(dq0), torch.empty_like(dq0), torch.empty_like(dq0)))
+    n = bb.bb_attn_backward_workspace_bytes(w.B, w.H, w.L, w.d, w.block)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        a, b_, c, o, g, l, gq, gk, gv = sets[i % n_sets]
+        bb.bb_attn_backward(a, b_, c, dpad, dri, doff, drows, w.B, w.H, w.L, w.d, w.block, w.r,
+                            o, g, l, gq, gk, gv, ws, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = 2.5 * useful_flops(w)
+    value = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "useful TFLOP/s, BigBird attn bwd L=4096 H=12 d=64 bf16, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) draws shaped like the BigBird-base attention layer)",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "L": w.L, "d": w.d,
+                   "block": w.block, "r": w.r, "pad": w.pad, "mode": args.mode, "input_sets": n_sets,
+                   "useful_gflop_per_step": round(flops / 1e9, 4),
+                   "executed_gflop_per_step": round(3.5 * useful_flops(w) / 1e9, 4)},
+        "roofline": {"bound": "mfma", "kernel": "whole backward call (pre, dq, dkdv, reduce)",
+                     "achieved": round(value, 3), "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_TFLOPS[w.dtype], 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(w, inputs, dout, ri, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +336,7 @@ def main():
                          "(reference point for the HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="", help="profiling command recorded by --pmc-summary")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -241,6 +359,9 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     bb.lib()
+    if args.which == "backward":
+        bench_backward(args, w, dev)
+        return
     launch = bb.BB_LAUNCH_SPLIT if args.launch == "split" else bb.BB_LAUNCH_FUSED
 
     t0 = time.perf_counter()

@@ -1053,11 +1053,12 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
 //   (LSE2 = LSE log2(e), c = log2(e)/sqrt(d)), D_t = sum_d dO[t] O[t],
 //   dS = P (dP - D) with dP = dO V^T,
 //   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO.
-// Three passes over the pattern plus two small kernels:
-//   bb_bwd_pre_kernel    D and LSE2 per row;
-//   bb_bwd_dq_kernel     query-stationary (the forward's work units): per key
-//                        tile S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
-//                        the two global query blocks as split-K chunks;
+// Two passes over the pattern plus a small reduce:
+//   bb_bwd_dq_kernel     query-stationary (the forward's work units): D and
+//                        LSE2 of its rows (stored for the next pass), then per
+//                        key tile S^T = K Q^T, dP^T = V dO^T, dS^T,
+//                        dQ^T += K^T dS^T; the two global query blocks as
+//                        split-K chunks;
 //   bb_bwd_dkdv_kernel   key-stationary: a middle key block j is seen by the
 //                        global query blocks, the band rows {j-1, j, j+1} and
 //                        the middle rows whose random list holds j (the
@@ -1092,31 +1093,6 @@ __device__ __forceinline__ bargs_ptr bargs() {
   bargs_ptr p = (bargs_ptr)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+s"(p));
   return p;
-}
-
-// D and LSE2 of every row: 4 threads per row, 16 dims each.
-template <typename T>
-__global__ void __launch_bounds__(256) bb_bwd_pre_kernel(BwdArgs a, int rows) {
-  static_assert(sizeof(T) == 2, "bf16 rows");
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const int row = t >> 2, part = t & 3;
-  float acc = 0.0f;
-  if (row < rows) {
-    const size_t off = static_cast<size_t>(row) * kD * sizeof(T) + part * 16 * sizeof(T);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(a.o + off + 16 * h);
-      const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(a.dout + off + 16 * h);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc += static_cast<float>(o8[e]) * static_cast<float>(g8[e]);
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  if (row < rows && part == 0) {
-    a.dsum[row] = acc;
-    a.lse2[row] = a.lse[row] * 1.4426950408889634f;
-  }
 }
 
 // 32 rows of stage S's K slot (SLOT 0, K swizzle) or V slot (SLOT 1, V
@@ -1288,10 +1264,28 @@ __device__ __forceinline__ void run_dq(int n_units) {
     const Unit cu = decode_unit<T, BS, 0>(kargs(), cur);
     const bargs_ptr b = bargs();
     const size_t row = cu.off / C::ROWB + cu.q0 + wq * 32 + (lane & 31);
-    const float lse2 = b->lse2[row], dsum = b->dsum[row];
-    u32x4 qop[C::QC], dop[C::QC];
+    u32x4 qop[C::QC], dop[C::QC], oop[C::QC];
     load_q<T, BS>(b->f.q + cu.off + static_cast<size_t>(cu.q0) * C::ROWB, wq, lane, qop);
     load_q<T, BS>(b->dout + cu.off + static_cast<size_t>(cu.q0) * C::ROWB, wq, lane, dop);
+    load_q<T, BS>(b->o + cu.off + static_cast<size_t>(cu.q0) * C::ROWB, wq, lane, oop);
+    // D = dO . O of this lane's row: each lane half holds half of the row's
+    // chunks; the partner half adds the other.  LSE2 = LSE log2(e).  Both are
+    // also stored for the dK/dV pass (by key group 0; global rows once per
+    // split-K chunk, the same values).
+    float dpart = 0.0f;
+#pragma unroll
+    for (int x = 0; x < C::QC; ++x) {
+      const bf16x8 g8 = __builtin_bit_cast(bf16x8, dop[x]), o8 = __builtin_bit_cast(bf16x8, oop[x]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart += static_cast<float>(g8[e]) * static_cast<float>(o8[e]);
+    }
+    const auto dsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart), __float_as_uint(dpart), false, false);
+    const float dsum = __uint_as_float(dsw[0]) + __uint_as_float(dsw[1]);
+    const float lse2 = b->lse[row] * 1.4426950408889634f;
+    if (wk == 0 && lane < 32) {
+      b->dsum[row] = dsum;
+      b->lse2[row] = lse2;
+    }
     const gchar_ptr vbh = (gchar_ptr)(b->f.v) + cu.off, kbh = (gchar_ptr)(b->f.k) + cu.off;
     const uint8_t* pad_b = HAS_PAD ? b->f.pad + static_cast<size_t>(cu.b) * b->f.L : nullptr;
     issue_tile<T, BS, 0>(vbh, kbh, tile_at(cu.tl, 0), wave, lane);
@@ -1882,9 +1876,7 @@ int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
   const long long bhs = static_cast<long long>(B) * H;
   const long long rows = bhs * a.f.L;
   const long long n_units = bhs * (2LL * a.f.n_s + a.f.nb - 2);
-  hipLaunchKernelGGL(bb_bwd_pre_kernel<T>, dim3(static_cast<unsigned>((rows * 4 + 255) / 256)), dim3(256), 0,
-                     stream, a, static_cast<int>(rows));
-  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  (void)rows;
   unsigned grid = 0;
   int st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dq_kernel<T, BS, HAS_PAD>), C::NT, n_units, &grid);
   if (st != BB_OK) return st;
