@@ -51,6 +51,12 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m block_sparse_long_bigbird_amd.build` (hipcc, gfx950)")
+    # torch ships its own HIP runtime under the same soname.  Loaded first, it
+    # is the one the library binds to, so torch's streams and memory and the
+    # library's launches share one runtime; loaded after the library, the
+    # process would map two runtimes and the library's launches on torch's
+    # streams would fail.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     c_int, c_size, c_u64, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64, ctypes.c_void_p
     L.bb_abi_version.restype = c_int
