@@ -1236,10 +1236,46 @@ __device__ __forceinline__ void finalize_dq_half(WaveState& ws, const Unit& w, i
     }
 }
 
+// End of a dQ unit: the key groups' dQ^T summed through stage S -- for four
+// key groups (block 128) first 2,3 -> 0,1 in full, then 0 <-> 1 by head dims.
+template <typename T, int BS, int S>
+__device__ __forceinline__ void finalize_dq(WaveState& ws, const Unit& w, int wq, int wk, int lane) {
+  using C = Cfg<T, BS>;
+  float* mo0 = reinterpret_cast<float*>(Stage<T, BS, S>::k());
+  float* mo1 = reinterpret_cast<float*>(Stage<T, BS, S>::v());
+  lds_barrier();   // every wave is past its last LDS read of the unit
+  if constexpr (C::WK == 4) {
+    if (wk >= 2) {
+      const int slot = (wk - 2) * C::WQ + wq;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        mo0[(slot * 16 + v) * 64 + lane] = ws.o[0][v];
+        mo1[(slot * 16 + v) * 64 + lane] = ws.o[1][v];
+      }
+    }
+    lds_barrier();
+    if (wk < 2) {
+      const int slot = wk * C::WQ + wq;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        ws.o[0][v] += mo0[(slot * 16 + v) * 64 + lane];
+        ws.o[1][v] += mo1[(slot * 16 + v) * 64 + lane];
+      }
+    }
+    lds_barrier();
+  }
+  if (wk == 0)
+    finalize_dq_half<T, BS, S, 0>(ws, w, wq, lane);
+  else if (wk == 1)
+    finalize_dq_half<T, BS, S, 1>(ws, w, wq, lane);
+  else
+    lds_barrier();   // key groups 2 and 3: the last round's barrier
+}
+
 template <typename T, int BS, bool HAS_PAD>
 __device__ __forceinline__ void run_dq(int n_units) {
   using C = Cfg<T, BS>;
-  static_assert(sizeof(T) == 2 && BS == 64, "backward: bf16, block 64");
+  static_assert(sizeof(T) == 2, "backward: bf16");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave % C::WQ, wk = wave / C::WQ;
@@ -1319,14 +1355,10 @@ __device__ __forceinline__ void run_dq(int n_units) {
 #undef BB_STEP
 #undef BB_TILE
     }
-    lds_barrier();   // every wave is past its last LDS read of the unit
-    if ((ntiles - 1) & 1) {
-      if (wk == 0) finalize_dq_half<T, BS, 1, 0>(ws, cu, wq, lane);
-      else finalize_dq_half<T, BS, 1, 1>(ws, cu, wq, lane);
-    } else {
-      if (wk == 0) finalize_dq_half<T, BS, 0, 0>(ws, cu, wq, lane);
-      else finalize_dq_half<T, BS, 0, 1>(ws, cu, wq, lane);
-    }
+    if ((ntiles - 1) & 1)
+      finalize_dq<T, BS, 1>(ws, cu, wq, wk, lane);
+    else
+      finalize_dq<T, BS, 0>(ws, cu, wq, wk, lane);
     lds_barrier();   // the exchange area is read before the next unit's first tile lands there
     cur = cursor_advance<T, BS, 0>(kargs(), cur, stride);
     if (cur.unit >= end) break;
@@ -1363,19 +1395,23 @@ struct KvUnit {
   KvTiles tl;
 };
 
+template <int BS>
 __device__ __forceinline__ KvUnit decode_kv_unit(bargs_ptr a, const Cursor& c) {
+  constexpr int KS = BS / 64;           // 64-key units per key block
+  constexpr int LKS = KS == 2 ? 1 : 0;
   const int nb = a->f.nb, n_s = a->f.n_s;
-  const int n_g = 2 * n_s;
+  const int n_g = 2 * n_s * KS;
   KvUnit w;
   w.bh = static_cast<size_t>(c.bh);
   w.off = static_cast<size_t>(c.bh) * a->f.L * (kD * 2);
   w.b = c.b;
   w.tl.nb = nb;
   if (c.u < n_g) {
-    w.gsel = c.u >= n_s ? 1 : 0;
-    const int chunk = c.u - (w.gsel ? n_s : 0);
-    w.k0 = (w.gsel ? nb - 1 : 0) * 64;
-    w.pbase = ((static_cast<size_t>(c.bh) * 2 + w.gsel) * n_s + chunk) * 64;
+    w.gsel = c.u >= n_s * KS ? 1 : 0;
+    const int rem = c.u - (w.gsel ? n_s * KS : 0);
+    const int chunk = rem >> LKS, kh = rem & (KS - 1);
+    w.k0 = (w.gsel ? nb - 1 : 0) * BS + kh * 64;
+    w.pbase = ((static_cast<size_t>(c.bh) * 2 + w.gsel) * n_s + chunk) * BS + kh * 64;
     w.tl.global = 1;
     w.tl.first = chunk * kChunkTiles;
     w.tl.nwin = 0;
@@ -1383,8 +1419,9 @@ __device__ __forceinline__ KvUnit decode_kv_unit(bargs_ptr a, const Cursor& c) {
     w.ntiles = nb - w.tl.first < kChunkTiles ? nb - w.tl.first : kChunkTiles;
   } else {
     w.gsel = -1;
-    const int j = c.u - n_g + 1;
-    w.k0 = j * 64;
+    const int v = c.u - n_g;
+    const int j = (v >> LKS) + 1, kh = v & (KS - 1);
+    w.k0 = j * BS + kh * 64;
     w.pbase = 0;
     const int lo = j - 1 < 1 ? 1 : j - 1;
     const int hi = j + 1 > nb - 2 ? nb - 2 : j + 1;
@@ -1505,13 +1542,54 @@ __device__ __forceinline__ void finalize_kv_half(KvState& st, const KvUnit& w, i
     }
 }
 
+// End of a dK/dV unit: the query groups' dK^T and dV^T summed -- for four
+// query groups (block 128) first 2,3 -> 0,1 in full (dV through stage 0, dK
+// through stage 1), then 0 <-> 1 by head dims.
+template <typename T, int BS>
+__device__ __forceinline__ void finalize_kv(KvState& st, const KvUnit& w, int wq, int wk, int lane) {
+  lds_barrier();   // every wave is past its last LDS read of the unit
+  if constexpr (BS / 32 == 4) {
+    float* xv = reinterpret_cast<float*>(Stage<T, BS, 0>::k());
+    float* xk = reinterpret_cast<float*>(Stage<T, BS, 1>::k());
+    if (wq >= 2) {
+      const int slot = ((wq - 2) * 2 + wk) * 32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        xv[(slot + v) * 64 + lane] = st.dv[0][v];
+        xv[(slot + 16 + v) * 64 + lane] = st.dv[1][v];
+        xk[(slot + v) * 64 + lane] = st.dk[0][v];
+        xk[(slot + 16 + v) * 64 + lane] = st.dk[1][v];
+      }
+    }
+    lds_barrier();
+    if (wq < 2) {
+      const int slot = (wq * 2 + wk) * 32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        st.dv[0][v] += xv[(slot + v) * 64 + lane];
+        st.dv[1][v] += xv[(slot + 16 + v) * 64 + lane];
+        st.dk[0][v] += xk[(slot + v) * 64 + lane];
+        st.dk[1][v] += xk[(slot + 16 + v) * 64 + lane];
+      }
+    }
+    lds_barrier();
+  }
+  if (wq == 0)
+    finalize_kv_half<T, BS, 0>(st, w, wk, lane);
+  else if (wq == 1)
+    finalize_kv_half<T, BS, 1>(st, w, wk, lane);
+  else
+    lds_barrier();   // query groups 2 and 3: the last round's barrier
+}
+
 template <typename T, int BS, bool HAS_PAD>
 __device__ __forceinline__ void run_dkdv(int n_units) {
   using C = Cfg<T, BS>;
-  static_assert(sizeof(T) == 2 && BS == 64, "backward: bf16, block 64");
+  static_assert(sizeof(T) == 2, "backward: bf16");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wq = wave % C::WQ, wk = wave / C::WQ;
+  // two key groups (32 keys each) of the 64-key unit, BS/32 query groups of each query tile
+  const int wk = wave & 1, wq = wave >> 1;
   int first, stride, end;
   {
     const int G = gridDim.x, x = blockIdx.x;
@@ -1530,7 +1608,7 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
   Cursor cur = cursor_at<T, BS, 0>(kargs(), first);
   for (;;) {
     const bargs_ptr b = bargs();
-    const KvUnit cu = decode_kv_unit(b, cur);
+    const KvUnit cu = decode_kv_unit<BS>(b, cur);
     // K^T and V^T of this wave's 32 keys as B operands (lane j: key k0 + 32 wk + j)
     u32x4 kop[C::QC], vop[C::QC];
     load_q<T, BS>(b->f.k + cu.off + static_cast<size_t>(cu.k0) * C::ROWB, wk, lane, kop);
@@ -1574,9 +1652,7 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
 #undef BB_STEP
 #undef BB_TILE
     }
-    lds_barrier();   // every wave is past its last LDS read of the unit
-    if (wq == 0) finalize_kv_half<T, BS, 0>(st, cu, wk, lane);
-    else finalize_kv_half<T, BS, 1>(st, cu, wk, lane);
+    finalize_kv<T, BS>(st, cu, wq, wk, lane);
     lds_barrier();
     cur = cursor_advance<T, BS, 0>(kargs(), cur, stride);
     if (cur.unit >= end) break;
@@ -1590,22 +1666,25 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
 template <typename T, int BS>
 __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
   constexpr int ROWB = kD * sizeof(T);
+  constexpr int UB = BS / 64;                                 // 64-row blocks per block
   const int rb = blockIdx.x & 3;
   const int grp = (blockIdx.x >> 2) & 1;
-  const int rest = blockIdx.x >> 3;
+  int rest = blockIdx.x >> 3;
+  const int ub = rest % UB;
+  rest /= UB;
   const int mat = rest % 3, gblk = rest / 3;
   const int bh = gblk >> 1, gsel = gblk & 1;
   const int blkid = gsel ? a.f.nb - 1 : 0;
   const int t = threadIdx.x;
   const int q = t >> 4, g = (t >> 3) & 1, j = rb * 8 + (t & 7);
   const int lane = j + 32 * g;
-  const int row = grp * 32 + j;
+  const int row = ub * 64 + grp * 32 + j;
   const float* part = mat == 0 ? a.dq_part : (mat == 1 ? a.dk_part : a.dv_part);
   char* dst = mat == 0 ? a.dq : (mat == 1 ? a.dk : a.dv);
   const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.f.n_s;
   f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
   for (int s = 0; s < a.f.n_s; ++s) {
-    const float* blk = part + (base + s) * BS * kD;
+    const float* blk = part + ((base + s) * BS + ub * 64) * kD;
     acc[0] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 0, q, lane));
     acc[1] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 1, q, lane));
   }
@@ -1868,14 +1947,14 @@ BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
   return w;
 }
 
-template <bool HAS_PAD>
+template <int BS, bool HAS_PAD>
 int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
   using T = __bf16;
-  constexpr int BS = 64;
   using C = Cfg<T, BS>;
   const long long bhs = static_cast<long long>(B) * H;
   const long long rows = bhs * a.f.L;
-  const long long n_units = bhs * (2LL * a.f.n_s + a.f.nb - 2);
+  // 64-row query units (dQ) and 64-key units (dK/dV): the same count
+  const long long n_units = bhs * (2LL * a.f.n_s + a.f.nb - 2) * (BS / 64);
   (void)rows;
   unsigned grid = 0;
   int st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dq_kernel<T, BS, HAS_PAD>), C::NT, n_units, &grid);
@@ -1888,7 +1967,7 @@ int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
   hipLaunchKernelGGL((bb_bwd_dkdv_kernel<T, BS, HAS_PAD>), dim3(grid), dim3(C::NT), 0, stream, a,
                      static_cast<int>(n_units));
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-  hipLaunchKernelGGL((bb_bwd_reduce_kernel<T, BS>), dim3(static_cast<unsigned>(bhs) * 2 * 3 * 8), dim3(64), 0,
+  hipLaunchKernelGGL((bb_bwd_reduce_kernel<T, BS>), dim3(static_cast<unsigned>(bhs) * 2 * 3 * (BS / 64) * 8), dim3(64), 0,
                      stream, a);
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   return BB_OK;
@@ -1898,7 +1977,7 @@ int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
 
 extern "C" size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, int block) {
   int nb = 0;
-  if (check_shape(B, H, L, d, block, 0, &nb) != BB_OK || block != 64) return 0;
+  if (check_shape(B, H, L, d, block, 0, &nb) != BB_OK) return 0;
   if (B == 0 || H == 0) return 0;
   return bwd_layout(B, H, L, nb, block).total;
 }
@@ -1913,7 +1992,6 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   int nb = 0;
   const int st = check_shape(B, H, L, d, block, r, &nb);
   if (st != BB_OK) return st;
-  if (block != 64) return BB_ERR_SHAPE;
   if (B == 0 || H == 0) return BB_OK;
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace || !inv_off) return BB_ERR_NULL;
   if (r > 0 && (!rand_idx || !inv_rows)) return BB_ERR_NULL;
@@ -1959,5 +2037,6 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   a.dk = static_cast<char*>(dk);
   a.dv = static_cast<char*>(dv);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return pad_mask ? launch_bwd<true>(a, B, H, s) : launch_bwd<false>(a, B, H, s);
+  if (block == 64) return pad_mask ? launch_bwd<64, true>(a, B, H, s) : launch_bwd<64, false>(a, B, H, s);
+  return pad_mask ? launch_bwd<128, true>(a, B, H, s) : launch_bwd<128, false>(a, B, H, s);
 }

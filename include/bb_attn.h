@@ -186,7 +186,7 @@ int bb_rand_idx_invert(const int32_t* rand_idx, int H, int L, int block, int r, 
                        int32_t* inv_rows);
 
 /* Bytes of device workspace bb_attn_backward needs (0 for empty or
- * unsupported sizes: the backward supports block 64). */
+ * unsupported sizes). */
 size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, int block);
 
 /*
@@ -208,7 +208,7 @@ size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, int block);
  *              other or any input.
  *   dtype      BB_BF16 only (fp32 accumulation, bf16 results rounded to
  *              nearest even); BB_FP32 returns BB_ERR_DTYPE.
- *   block      64 only (128: BB_ERR_SHAPE).
+ *   block      64 or 128, as the forward.
  *   workspace  DEVICE, >= bb_attn_backward_workspace_bytes(), 256-byte aligned,
  *              no initialisation needed; concurrent calls need distinct ones.
  * Alignment: q, k, v, out, dout, dq, dk, dv 16 bytes; pad_mask 8; lse,

@@ -109,6 +109,11 @@ BWD_CASES = [
           pad_lo_blocks=10, pad_hi_blocks=24, data_seed=59),
     small("bwd_outliers_unscaled", B=1, H=2, L=16 * 64, block=64, r=3, outlier_frac=0.02,
           outlier_mult=8.0, data_seed=60),
+    small("bwd_bs128_nb3", B=1, H=2, L=3 * 128, block=128, r=0, data_seed=61),
+    small("bwd_bs128_nb6_r1", B=2, H=1, L=6 * 128, block=128, r=1, data_seed=62),
+    small("bwd_bs128_nb11_r4_pad", B=1, H=2, L=11 * 128, block=128, r=4, pad="fixed",
+          valid_len=11 * 128 - 200, data_seed=63),
+    small("bwd_bs128_nb22_r16_two_trips", B=1, H=1, L=22 * 128, block=128, r=16, data_seed=64),
 ]
 
 

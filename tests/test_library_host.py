@@ -253,7 +253,7 @@ def bwd(lib, q=FAKE, k=2 * FAKE, v=3 * FAKE, pad=0, rand=4 * FAKE, inv_off=10 * 
 def test_backward_validation_errors(lib):
     assert bwd(lib, dtype=0) == 3                       # fp32: BB_ERR_DTYPE
     assert bwd(lib, dtype=9) == 3
-    assert bwd(lib, block=128, L=2048) == 2             # block 64 only
+    assert bwd(lib, block=32) == 2
     assert bwd(lib, d=32) == 2
     assert bwd(lib, r=12) == 2
     for name in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "ws", "inv_off", "rand", "inv_rows"):
@@ -268,19 +268,21 @@ def test_backward_validation_errors(lib):
     assert need > 0
     assert bwd(lib, ws_bytes=need - 1) == 5
     assert bwd(lib, B=0, q=0, k=0, v=0, out=0, ws=0) == 0
-    assert lib.bb_attn_backward_workspace_bytes(1, 2, 2048, 64, 128) == 0
+    need128 = lib.bb_attn_backward_workspace_bytes(1, 1, 2048, 64, 128)
+    assert need128 > 0
+    assert bwd(lib, B=1, H=1, block=128, L=2048, ws_bytes=need128 - 1) == 5
 
 
 def test_backward_workspace_size_formula(lib):
-    for B, H, L in [(4, 12, 4096), (1, 8, 16384), (1, 2, 192)]:
-        nb = L // 64
+    for B, H, L, block in [(4, 12, 4096, 64), (1, 8, 16384, 64), (1, 2, 192, 64), (1, 12, 32768, 128)]:
+        nb = L // block
         n_s = -(-nb // 8)
         def a256(x):
             return (x + 255) // 256 * 256
         rows = B * H * L
-        part = B * H * 2 * n_s * 64 * 64 * 4
+        part = B * H * 2 * n_s * block * 64 * 4
         exp = 2 * a256(rows * 4) + 2 * a256(part) + part
-        assert lib.bb_attn_backward_workspace_bytes(B, H, L, 64, 64) == exp
+        assert lib.bb_attn_backward_workspace_bytes(B, H, L, 64, block) == exp
 
 
 def test_forward_lse_needs_a_buffer(lib):
