@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "BB_OK", 1: "BB_ERR_NULL", 2: "BB_ERR_SHAPE", 3: "BB_ERR_DTYP
                 7: "BB_ERR_ALIAS", 8: "BB_ERR_ALIGN"}
 
 # Every symbol include/bb_attn.h declares.
-EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_check",
+EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_build_capped",
+           "bb_rand_idx_check",
            "bb_attn_workspace_bytes", "bb_attn_forward", "bb_attn_forward_ex",
            "bb_attn_forward_timed", "bb_attn_forward_lse", "bb_rand_idx_invert",
            "bb_attn_backward_workspace_bytes", "bb_attn_backward")
@@ -65,6 +66,8 @@ def lib():
     L.bb_status_str.argtypes = [c_int]
     L.bb_rand_idx_build.restype = c_int
     L.bb_rand_idx_build.argtypes = [c_u64, c_int, c_int, c_int, c_int, vp]
+    L.bb_rand_idx_build_capped.restype = c_int
+    L.bb_rand_idx_build_capped.argtypes = [c_u64, c_int, c_int, c_int, c_int, c_int, vp]
     L.bb_rand_idx_check.restype = c_int
     L.bb_rand_idx_check.argtypes = [vp, c_int, c_int, c_int, c_int]
     L.bb_attn_workspace_bytes.restype = c_size
@@ -105,6 +108,17 @@ def bb_rand_idx_build(seed: int, H: int, L: int, block: int, r: int) -> np.ndarr
                                  out.ctypes.data if out.size else None)
     if st != BB_OK:
         raise BBError(st, "bb_rand_idx_build")
+    return out
+
+
+def bb_rand_idx_build_capped(seed: int, H: int, L: int, block: int, r: int, last_idx: int) -> np.ndarray:
+    """Host random-block table with the random range capped at token last_idx."""
+    nb = L // block if block > 0 else 0
+    out = np.zeros((max(H, 0), max(nb - 2, 0), max(r, 0)), dtype=np.int32)
+    st = lib().bb_rand_idx_build_capped(ctypes.c_uint64(seed & (2**64 - 1)), H, L, block, r, last_idx,
+                                        out.ctypes.data if out.size else None)
+    if st != BB_OK:
+        raise BBError(st, "bb_rand_idx_build_capped")
     return out
 
 

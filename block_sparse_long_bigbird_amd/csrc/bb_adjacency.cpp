@@ -68,21 +68,22 @@ int check_sizes(int H, int L, int block, int r, int* nb_out) {
   return BB_OK;
 }
 
-}  // namespace
-
-extern "C" int bb_rand_idx_build(uint64_t seed, int H, int L, int block, int r, int32_t* rand_idx) {
-  int nb = 0;
-  const int st = check_sizes(H, L, block, r, &nb);
-  if (st != BB_OK) return st;
-  if (H == 0 || r == 0) return BB_OK;
-  if (rand_idx == nullptr) return BB_ERR_NULL;
+// The table with random candidates limited to blocks j <= jmax (jmax >= nb-2:
+// no limit).  Every row must keep at least r candidates.
+int build_table(uint64_t seed, int H, int nb, int r, int jmax, int32_t* rand_idx) {
   std::vector<int32_t> cand;
   cand.reserve(nb);
+  const int hi = jmax < nb - 2 ? jmax : nb - 2;
+  for (int i = 1; i <= nb - 2; ++i) {
+    int n = 0;
+    for (int j = 1; j <= hi; ++j) n += (j < i - 1 || j > i + 1) ? 1 : 0;
+    if (n < r) return BB_ERR_SHAPE;
+  }
   for (int h = 0; h < H; ++h) {
     SplitMix64 g = head_stream(seed, h);
     for (int i = 1; i <= nb - 2; ++i) {
       cand.clear();
-      for (int j = 1; j <= nb - 2; ++j)
+      for (int j = 1; j <= hi; ++j)
         if (j < i - 1 || j > i + 1) cand.push_back(j);
       const int n = static_cast<int>(cand.size());
       for (int t = 0; t < r; ++t) {  // partial Fisher-Yates: first r of a uniform permutation
@@ -95,6 +96,30 @@ extern "C" int bb_rand_idx_build(uint64_t seed, int H, int L, int block, int r, 
     }
   }
   return BB_OK;
+}
+
+}  // namespace
+
+extern "C" int bb_rand_idx_build(uint64_t seed, int H, int L, int block, int r, int32_t* rand_idx) {
+  int nb = 0;
+  const int st = check_sizes(H, L, block, r, &nb);
+  if (st != BB_OK) return st;
+  if (H == 0 || r == 0) return BB_OK;
+  if (rand_idx == nullptr) return BB_ERR_NULL;
+  return build_table(seed, H, nb, r, nb - 2, rand_idx);
+}
+
+extern "C" int bb_rand_idx_build_capped(uint64_t seed, int H, int L, int block, int r, int last_idx,
+                                        int32_t* rand_idx) {
+  int nb = 0;
+  const int st = check_sizes(H, L, block, r, &nb);
+  if (st != BB_OK) return st;
+  if (last_idx <= 0) return bb_rand_idx_build(seed, H, L, block, r, rand_idx);
+  // a block counts when it lies wholly before token last_idx
+  const int jmax = last_idx / block - 1;
+  if (H == 0 || r == 0) return BB_OK;
+  if (rand_idx == nullptr) return BB_ERR_NULL;
+  return build_table(seed, H, nb, r, jmax, rand_idx);
 }
 
 extern "C" int bb_rand_idx_check(const int32_t* rand_idx, int H, int L, int block, int r) {

@@ -84,6 +84,21 @@ const char* bb_status_str(int status);
 int bb_rand_idx_build(uint64_t seed, int H, int L, int block, int r, int32_t* rand_idx);
 
 /*
+ * bb_rand_idx_build with the random range capped: the page's layer draws its
+ * random blocks only from the first last_idx tokens (page "models 仓库中的 BigBird：
+ * 线性复杂度稀疏注意力与长序列训练的完整实践", section "随机块掩码是如何生成的").
+ * A block counts when it lies wholly before token last_idx: row i takes r
+ * distinct ids from {1 .. min(nb-2, last_idx/block - 1)} \ {i-1, i, i+1}.
+ *   last_idx  cap in tokens; <= 0, or >= (nb-1)*block: no cap (the same bytes
+ *             as bb_rand_idx_build for the same arguments).
+ * Same generator, order and output layout as bb_rand_idx_build.
+ * Errors: as bb_rand_idx_build; BB_ERR_SHAPE also when some row keeps fewer
+ * than r candidates under the cap (nothing is written then).
+ */
+int bb_rand_idx_build_capped(uint64_t seed, int H, int L, int block, int r, int last_idx,
+                             int32_t* rand_idx);
+
+/*
  * Validate a HOST random-block table [H][nb-2][r]: every entry in 1..nb-2,
  * outside {i-1, i, i+1} for its middle block i, no repeat within a row.  Row
  * order is free.  Returns BB_OK, BB_ERR_RAND_IDX, BB_ERR_SHAPE or BB_ERR_NULL.

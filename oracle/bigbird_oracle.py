@@ -68,13 +68,15 @@ def num_blocks(L: int, block: int) -> int:
     return nb
 
 
-def check_rand_idx(rand_idx, H: int, L: int, block: int, r: int) -> None:
+def check_rand_idx(rand_idx, H: int, L: int, block: int, r: int, last_idx: int = 0) -> None:
     """Raise ValueError unless rand_idx is a valid random-block table.
 
     [P2-randmask]: per head, one row per middle block (nb-2 rows), each row
     holding num_rand_blocks distinct block ids drawn from the middle blocks
     1..nb-2 with the row's own window {i-1, i, i+1} removed.  Row i-1 belongs
     to middle block i.  Order inside a row is not a constraint.
+    last_idx > 0: the same page caps the random range at the first last_idx
+    tokens; a block is inside the cap when it ends at or before that token.
     """
     nb = num_blocks(L, block)
     a = np.asarray(rand_idx)
@@ -95,6 +97,8 @@ def check_rand_idx(rand_idx, H: int, L: int, block: int, r: int) -> None:
                     raise ValueError(f"head {h} block {i}: random block {e} inside the window")
                 if e in seen:
                     raise ValueError(f"head {h} block {i}: random block {e} repeated")
+                if last_idx > 0 and (e + 1) * block > last_idx:
+                    raise ValueError(f"head {h} block {i}: random block {e} beyond token {last_idx}")
                 seen.add(e)
 
 

@@ -174,3 +174,26 @@ def test_backward_full_size_sampled_units(dev):
     q, k, v, pad = inputs
     exp = attention_backward(f64(q), f64(k), f64(v), pad.numpy(), ri, w.block, f64(dout), units=units)
     check_grads(got, exp, units=units)
+
+
+def test_capped_random_range_forward_and_backward(dev):
+    """A table whose random blocks all sit in the first 8 blocks (cap at token
+    512): the inverted table then gives those key blocks long query lists
+    (several trips of the dK/dV tile loop)."""
+    w = small("capped_nb24_r3", B=1, H=2, L=24 * 64, block=64, r=3, pad="fixed",
+              valid_len=24 * 64 - 90, data_seed=65)
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build_capped(3, w.H, w.L, w.block, w.r, 8 * 64)
+    assert ri.max() <= 7
+    off, _ = bb.bb_rand_idx_invert(ri, w.H, w.L, w.block, w.r)
+    say(f"  longest inverted list: {int(np.diff(off, axis=1).max())} rows")
+    got = run_backward(w, dev, inputs, ri, dout)
+    q, k, v, pad = inputs
+    exp = attention_backward(f64(q), f64(k), f64(v), pad.numpy(), ri, w.block, f64(dout))
+    check_grads(got, exp)
+    _, out, _ = forward_lse(w, dev, inputs, ri)
+    e = np.abs(out.float().cpu().numpy() - attention_forward(f64(q), f64(k), f64(v), pad.numpy(), ri,
+                                                              w.block)).max()
+    say(f"  forward err {e:.3e}")
+    assert e <= 2e-2

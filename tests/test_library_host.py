@@ -293,3 +293,50 @@ def test_forward_lse_needs_a_buffer(lib):
     st = lib.bb_attn_forward_lse(P(FAKE), P(2 * FAKE), P(3 * FAKE), None, P(4 * FAKE), 2, 3, 1024, 64, 64,
                                  3, P(5 * FAKE), 1, P(6 * FAKE), 1 << 30, None, P(7 * FAKE + 2))
     assert st == 8
+
+
+# ------------------------------------------------ capped random range (host) ---
+
+@pytest.mark.parametrize("nb,block,r,last_idx", [(64, 64, 3, 1024), (40, 64, 2, 640), (16, 1, 3, 9),
+                                                 (256, 64, 3, 4096)])
+def test_capped_builder_respects_cap(lib, nb, block, r, last_idx):
+    t = bb.bb_rand_idx_build_capped(5, 3, nb * block, block, r, last_idx)
+    check_rand_idx(t, 3, nb * block, block, r, last_idx=last_idx)   # the oracle's checker
+    assert bb.bb_rand_idx_check(t, 3, nb * block, block, r) == bb.BB_OK
+    assert (np.diff(t, axis=2) > 0).all()
+    assert t.max() <= last_idx // block - 1
+
+
+def test_capped_builder_without_binding_cap_is_the_plain_builder(lib):
+    a = bb.bb_rand_idx_build(77, 4, 4096, 64, 3)
+    for cap in (0, -5, 63 * 64, 64 * 64, 1 << 20):
+        assert np.array_equal(bb.bb_rand_idx_build_capped(77, 4, 4096, 64, 3, cap), a)
+    assert not np.array_equal(bb.bb_rand_idx_build_capped(77, 4, 4096, 64, 3, 62 * 64), a)
+
+
+def test_capped_builder_rejects_infeasible_cap(lib):
+    # cap at token 6*64: candidates {1..5}; rows 2, 3 and 4 keep two each ({4,5}, {1,5}, {1,2})
+    bb.bb_rand_idx_build_capped(1, 1, 20 * 64, 64, 2, 6 * 64)
+    with pytest.raises(bb.BBError):
+        bb.bb_rand_idx_build_capped(1, 1, 20 * 64, 64, 3, 6 * 64)
+    with pytest.raises(ValueError):
+        check_rand_idx(bb.bb_rand_idx_build(1, 1, 20 * 64, 64, 3), 1, 20 * 64, 64, 3, last_idx=6 * 64)
+
+
+def test_capped_builder_uniform_over_capped_candidates(lib):
+    """Row i picks each of its capped candidates with frequency r/|C(i)| (chi-square)."""
+    nb, r, H, seeds, cap = 20, 2, 4, 2000, 9
+    counts = np.zeros((nb - 2, nb), dtype=np.int64)
+    for s in range(seeds):
+        t = bb.bb_rand_idx_build_capped(s * 104729 + 3, H, nb, 1, r, cap)
+        for h in range(H):
+            for row in range(nb - 2):
+                counts[row, t[h, row]] += 1
+    n = seeds * H
+    for row in range(nb - 2):
+        i = row + 1
+        cand = [j for j in range(1, min(nb - 2, cap - 1) + 1) if j not in (i - 1, i, i + 1)]
+        assert counts[row, [j for j in range(nb) if j not in cand]].sum() == 0
+        obs = counts[row, cand]
+        p = stats.chisquare(obs, np.full(len(cand), n * r / len(cand))).pvalue
+        assert p > 1e-3, (row, obs, p)
