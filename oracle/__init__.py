@@ -13,6 +13,7 @@ from .bigbird_oracle import (  # noqa: F401
     attention_rows,
     block_adjacency,
     check_rand_idx,
+    layer_forward,
     num_blocks,
     token_mask,
 )

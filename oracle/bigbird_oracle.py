@@ -279,3 +279,27 @@ def attention_backward(q, k, v, pad_mask, rand_idx, block: int, dout, units=None
         dk[b, h] = dk_acc
         dv[b, h] = dv_acc
     return dq, dk, dv
+
+
+def layer_forward(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, H: int, block: int) -> np.ndarray:
+    """The attention layer around the block-sparse attention, fp64.
+
+    [P2-pattern] page, the layer's construction: query, key and value come
+    from input projections of the hidden states (key_dim = hidden / heads),
+    and an output projection maps the concatenated heads back to hidden:
+      [q | k | v] = x W_qkv^T + b_qkv      (W_qkv: [3*hidden, hidden], rows q, then k, then v)
+      q, k, v split into H heads of d = hidden / H (head h = columns h*d .. h*d+d-1)
+      o = attention(q, k, v) per head; concatenated back to [B, L, hidden]
+      y = o W_o^T + b_o                     (W_o: [hidden, hidden])
+    x: [B, L, hidden].  Returns fp64 [B, L, hidden].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, L, hid = x.shape
+    d = hid // H
+    proj = x @ np.asarray(w_qkv, np.float64).T + np.asarray(b_qkv, np.float64)
+    def heads(t):                                        # [B, L, hid] -> [B, H, L, d]
+        return t.reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    q, k, v = (heads(proj[..., i * hid:(i + 1) * hid]) for i in range(3))
+    o = attention_forward(q, k, v, pad_mask, rand_idx, block)
+    o = o.transpose(0, 2, 1, 3).reshape(B, L, hid)
+    return o @ np.asarray(w_o, np.float64).T + np.asarray(b_o, np.float64)

@@ -1,0 +1,75 @@
+"""Pins for the oracle's attention layer (projections around the block-sparse
+attention), CPU only:
+  - identity projections with zero bias reduce the layer to the attention of
+    the input split into heads (checked against the oracle's own, already
+    pinned, attention, and per pair for one row);
+  - the projections against torch.nn.functional.linear in float64 on the
+    same weights (independent library code), with the attention between them;
+  - linearity in the output projection: scaling W_o and b_o scales y.
+"""
+
+import numpy as np
+import torch
+
+from oracle import attention_forward, layer_forward
+
+
+def sample_rand_idx(rng, H, nb, r):
+    out = np.zeros((H, nb - 2, r), dtype=np.int32)
+    for h in range(H):
+        for i in range(1, nb - 1):
+            cand = [j for j in range(1, nb - 1) if j not in (i - 1, i, i + 1)]
+            out[h, i - 1] = rng.choice(cand, size=r, replace=False)
+    return out
+
+
+def case(seed, B=2, L=48, hid=12, H=3, block=4, r=2, padded=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, L, hid))
+    w_qkv = rng.standard_normal((3 * hid, hid)) / np.sqrt(hid)
+    b_qkv = rng.standard_normal(3 * hid) * 0.1
+    w_o = rng.standard_normal((hid, hid)) / np.sqrt(hid)
+    b_o = rng.standard_normal(hid) * 0.1
+    ri = sample_rand_idx(rng, H, L // block, r)
+    pad = None
+    if padded:
+        pad = np.ones((B, L), dtype=np.uint8)
+        pad[:, L - 7:] = 0
+    return x, w_qkv, b_qkv, w_o, b_o, pad, ri
+
+
+def test_identity_projections_give_the_attention_of_the_heads():
+    x, _, _, _, _, pad, ri = case(1)
+    B, L, hid = x.shape
+    H, d = 3, 4
+    eye = np.eye(hid)
+    y = layer_forward(x, np.concatenate([eye, eye, eye]), np.zeros(3 * hid), eye, np.zeros(hid),
+                      pad, ri, H, 4)
+    xh = x.reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    att = attention_forward(xh, xh, xh, pad, ri, 4)
+    assert np.abs(y - att.transpose(0, 2, 1, 3).reshape(B, L, hid)).max() <= 1e-12
+    # one output row per pair: head 1 of row 0 (a global row: every key)
+    b, t = 0, 0
+    q = xh[b, 1, t]
+    s = xh[b, 1] @ q / np.sqrt(d) - 10000.0 * (pad[b] == 0)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    assert np.abs(y[b, t, d:2 * d] - p @ xh[b, 1]).max() <= 1e-12
+
+
+def test_projections_match_torch_linear():
+    x, w_qkv, b_qkv, w_o, b_o, pad, ri = case(2)
+    B, L, hid = x.shape
+    H, d = 3, hid // 3
+    t = torch.nn.functional.linear(torch.tensor(x), torch.tensor(w_qkv), torch.tensor(b_qkv)).numpy()
+    qkv = [t[..., i * hid:(i + 1) * hid].reshape(B, L, H, d).transpose(0, 2, 1, 3) for i in range(3)]
+    att = attention_forward(*qkv, pad, ri, 4).transpose(0, 2, 1, 3).reshape(B, L, hid)
+    exp = torch.nn.functional.linear(torch.tensor(att), torch.tensor(w_o), torch.tensor(b_o)).numpy()
+    assert np.abs(layer_forward(x, w_qkv, b_qkv, w_o, b_o, pad, ri, H, 4) - exp).max() <= 1e-12
+
+
+def test_output_projection_is_linear():
+    x, w_qkv, b_qkv, w_o, b_o, pad, ri = case(3, padded=False)
+    y1 = layer_forward(x, w_qkv, b_qkv, w_o, b_o, None, ri, 3, 4)
+    y2 = layer_forward(x, w_qkv, b_qkv, 2.5 * w_o, 2.5 * b_o, None, ri, 3, 4)
+    assert np.abs(y2 - 2.5 * y1).max() <= 1e-12
