@@ -33,7 +33,8 @@ EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_
            "bb_rand_idx_check",
            "bb_attn_workspace_bytes", "bb_attn_forward", "bb_attn_forward_ex",
            "bb_attn_forward_timed", "bb_attn_forward_lse", "bb_rand_idx_invert",
-           "bb_attn_backward_workspace_bytes", "bb_attn_backward")
+           "bb_attn_backward_workspace_bytes", "bb_attn_backward", "bb_layer_workspace_bytes",
+           "bb_layer_forward")
 
 _lib = None
 
@@ -88,6 +89,10 @@ def lib():
     L.bb_attn_backward.restype = c_int
     L.bb_attn_backward.argtypes = ([vp, vp, vp, vp, vp, vp, vp] + [c_int] * 6 +
                                    [vp, vp, vp, vp, vp, vp, c_int, vp, c_size, vp])
+    L.bb_layer_workspace_bytes.restype = c_size
+    L.bb_layer_workspace_bytes.argtypes = [c_int] * 5
+    L.bb_layer_forward.restype = c_int
+    L.bb_layer_forward.argtypes = [vp] * 7 + [c_int] * 6 + [vp, c_int, vp, c_size, vp]
     _lib = L
     return L
 
@@ -266,3 +271,21 @@ def bb_attn_backward(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B: int, H: 
                                 _stream_handle(q, stream))
     if st != BB_OK:
         raise BBError(st, "bb_attn_backward")
+
+
+def bb_layer_workspace_bytes(B: int, L: int, hidden: int, H: int, block: int) -> int:
+    return int(lib().bb_layer_workspace_bytes(B, L, hidden, H, block))
+
+
+def bb_layer_forward(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, B: int, L: int, hidden: int, H: int,
+                     block: int, r: int, y, workspace, stream=None) -> None:
+    """Enqueue the attention layer (projections + block-sparse attention)."""
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("b_qkv", b_qkv), ("w_o", w_o), ("b_o", b_o),
+                    ("pad_mask", pad_mask), ("rand_idx", rand_idx), ("y", y), ("workspace", workspace)):
+        _check_device_tensor(name, t)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().bb_layer_forward(_ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_o), _ptr(b_o), _ptr(pad_mask),
+                                _ptr(rand_idx), B, L, hidden, H, block, r, _ptr(y), _dtype_code(x),
+                                _ptr(workspace), ws_bytes, _stream_handle(x, stream))
+    if st != BB_OK:
+        raise BBError(st, "bb_layer_forward")

@@ -1706,6 +1706,143 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
   run_dkdv<T, BS, HAS_PAD>(n_units);
 }
 
+
+// ================================================================== layer ==
+// Projections of the attention layer (the page's layer construction: input
+// projections of the hidden states to query, key and value, key_dim =
+// hidden / heads, and an output projection of the concatenated heads):
+//   C = A W^T + bias, bf16 operands, fp32 accumulation, bf16 results.
+//   A: MODE 0 the hidden states x [M = B*L][K = hidden];
+//      MODE 1 the attention output in its head-split layout [B][H][L][64]
+//      (k = 64 h + dd: one K step of 64 is one head, 128 contiguous rows).
+//   W: [N][K], the [out][in] layout of a linear layer.
+//   C: MODE 0 q, k and v in the attention's layout [B][H][L][64] (columns
+//      n of [q | k | v], N = 3*hidden); MODE 1 y [M][N].
+// Workgroup tile 128 rows of A x 128 rows of W; K in steps of 64 through a
+// two-stage LDS ring filled by the same DMA as the attention.  4 waves of
+// 64 x 64 (2 x 2 subtiles of 32 x 32), computed transposed (C^T = W A^T):
+// lane = row of A, 16 accumulators = 2 runs of 8 consecutive columns, so
+// the epilogue writes 16-byte runs with the bias added.
+
+struct ProjArgs {
+  const char* a;
+  const char* w;
+  const float* bias;
+  char* out;
+  int M, N, K;
+  int L, H;      // sequence length, heads (head-split layouts)
+  int hidden;
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) bb_proj_kernel(ProjArgs g) {
+  constexpr int MT = 128 * 128;                  // bytes per matrix per stage: 128 rows x 64 bf16
+  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * MT];   // [stage][A, W]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int j = lane & 31, gh = lane >> 5;
+  const int tiles_n = g.N / 128;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * 128, n0 = tn * 128;
+  const int nk = g.K / 64;
+  // A rows of this tile: MODE 1 reads head ks of batch b, rows l0 .. l0+127
+  const int b0 = m0 / g.L, l0 = m0 - b0 * g.L;
+  const size_t a_row = MODE == 0 ? static_cast<size_t>(g.K) * 2 : 128;
+  // per-lane DMA offsets (4 instructions per wave per matrix) and LDS slots
+  uint32_t ao[4], wo[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int ins = wave + 4 * jj;
+    const int slot = ins * 64 + lane;
+    const int row = slot >> 3, p = slot & 7;
+    ao[jj] = static_cast<uint32_t>(row * a_row + ((p ^ (row & 7)) << 4));
+    wo[jj] = static_cast<uint32_t>(static_cast<size_t>(row) * g.K * 2 + ((p ^ swz_k(row)) << 4));
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int ks, int st) {
+    const gchar_ptr ab = MODE == 0
+        ? (gchar_ptr)(g.a) + static_cast<size_t>(m0) * g.K * 2 + static_cast<size_t>(ks) * 128
+        : (gchar_ptr)(g.a) + ((static_cast<size_t>(b0) * g.H + ks) * g.L + l0) * 128;
+    const gchar_ptr wb = (gchar_ptr)(g.w) + static_cast<size_t>(n0) * g.K * 2 + static_cast<size_t>(ks) * 128;
+    const uint32_t la = lds0 + st * 2 * MT, lw = la + MT;
+#pragma unroll
+    for (int jj = 0; jj < 4; jj += 2) {
+      const int i0 = wave + 4 * jj, i1 = wave + 4 * (jj + 1);
+      dma16x4(ab, wb, ao[jj], wo[jj], ao[jj + 1], wo[jj + 1], __builtin_amdgcn_readfirstlane(la + i0 * 1024),
+              __builtin_amdgcn_readfirstlane(lw + i0 * 1024), __builtin_amdgcn_readfirstlane(la + i1 * 1024),
+              __builtin_amdgcn_readfirstlane(lw + i1 * 1024));
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+  issue(0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    const int st = ks & 1;
+    __builtin_amdgcn_s_waitcnt(7 << 4);
+    ring_barrier();
+    if (ks + 1 < nk) issue(ks + 1, st ^ 1);
+    const char* la = lds + st * 2 * MT;
+    const char* lw = la + MT;
+    u32x4 bop[2][4];
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+      const int row = wm * 64 + ms * 32 + j;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        bop[ms][x] = *reinterpret_cast<const u32x4*>(la + row * 128 + (((2 * x + gh) ^ (row & 7)) << 4));
+    }
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+      const int row = wn * 64 + ns * 32 + perm_row(j);
+      u32x4 aop[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        aop[x] = *reinterpret_cast<const u32x4*>(lw + row * 128 + (((2 * x + gh) ^ swz_k(row)) << 4));
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+          acc[ns][ms] = mfma_qk(aop[x], bop[ms][x], acc[ns][ms], static_cast<__bf16*>(nullptr));
+    }
+  }
+  // epilogue: lane (j, gh) holds C[m][n] for m = its row, n in two runs of 8
+#pragma unroll
+  for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+      const int m = m0 + wm * 64 + ms * 32 + j;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + wn * 64 + ns * 32 + 16 * h + 8 * gh;
+        const f32x4 b0v = *reinterpret_cast<const f32x4*>(g.bias + n);
+        const f32x4 b1v = *reinterpret_cast<const f32x4*>(g.bias + n + 4);
+        float x8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x8[e] = acc[ns][ms][8 * h + e] + b0v[e];
+          x8[4 + e] = acc[ns][ms][8 * h + 4 + e] + b1v[e];
+        }
+        char* dst;
+        if (MODE == 0) {
+          const int which = n / g.hidden, nn = n - which * g.hidden;
+          const int hh = nn >> 6, dd = nn & 63;
+          const int bb = m / g.L, l = m - bb * g.L;
+          dst = g.out + static_cast<size_t>(which) * g.M * g.hidden * 2 +
+                ((static_cast<size_t>(bb) * g.H + hh) * g.L + l) * 128 + dd * 2;
+        } else {
+          dst = g.out + (static_cast<size_t>(m) * g.N + n) * 2;
+        }
+        store_row8(dst, x8, static_cast<__bf16*>(nullptr));
+      }
+    }
+}
+
 // ---------------------------------------------------------------- host side --
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -2039,4 +2176,90 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (block == 64) return pad_mask ? launch_bwd<64, true>(a, B, H, s) : launch_bwd<64, false>(a, B, H, s);
   return pad_mask ? launch_bwd<128, true>(a, B, H, s) : launch_bwd<128, false>(a, B, H, s);
+}
+
+// --------------------------------------------------------------- layer host --
+
+namespace {
+
+struct LayerLayout {
+  size_t q, k, v, o, attn, total;
+};
+
+LayerLayout layer_layout(int B, int L, int hidden, int H, int block) {
+  const size_t plane = static_cast<size_t>(B) * L * hidden * 2;
+  LayerLayout w;
+  w.q = 0;
+  w.k = w.q + align256(plane);
+  w.v = w.k + align256(plane);
+  w.o = w.v + align256(plane);
+  w.attn = w.o + align256(plane);
+  w.total = w.attn + bb_attn_workspace_bytes(B, H, L, kD, block);
+  return w;
+}
+
+int check_layer(int B, int L, int hidden, int H, int block, int r) {
+  if (B < 0 || L <= 0 || H <= 0 || hidden <= 0) return BB_ERR_SHAPE;
+  if (hidden != H * kD || hidden % 128 != 0 || L % 128 != 0) return BB_ERR_SHAPE;
+  int nb = 0;
+  return check_shape(B, H, L, kD, block, r, &nb);
+}
+
+}  // namespace
+
+extern "C" size_t bb_layer_workspace_bytes(int B, int L, int hidden, int H, int block) {
+  if (check_layer(B, L, hidden, H, block, 0) != BB_OK || B == 0) return 0;
+  return layer_layout(B, L, hidden, H, block).total;
+}
+
+extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b_qkv, const void* w_o,
+                                const float* b_o, const uint8_t* pad_mask, const int32_t* rand_idx, int B, int L,
+                                int hidden, int H, int block, int r, void* y, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
+  if (dtype != BB_BF16) return BB_ERR_DTYPE;
+  const int st = check_layer(B, L, hidden, H, block, r);
+  if (st != BB_OK) return st;
+  if (B == 0) return BB_OK;
+  if (!x || !w_qkv || !b_qkv || !w_o || !b_o || !y || !workspace) return BB_ERR_NULL;
+  if (r > 0 && !rand_idx) return BB_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(y, 16) || !aligned(b_qkv, 16) ||
+      !aligned(b_o, 16) || !aligned(workspace, 256) || (pad_mask && !aligned(pad_mask, 8)) ||
+      (rand_idx && !aligned(rand_idx, 4)))
+    return BB_ERR_ALIGN;
+  const size_t xbytes = static_cast<size_t>(B) * L * hidden * 2;
+  if (overlap(y, x, xbytes)) return BB_ERR_ALIAS;
+  const LayerLayout w = layer_layout(B, L, hidden, H, block);
+  if (workspace_bytes < w.total) return BB_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = B * L;
+  ProjArgs pa{};
+  pa.a = static_cast<const char*>(x);
+  pa.w = static_cast<const char*>(w_qkv);
+  pa.bias = b_qkv;
+  pa.out = ws + w.q;   // q, k, v planes follow each other (each B*L*hidden*2 bytes, 256-aligned)
+  pa.M = M;
+  pa.N = 3 * hidden;
+  pa.K = hidden;
+  pa.L = L;
+  pa.H = H;
+  pa.hidden = hidden;
+  hipLaunchKernelGGL((bb_proj_kernel<0>), dim3(static_cast<unsigned>((M / 128) * (3 * hidden / 128))), dim3(256), 0,
+                     s, pa);
+  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  const int fst = forward_impl(ws + w.q, ws + w.k, ws + w.v, pad_mask, rand_idx, B, H, L, kD, block, r, ws + w.o,
+                               BB_BF16, ws + w.attn, workspace_bytes - w.attn, stream, BB_LAUNCH_FUSED, nullptr,
+                               nullptr, nullptr);
+  if (fst != BB_OK) return fst;
+  ProjArgs po = pa;
+  po.a = ws + w.o;
+  po.w = static_cast<const char*>(w_o);
+  po.bias = b_o;
+  po.out = static_cast<char*>(y);
+  po.N = hidden;
+  hipLaunchKernelGGL((bb_proj_kernel<1>), dim3(static_cast<unsigned>((M / 128) * (hidden / 128))), dim3(256), 0, s,
+                     po);
+  if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  return BB_OK;
 }

@@ -167,3 +167,25 @@ def make_dout(w: Workload):
     rng = np.random.Generator(np.random.PCG64(w.data_seed + 1000))
     g = rng.standard_normal((w.B, w.H, w.L, w.d), dtype=np.float32)
     return torch.from_numpy(g).to(torch_dtype(w.dtype))
+
+
+def make_layer_inputs(w: Workload):
+    """Hidden states and synthetic projection weights for the attention layer of
+    a workload's shape (hidden = H * d), as CPU torch tensors from their own
+    stream (PCG64 seeded with data_seed + 2000): x ~ N(0, 1) [B, L, hidden] and
+    the weights ~ N(0, 1/hidden) [out, in], both rounded to bf16; biases
+    ~ N(0, 0.02^2) in float32; plus the workload's pad mask (or None)."""
+    import torch
+    hid = w.H * w.d
+    rng = np.random.Generator(np.random.PCG64(w.data_seed + 2000))
+    x = rng.standard_normal((w.B, w.L, hid), dtype=np.float32)
+    s = np.float32(1.0 / np.sqrt(hid))
+    w_qkv = rng.standard_normal((3 * hid, hid), dtype=np.float32) * s
+    b_qkv = rng.standard_normal(3 * hid, dtype=np.float32) * np.float32(0.02)
+    w_o = rng.standard_normal((hid, hid), dtype=np.float32) * s
+    b_o = rng.standard_normal(hid, dtype=np.float32) * np.float32(0.02)
+    _, _, _, pad = draw(w)
+    bf = torch.bfloat16
+    return (torch.from_numpy(x).to(bf), torch.from_numpy(w_qkv).to(bf), torch.from_numpy(b_qkv),
+            torch.from_numpy(w_o).to(bf), torch.from_numpy(b_o),
+            None if pad is None else torch.from_numpy(pad))

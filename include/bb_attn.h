@@ -236,6 +236,36 @@ int bb_attn_backward(const void* q, const void* k, const void* v, const uint8_t*
                      const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * The attention layer around the op: input projections of the hidden states
+ * to query, key and value (key_dim = hidden / heads), the block-sparse
+ * attention of bb_attn_forward, and the output projection of the
+ * concatenated heads.  Source: page "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的
+ * 完整实践", the layer's construction (projections of width hidden / heads per
+ * head) and section "BigBird：从二次方注意力到线性稀疏注意力" (the attention).
+ *   [q | k | v] = x w_qkv^T + b_qkv, split into H heads of 64;
+ *   o = attention(q, k, v) (bb_attn_forward's definition, the same pad_mask and
+ *   rand_idx); y = concat_heads(o) w_o^T + b_o.
+ *   x          DEVICE bf16 [B][L][hidden], 16-byte aligned.
+ *   w_qkv      DEVICE bf16 [3*hidden][hidden] (rows: q outputs, then k, then v;
+ *              the [out][in] layout of a linear layer), 16-byte aligned.
+ *   b_qkv      DEVICE float [3*hidden], 16-byte aligned.
+ *   w_o, b_o   DEVICE bf16 [hidden][hidden], float [hidden], 16-byte aligned.
+ *   pad_mask, rand_idx, block, r
+ *              as bb_attn_forward.
+ *   hidden     H * 64, a multiple of 128; L a multiple of 128 and of block.
+ *   y          DEVICE bf16 [B][L][hidden], fully overwritten, must not overlap x.
+ *   dtype      BB_BF16 only (fp32 accumulation; q, k, v and the attention output
+ *              are stored as bf16 between the steps).
+ *   workspace  DEVICE, >= bb_layer_workspace_bytes(), 256-byte aligned.
+ * Asynchronous on `stream`; checks as bb_attn_forward, nothing launched on error.
+ */
+size_t bb_layer_workspace_bytes(int B, int L, int hidden, int H, int block);
+int bb_layer_forward(const void* x, const void* w_qkv, const float* b_qkv, const void* w_o, const float* b_o,
+                     const uint8_t* pad_mask, const int32_t* rand_idx, int B, int L, int hidden, int H,
+                     int block, int r, void* y, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

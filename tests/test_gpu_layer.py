@@ -1,0 +1,88 @@
+"""GPU parity of the attention layer (bb_layer_forward) against the fp64
+oracle's layer_forward.
+
+Tolerance: max |gpu - oracle| <= 2e-2 * max |oracle| per case.  The layer
+keeps q, k, v and the attention output in bf16 between its steps (relative
+rounding 2^-9 each, fp32 accumulation inside every product) and rounds y to
+bf16.  The output is NaN-poisoned first and scanned.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_bigbird_amd import binding as bb
+from block_sparse_long_bigbird_amd.workloads import WORKLOADS, make_layer_inputs, small
+from oracle import layer_forward
+
+pytestmark = pytest.mark.gpu
+REL = 2e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    bb.lib()
+    return torch.device("cuda:0")
+
+
+def run_layer(w, dev, inputs, ri):
+    x, w_qkv, b_qkv, w_o, b_o, pad = inputs
+    hid = w.H * w.d
+    y = torch.full((w.B, w.L, hid), float("nan"), dtype=torch.bfloat16, device=dev)
+    n = bb.bb_layer_workspace_bytes(w.B, w.L, hid, w.H, w.block)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
+    say(f"  layer {w.name} B={w.B} L={w.L} hidden={hid} H={w.H} block={w.block} r={w.r}")
+    bb.bb_layer_forward(x.to(dev), w_qkv.to(dev), b_qkv.to(dev), w_o.to(dev), b_o.to(dev),
+                        None if pad is None else pad.to(dev),
+                        torch.from_numpy(ri).to(dev) if w.r > 0 else None,
+                        w.B, w.L, hid, w.H, w.block, w.r, y, ws)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+def f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def check(w, dev):
+    inputs = make_layer_inputs(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    got = run_layer(w, dev, inputs, ri)
+    x, w_qkv, b_qkv, w_o, b_o, pad = inputs
+    exp = layer_forward(f64(x), f64(w_qkv), b_qkv.numpy().astype(np.float64), f64(w_o),
+                        b_o.numpy().astype(np.float64), None if pad is None else pad.numpy(), ri, w.H,
+                        w.block)
+    assert not np.isnan(got).any(), "unwritten (NaN) outputs"
+    err, scale = np.abs(got - exp).max(), np.abs(exp).max()
+    say(f"  max err {err:.3e}  max |ref| {scale:.3e}  rel {err / scale:.3e}")
+    assert err <= REL * scale
+
+
+LAYER_CASES = [
+    small("layer_h128_nb4", B=1, H=2, L=4 * 64, block=64, r=0, data_seed=71),
+    small("layer_h256_nb8_r3_pad", B=2, H=4, L=8 * 64, block=64, r=3, pad="fixed",
+          valid_len=8 * 64 - 77, data_seed=72),
+    small("layer_h128_bs128_nb6_r1", B=1, H=2, L=6 * 128, block=128, r=1, data_seed=73),
+    small("layer_h768_nb10_r3", B=1, H=12, L=10 * 64 + 128, block=64, r=3, data_seed=74),
+]
+
+
+@pytest.mark.parametrize("w", LAYER_CASES, ids=[w.name for w in LAYER_CASES])
+def test_layer_matches_oracle(dev, w):
+    check(w, dev)
+
+
+def test_layer_full_size_one_sequence(dev):
+    """BigBird-base shape (hidden 768, 12 heads, L 4096, padded) for one sequence."""
+    base = WORKLOADS["base_B4_H12_L4096_pad"]
+    w = small("layer_base_B1", B=1, H=base.H, L=base.L, block=base.block, r=base.r,
+              pad="fixed", valid_len=base.L - 1000, value_scale=base.value_scale, data_seed=75)
+    check(w, dev)

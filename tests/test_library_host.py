@@ -340,3 +340,30 @@ def test_capped_builder_uniform_over_capped_candidates(lib):
         obs = counts[row, cand]
         p = stats.chisquare(obs, np.full(len(cand), n * r / len(cand))).pvalue
         assert p > 1e-3, (row, obs, p)
+
+
+
+# ------------------------------------------------------ the layer (host side) ---
+
+def layer(lib, x=FAKE, wqkv=2 * FAKE, bqkv=3 * FAKE, wo=4 * FAKE, bo=5 * FAKE, pad=0, rand=6 * FAKE, B=1, L=512,
+          hidden=256, H=4, block=64, r=3, y=7 * FAKE, dtype=1, ws=8 * FAKE, ws_bytes=1 << 30):
+    P = ctypes.c_void_p
+    return lib.bb_layer_forward(P(x), P(wqkv), P(bqkv), P(wo), P(bo), P(pad), P(rand), B, L, hidden, H, block, r,
+                                P(y), dtype, P(ws), ws_bytes, None)
+
+
+def test_layer_validation_errors(lib):
+    assert layer(lib, dtype=0) == 3
+    assert layer(lib, hidden=192, H=3) == 2            # hidden not a multiple of 128
+    assert layer(lib, hidden=256, H=2) == 2            # head dim 128
+    assert layer(lib, L=576) == 2                      # L not a multiple of 128
+    assert layer(lib, r=7) == 2                        # r > nb-5
+    for name in ("x", "wqkv", "bqkv", "wo", "bo", "y", "ws", "rand"):
+        assert layer(lib, **{name: 0}) == 1, name
+    assert layer(lib, bqkv=3 * FAKE + 4) == 8
+    assert layer(lib, y=FAKE) == 7
+    need = lib.bb_layer_workspace_bytes(1, 512, 256, 4, 64)
+    plane = 512 * 256 * 2
+    assert need == 4 * plane + lib.bb_attn_workspace_bytes(1, 4, 512, 64, 64)
+    assert layer(lib, ws_bytes=need - 1) == 5
+    assert layer(lib, B=0, x=0, y=0, ws=0) == 0
