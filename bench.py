@@ -5,6 +5,10 @@
     python bench.py --pass backward [--steps K] [--warmup W] [--workload NAME] [--mode cold|warm]
     python bench.py --pmc-summary FETCH_CSV WRITE_CSV --workload NAME --command "..."
 
+`--pass layer` times bb_layer_forward: the QKV projection, the attention and
+the output projection of the layer (hidden = H*64, synthetic weights); its
+useful FLOPs add 2*M*N*K per projection (M = B*L) to the attention's.
+
 `--pass backward` times bb_attn_backward instead (the default is the forward,
 the headline): one step = one backward call over the whole batch (D and
 LSE2, the dQ pass, the dK/dV pass, the split-K reduce), its inputs (q, k, v,
@@ -238,6 +242,72 @@ def cpu_baseline_backward(w, inputs, dout, ri, budget_s: float):
     }
 
 
+def bench_layer(args, w, dev):
+    """One JSON line for bb_layer_forward (see the module docstring)."""
+    import torch
+
+    from block_sparse_long_bigbird_amd import binding as bb
+    from block_sparse_long_bigbird_amd.workloads import make_layer_inputs
+
+    hid = w.H * w.d
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    x, w_qkv, b_qkv, w_o, b_o, pad = make_layer_inputs(w)
+    dpad = None if pad is None else pad.to(dev)
+    dri = torch.from_numpy(ri).to(dev) if w.r > 0 else None
+    weights = [t.to(dev) for t in (w_qkv, b_qkv, w_o, b_o)]
+    x0 = x.to(dev)
+    footprint = 2 * x0.numel() * x0.element_size()
+    n_sets = 1 if args.mode == "warm" else max(2, math.ceil(2.1 * LLC_BYTES / footprint))
+    sets = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0)) for i in range(n_sets)]
+    n = bb.bb_layer_workspace_bytes(w.B, w.L, hid, w.H, w.block)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        xi, yi = sets[i % n_sets]
+        bb.bb_layer_forward(xi, *weights, dpad, dri, w.B, w.L, hid, w.H, w.block, w.r, yi, ws,
+                            stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    M = w.B * w.L
+    proj = 2 * M * (3 * hid) * hid + 2 * M * hid * hid
+    flops = useful_flops(w) + proj
+    value = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "useful TFLOP/s, BigBird attention layer fwd (projections + attn) L=4096 hidden=768 bf16, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "tokens_per_s": round(w.tokens / (ms * 1e-3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,1/hidden) weights)",
+        "config": {"workload": w.name, "pass": "layer", "B": w.B, "L": w.L, "hidden": hid, "H": w.H,
+                   "block": w.block, "r": w.r, "pad": w.pad, "mode": args.mode, "input_sets": n_sets,
+                   "useful_gflop_per_step": round(flops / 1e9, 4),
+                   "projection_gflop_per_step": round(proj / 1e9, 4)},
+        "roofline": {"bound": "mfma", "kernel": "whole layer call (2 projections + attention)",
+                     "achieved": round(value, 3), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_TFLOPS["bf16"], 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_backward(args, w, dev):
     """One JSON line for bb_attn_backward (see the module docstring)."""
     import torch
@@ -336,7 +406,7 @@ def main():
                          "(reference point for the HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="", help="profiling command recorded by --pmc-summary")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "layer"], default="forward")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -361,6 +431,9 @@ def main():
     bb.lib()
     if args.which == "backward":
         bench_backward(args, w, dev)
+        return
+    if args.which == "layer":
+        bench_layer(args, w, dev)
         return
     launch = bb.BB_LAUNCH_SPLIT if args.launch == "split" else bb.BB_LAUNCH_FUSED
 
