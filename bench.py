@@ -84,9 +84,18 @@ def algorithmic_bytes(w):
     return b
 
 
+# The forward kernels and every device helper they use come first in the
+# source; the backward and layer sections follow this marker and do not change
+# the forward's code.
+FORWARD_END = b"// ================================================================ backward =="
+
+
 def source_sha256() -> str:
+    """sha256 of the forward part of the kernel source (up to FORWARD_END)."""
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+        text = f.read()
+    cut = text.find(FORWARD_END)
+    return hashlib.sha256(text if cut < 0 else text[:cut]).hexdigest()
 
 
 def traffic_path(workload: str) -> str:
