@@ -10,8 +10,8 @@ the output projection of the layer (hidden = H*64, synthetic weights); its
 useful FLOPs add 2*M*N*K per projection (M = B*L) to the attention's.
 
 `--pass backward` times bb_attn_backward instead (the default is the forward,
-the headline): one step = one backward call over the whole batch (D and
-LSE2, the dQ pass, the dK/dV pass, the split-K reduce), its inputs (q, k, v,
+the headline): one step = one backward call over the whole batch (the dQ
+pass, which also forms D and LSE2, the dK/dV pass, the split-K reduce), its inputs (q, k, v,
 out, dout, lse from one forward) resident in HBM.  Useful backward FLOPs are
 10*d per attended pair -- the five products of the recompute-based backward
 (S, dP, dV, dK, dQ); the kernels execute 14*d (S and dP in both passes).
@@ -387,7 +387,7 @@ def bench_backward(args, w, dev):
                    "block": w.block, "r": w.r, "pad": w.pad, "mode": args.mode, "input_sets": n_sets,
                    "useful_gflop_per_step": round(flops / 1e9, 4),
                    "executed_gflop_per_step": round(3.5 * useful_flops(w) / 1e9, 4)},
-        "roofline": {"bound": "mfma", "kernel": "whole backward call (pre, dq, dkdv, reduce)",
+        "roofline": {"bound": "mfma", "kernel": "whole backward call (dq, dkdv, reduce)",
                      "achieved": round(value, 3), "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                      "frac": round(value / PEAK_TFLOPS[w.dtype], 4), "traffic": None},
         "cpu_baseline": None,
