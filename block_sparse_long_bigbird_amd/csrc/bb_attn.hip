@@ -1078,8 +1078,7 @@ struct BwdArgs {
   const float* lse;         // forward row log-sum-exp (natural log) [B*H][L]
   const int32_t* inv_off;   // [H][nb+1] ranges of inv_rows per (head, key block)
   const int32_t* inv_rows;  // middle query blocks holding each key block in their random list
-  float* lse2;              // workspace [B*H][L]: LSE * log2(e)
-  float* dsum;              // workspace [B*H][L]: D
+  f32x2* rowstat;           // workspace [B*H][L]: (LSE * log2(e), D) per row
   float* dq_part;           // workspace [B*H][2][n_s][BS][d], lane-major 64 x 64 blocks
   float* dk_part;
   float* dv_part;
@@ -1319,8 +1318,8 @@ __device__ __forceinline__ void run_dq(int n_units) {
     const float dsum = __uint_as_float(dsw[0]) + __uint_as_float(dsw[1]);
     const float lse2 = b->lse[row] * 1.4426950408889634f;
     if (wk == 0 && lane < 32) {
-      b->dsum[row] = dsum;
-      b->lse2[row] = lse2;
+      const f32x2 rs = {lse2, dsum};
+      b->rowstat[row] = rs;
     }
     const gchar_ptr vbh = (gchar_ptr)(b->f.v) + cu.off, kbh = (gchar_ptr)(b->f.k) + cu.off;
     const uint8_t* pad_b = HAS_PAD ? b->f.pad + static_cast<size_t>(cu.b) * b->f.L : nullptr;
@@ -1445,31 +1444,63 @@ struct KvState {
   f32x16 dv[2];   // dV^T
 };
 
+// (LSE2, D) of the query tile in stage S: BS pairs, filled by a DMA of its own
+// alongside the tile's, so a step reads them from LDS.  1 KiB: one DMA
+// instruction (64 lanes x 16 bytes); at block 64 its upper half holds a copy.
+template <int BS, int S>
+struct RowStats {
+  static __device__ __forceinline__ char* buf() {
+    __shared__ __attribute__((aligned(1024))) char b[1024];
+    return b;
+  }
+};
+
+// One 64 x 16-byte DMA into LDS at the wave-uniform address m0v (+16 per
+// lane) from base + off (per lane).  The leading s_nop 4 gives the 5 wait
+// states an SGPR written by a vector instruction needs before a vector-memory
+// instruction reads it; the M0 write gets its 1.
+__device__ __forceinline__ void dma16x1(gchar_ptr base, uint32_t off, uint32_t m0v) {
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(m0v)
+               : "memory", "m0");
+}
+
+// Wave 0 fetches the (LSE2, D) pairs of query tile `tile` into stage S: lane
+// l takes pairs 2 (l mod BS/2) .. +1 (16 bytes; the rows of one (b, h) stay
+// inside it).
+template <int BS, int S>
+__device__ __forceinline__ void issue_rowstats(gchar_ptr rs_bh, int tile, int wave, int lane) {
+  if (wave != 0) return;
+  const uint32_t off = static_cast<uint32_t>((tile * BS + 2 * (lane % (BS / 2))) * 8);
+  dma16x1(rs_bh, off, __builtin_amdgcn_readfirstlane(lds_addr(RowStats<BS, S>::buf())));
+}
+
 // One query tile: this wave's 32 keys x its 32 queries of the tile.
 template <typename T, int BS, int S>
 __device__ __forceinline__ void step_kv(KvState& st, const u32x4 (&kop)[Cfg<T, BS>::QC],
                                         const u32x4 (&vop)[Cfg<T, BS>::QC], float kbias_c, bool last,
                                         int tile_u, int tile_fill, gchar_ptr qbh, gchar_ptr gbh,
-                                        const float* lse2_bh, const float* dsum_bh, int wave, int lane, int wq) {
+                                        gchar_ptr rs_bh, int wave, int lane, int wq) {
   const int qb = wq * 32, g = lane >> 5;
   __builtin_amdgcn_s_waitcnt(7 << 4);
   ring_barrier();
-  // LSE2 and D of this lane's 16 accumulator rows: two runs of 8 queries
-  const size_t r0 = static_cast<size_t>(tile_u) * BS + qb + 8 * g;
+  // (LSE2, D) of this lane's 16 accumulator rows (two runs of 8 queries), from LDS
+  const char* rsl = RowStats<BS, S>::buf() + (qb + 8 * g) * 8;
   f32x4 l4[4], d4[4];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      l4[2 * h + x] = *reinterpret_cast<const f32x4*>(lse2_bh + r0 + 16 * h + 4 * x);
-      d4[2 * h + x] = *reinterpret_cast<const f32x4*>(dsum_bh + r0 + 16 * h + 4 * x);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(rsl + (16 * h + 4 * x) * 8);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(rsl + (16 * h + 4 * x) * 8 + 16);
+      l4[2 * h + x] = {a[0], a[2], c[0], c[2]};
+      d4[2 * h + x] = {a[1], a[3], c[1], c[3]};
     }
   const f32x16 s = rows_times<T, BS, S, 0>(kop, qb, lane);    // S = Q K^T (rows = queries)
   const f32x16 dp = rows_times<T, BS, S, 1>(vop, qb, lane);   // dP = dO V^T
   const VOp<T> got = cols_op<T, BS, S, 1>(qb, lane);         // dO^T
   const VOp<T> qt = cols_op<T, BS, S, 0>(qb, lane);          // Q^T
-  // P and dS before the next tile's DMA is issued: the compiler's own wait
-  // for the LSE2 / D loads then drains nothing but them.
   float p[16], ds[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -1480,8 +1511,10 @@ __device__ __forceinline__ void step_kv(KvState& st, const u32x4 (&kop)[Cfg<T, B
   bf16x8 pb[2], db[2];
   pack_pairs(p, pb);
   pack_pairs(ds, db);
-  asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(db[0]), "+v"(db[1]));
-  if (!last) issue_tile<T, BS, S ^ 1>(qbh, gbh, tile_fill, wave, lane);
+  if (!last) {
+    issue_tile<T, BS, S ^ 1>(qbh, gbh, tile_fill, wave, lane);
+    issue_rowstats<BS, S ^ 1>(rs_bh, tile_fill, wave, lane);
+  }
 #pragma unroll
   for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
@@ -1619,9 +1652,9 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
       kbias_c = pv == 0 ? kMaskRaw * kScaleLog2 : 0.0f;
     }
     const gchar_ptr qbh = (gchar_ptr)(b->f.q) + cu.off, gbh = (gchar_ptr)(b->dout) + cu.off;
-    const float* lse2_bh = b->lse2 + cu.bh * b->f.L;
-    const float* dsum_bh = b->dsum + cu.bh * b->f.L;
+    const gchar_ptr rs_bh = (gchar_ptr)(b->rowstat + cu.bh * b->f.L);
     issue_tile<T, BS, 0>(qbh, gbh, kv_tile_at(cu.tl, 0), wave, lane);
+    issue_rowstats<BS, 0>(rs_bh, kv_tile_at(cu.tl, 0), wave, lane);
     KvState st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -1646,7 +1679,7 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
 #define BB_STEP(k)                                                                                    \
   if ((k) < rem)                                                                                      \
     step_kv<T, BS, (k) % 2>(st, kop, vop, kbias_c, (k) + 1 == rem, BB_TILE(k), BB_TILE((k) + 1), qbh,   \
-                            gbh, lse2_bh, dsum_bh, wave, lane, wq);
+                            gbh, rs_bh, wave, lane, wq);
       BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
       BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
@@ -2067,7 +2100,7 @@ extern "C" int bb_attn_forward(const void* q, const void* k, const void* v, cons
 namespace {
 
 struct BwdLayout {
-  size_t lse2, dsum, dq, dk, dv, total;
+  size_t rowstat, dq, dk, dv, total;
 };
 
 BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
@@ -2075,9 +2108,8 @@ BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
   const size_t n_s = static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
   const size_t part = static_cast<size_t>(B) * H * 2 * n_s * block * kD * sizeof(float);
   BwdLayout w;
-  w.lse2 = 0;
-  w.dsum = w.lse2 + align256(rows * sizeof(float));
-  w.dq = w.dsum + align256(rows * sizeof(float));
+  w.rowstat = 0;
+  w.dq = w.rowstat + align256(rows * 2 * sizeof(float));
   w.dk = w.dq + align256(part);
   w.dv = w.dk + align256(part);
   w.total = w.dv + part;
@@ -2165,8 +2197,7 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   a.inv_off = inv_off;
   a.inv_rows = inv_rows;
   char* ws = static_cast<char*>(workspace);
-  a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
-  a.dsum = reinterpret_cast<float*>(ws + w.dsum);
+  a.rowstat = reinterpret_cast<f32x2*>(ws + w.rowstat);
   a.dq_part = reinterpret_cast<float*>(ws + w.dq);
   a.dk_part = reinterpret_cast<float*>(ws + w.dk);
   a.dv_part = reinterpret_cast<float*>(ws + w.dv);
