@@ -197,3 +197,25 @@ def test_capped_random_range_forward_and_backward(dev):
                                                               w.block)).max()
     say(f"  forward err {e:.3e}")
     assert e <= 2e-2
+
+
+def test_backward_pathx_sampled_unit(dev):
+    """The Path-X shape (1 x 8 x 16384): blocks 240..255 are padding, the
+    global key block 255 included (its dK and dV rows are zero; the padded
+    query rows follow the same rule).  Every output scanned for NaN, one
+    (batch, head) unit compared in full with the oracle."""
+    w = WORKLOADS["pathx_B1_H8_L16384_pad"]
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    got = run_backward(w, dev, inputs, ri, dout)
+    for a in got:
+        assert not np.isnan(a).any()
+    units = [(0, 3)]
+    q, k, v, pad = inputs
+    exp = attention_backward(f64(q), f64(k), f64(v), pad.numpy(), ri, w.block, f64(dout), units=units,
+                             row_group=2048)
+    check_grads(got, exp, units=units)
+    # padded keys get no gradient
+    valid = int(pad[0].sum())
+    assert np.abs(got[1][0, :, valid:]).max() == 0.0 and np.abs(got[2][0, :, valid:]).max() == 0.0
