@@ -1121,10 +1121,25 @@ __device__ __forceinline__ f32x16 rows_times(const u32x4 (&bop)[Cfg<T, BS>::QC],
 // r, r+4, r+16 and r+20 on one pattern).
 template <typename T, int BS, int S, int SLOT>
 __device__ __forceinline__ VOp<T> cols_op(int rbase, int lane) {
-  static_assert(sizeof(T) == 2, "bf16 operands");
   using C = Cfg<T, BS>;
   const char* sb = SLOT ? Stage<T, BS, S>::v() : Stage<T, BS, S>::k();
   VOp<T> vo;
+  if constexpr (sizeof(T) == 4) {
+    // fp32 (32x32x2 products): lane (dim, g) takes row 16 (v / 8) + 8 g + v % 8
+    // of the 32, one float per product, as the forward's fp32 V^T reads
+    const int j = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) {
+      const int dim = dh * 32 + perm_row(j);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = rbase + 16 * (v >> 3) + 8 * g + (v & 7);
+        const int sw = SLOT ? swz_v(row) : swz_k(row);
+        vo.a[dh][v] = *reinterpret_cast<const float*>(sb + row * C::ROWB + (((dim >> 2) ^ sw) << 4) + (dim & 3) * 4);
+      }
+    }
+    return vo;
+  } else {
   const int g = lane >> 5, e4 = (lane >> 2) & 3;
   const int r0 = rbase + 8 * g + e4;
   const int sw = SLOT ? swz_v(r0) : swz_k(r0);
@@ -1141,6 +1156,7 @@ __device__ __forceinline__ VOp<T> cols_op(int rbase, int lane) {
     }
   }
   return vo;
+  }
 }
 
 // Two bf16 pairs per 4 fp32 values, in the PV operand layout.
@@ -1154,6 +1170,26 @@ __device__ __forceinline__ void pack_pairs(const float (&x)[16], bf16x8 (&pb)[2]
       pb[h][e] = c2[0];
       pb[h][e + 1] = c2[1];
     }
+}
+
+// acc[dh] += A[dh] . X over this subtile's 32 rows, with A a transposed
+// operand (cols_op) and X the 16 fp32 values of a score-type product (lane =
+// column): bf16 pairs into 32x32x16 products, or fp32 into 32x32x2 ones.
+__device__ __forceinline__ void tprod(f32x16 (&acc)[2], const VOp<__bf16>& a, const float (&x)[16]) {
+  bf16x8 xb[2];
+  pack_pairs(x, xb);
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+      acc[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a[dh][mm], xb[mm], acc[dh], 0, 0, 0);
+}
+__device__ __forceinline__ void tprod(f32x16 (&acc)[2], const VOp<float>& a, const float (&x)[16]) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+      acc[dh] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[dh][v], x[v], acc[dh], 0, 0, 0);
 }
 
 // ---- dQ pass ----------------------------------------------------------------
@@ -1185,13 +1221,7 @@ __device__ __forceinline__ void step_dq(WaveState& ws, const u32x4 (&qop)[Cfg<T,
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], kScaleLog2, -off));
     ds[v] = p * (dp[v] - dsum);
   }
-  bf16x8 db[2];
-  pack_pairs(ds, db);
-#pragma unroll
-  for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-      ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt.a[dh][mm], db[mm], ws.o[dh], 0, 0, 0);
+  tprod(ws.o, kt, ds);
 }
 
 // Sum of the two key groups' dQ^T halves (exchanged through stage S), scaled
@@ -1274,7 +1304,6 @@ __device__ __forceinline__ void finalize_dq(WaveState& ws, const Unit& w, int wq
 template <typename T, int BS, bool HAS_PAD>
 __device__ __forceinline__ void run_dq(int n_units) {
   using C = Cfg<T, BS>;
-  static_assert(sizeof(T) == 2, "backward: bf16");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave % C::WQ, wk = wave / C::WQ;
@@ -1310,9 +1339,14 @@ __device__ __forceinline__ void run_dq(int n_units) {
     float dpart = 0.0f;
 #pragma unroll
     for (int x = 0; x < C::QC; ++x) {
-      const bf16x8 g8 = __builtin_bit_cast(bf16x8, dop[x]), o8 = __builtin_bit_cast(bf16x8, oop[x]);
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 g8 = __builtin_bit_cast(bf16x8, dop[x]), o8 = __builtin_bit_cast(bf16x8, oop[x]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dpart += static_cast<float>(g8[e]) * static_cast<float>(o8[e]);
+        for (int e = 0; e < 8; ++e) dpart += static_cast<float>(g8[e]) * static_cast<float>(o8[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dpart += __uint_as_float(dop[x][e]) * __uint_as_float(oop[x][e]);
+      }
     }
     const auto dsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart), __float_as_uint(dpart), false, false);
     const float dsum = __uint_as_float(dsw[0]) + __uint_as_float(dsw[1]);
@@ -1394,7 +1428,7 @@ struct KvUnit {
   KvTiles tl;
 };
 
-template <int BS>
+template <typename T, int BS>
 __device__ __forceinline__ KvUnit decode_kv_unit(bargs_ptr a, const Cursor& c) {
   constexpr int KS = BS / 64;           // 64-key units per key block
   constexpr int LKS = KS == 2 ? 1 : 0;
@@ -1402,7 +1436,7 @@ __device__ __forceinline__ KvUnit decode_kv_unit(bargs_ptr a, const Cursor& c) {
   const int n_g = 2 * n_s * KS;
   KvUnit w;
   w.bh = static_cast<size_t>(c.bh);
-  w.off = static_cast<size_t>(c.bh) * a->f.L * (kD * 2);
+  w.off = static_cast<size_t>(c.bh) * a->f.L * Cfg<T, BS>::ROWB;
   w.b = c.b;
   w.tl.nb = nb;
   if (c.u < n_g) {
@@ -1508,20 +1542,29 @@ __device__ __forceinline__ void step_kv(KvState& st, const u32x4 (&kop)[Cfg<T, B
     p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], kScaleLog2, kbias_c - l2));
     ds[v] = p[v] * (dp[v] - dd);
   }
-  bf16x8 pb[2], db[2];
-  pack_pairs(p, pb);
-  pack_pairs(ds, db);
-  if (!last) {
-    issue_tile<T, BS, S ^ 1>(qbh, gbh, tile_fill, wave, lane);
-    issue_rowstats<BS, S ^ 1>(rs_bh, tile_fill, wave, lane);
-  }
-#pragma unroll
-  for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-      st.dv[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(got.a[dh][mm], pb[mm], st.dv[dh], 0, 0, 0);
-      st.dk[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt.a[dh][mm], db[mm], st.dk[dh], 0, 0, 0);
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 pb[2], db[2];
+    pack_pairs(p, pb);
+    pack_pairs(ds, db);
+    if (!last) {
+      issue_tile<T, BS, S ^ 1>(qbh, gbh, tile_fill, wave, lane);
+      issue_rowstats<BS, S ^ 1>(rs_bh, tile_fill, wave, lane);
     }
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh) {
+        st.dv[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(got.a[dh][mm], pb[mm], st.dv[dh], 0, 0, 0);
+        st.dk[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt.a[dh][mm], db[mm], st.dk[dh], 0, 0, 0);
+      }
+  } else {
+    if (!last) {
+      issue_tile<T, BS, S ^ 1>(qbh, gbh, tile_fill, wave, lane);
+      issue_rowstats<BS, S ^ 1>(rs_bh, tile_fill, wave, lane);
+    }
+    tprod(st.dv, got, p);
+    tprod(st.dk, qt, ds);
+  }
 }
 
 // Sum of the two query groups' dK^T and dV^T (wave wq keeps dims
@@ -1618,7 +1661,6 @@ __device__ __forceinline__ void finalize_kv(KvState& st, const KvUnit& w, int wq
 template <typename T, int BS, bool HAS_PAD>
 __device__ __forceinline__ void run_dkdv(int n_units) {
   using C = Cfg<T, BS>;
-  static_assert(sizeof(T) == 2, "backward: bf16");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // two key groups (32 keys each) of the 64-key unit, BS/32 query groups of each query tile
@@ -1641,7 +1683,7 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
   Cursor cur = cursor_at<T, BS, 0>(kargs(), first);
   for (;;) {
     const bargs_ptr b = bargs();
-    const KvUnit cu = decode_kv_unit<BS>(b, cur);
+    const KvUnit cu = decode_kv_unit<T, BS>(b, cur);
     // K^T and V^T of this wave's 32 keys as B operands (lane j: key k0 + 32 wk + j)
     u32x4 kop[C::QC], vop[C::QC];
     load_q<T, BS>(b->f.k + cu.off + static_cast<size_t>(cu.k0) * C::ROWB, wk, lane, kop);
@@ -1731,11 +1773,11 @@ __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
 }
 
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(3))) bb_bwd_dq_kernel(BwdArgs, int n_units) {
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : (BS == 64 ? 1 : 2)))) bb_bwd_dq_kernel(BwdArgs, int n_units) {
   run_dq<T, BS, HAS_PAD>(n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(2))) bb_bwd_dkdv_kernel(BwdArgs, int n_units) {
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : (BS == 64 ? 1 : 2)))) bb_bwd_dkdv_kernel(BwdArgs, int n_units) {
   run_dkdv<T, BS, HAS_PAD>(n_units);
 }
 
@@ -2116,9 +2158,8 @@ BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
   return w;
 }
 
-template <int BS, bool HAS_PAD>
+template <typename T, int BS, bool HAS_PAD>
 int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
-  using T = __bf16;
   using C = Cfg<T, BS>;
   const long long bhs = static_cast<long long>(B) * H;
   const long long rows = bhs * a.f.L;
@@ -2157,7 +2198,6 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
                                 const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
-  if (dtype != BB_BF16) return BB_ERR_DTYPE;
   int nb = 0;
   const int st = check_shape(B, H, L, d, block, r, &nb);
   if (st != BB_OK) return st;
@@ -2170,7 +2210,7 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   if ((pad_mask && !aligned(pad_mask, 8)) || !aligned(workspace, 256) || !aligned(lse, 4) ||
       !aligned(inv_off, 4) || (rand_idx && !aligned(rand_idx, 4)) || (inv_rows && !aligned(inv_rows, 4)))
     return BB_ERR_ALIGN;
-  const size_t bytes = static_cast<size_t>(B) * H * L * d * 2;
+  const size_t bytes = static_cast<size_t>(B) * H * L * d * (dtype == BB_BF16 ? 2 : 4);
   const void* ins[] = {q, k, v, out, dout};
   for (void* g : {dq, dk, dv}) {
     for (const void* x : ins)
@@ -2205,8 +2245,14 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   a.dk = static_cast<char*>(dk);
   a.dv = static_cast<char*>(dv);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (block == 64) return pad_mask ? launch_bwd<64, true>(a, B, H, s) : launch_bwd<64, false>(a, B, H, s);
-  return pad_mask ? launch_bwd<128, true>(a, B, H, s) : launch_bwd<128, false>(a, B, H, s);
+  if (dtype == BB_BF16) {
+    if (block == 64)
+      return pad_mask ? launch_bwd<__bf16, 64, true>(a, B, H, s) : launch_bwd<__bf16, 64, false>(a, B, H, s);
+    return pad_mask ? launch_bwd<__bf16, 128, true>(a, B, H, s) : launch_bwd<__bf16, 128, false>(a, B, H, s);
+  }
+  if (block == 64)
+    return pad_mask ? launch_bwd<float, 64, true>(a, B, H, s) : launch_bwd<float, 64, false>(a, B, H, s);
+  return pad_mask ? launch_bwd<float, 128, true>(a, B, H, s) : launch_bwd<float, 128, false>(a, B, H, s);
 }
 
 // --------------------------------------------------------------- layer host --

@@ -221,8 +221,8 @@ size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, int block);
  *   dout       DEVICE upstream gradient [B][H][L][d].
  *   dq, dk, dv DEVICE [B][H][L][d], fully overwritten; must not overlap each
  *              other or any input.
- *   dtype      BB_BF16 only (fp32 accumulation, bf16 results rounded to
- *              nearest even); BB_FP32 returns BB_ERR_DTYPE.
+ *   dtype      BB_BF16 (fp32 accumulation, bf16 results rounded to nearest
+ *              even) or BB_FP32, as the forward.
  *   block      64 or 128, as the forward.
  *   workspace  DEVICE, >= bb_attn_backward_workspace_bytes(), 256-byte aligned,
  *              no initialisation needed; concurrent calls need distinct ones.

@@ -251,14 +251,13 @@ def bwd(lib, q=FAKE, k=2 * FAKE, v=3 * FAKE, pad=0, rand=4 * FAKE, inv_off=10 * 
 
 
 def test_backward_validation_errors(lib):
-    assert bwd(lib, dtype=0) == 3                       # fp32: BB_ERR_DTYPE
-    assert bwd(lib, dtype=9) == 3
+    assert bwd(lib, dtype=9) == 3                       # BB_ERR_DTYPE
     assert bwd(lib, block=32) == 2
     assert bwd(lib, d=32) == 2
     assert bwd(lib, r=12) == 2
     for name in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "ws", "inv_off", "rand", "inv_rows"):
         assert bwd(lib, **{name: 0}) == 1, name         # BB_ERR_NULL
-    assert bwd(lib, r=0, rand=0, inv_rows=0) != 1       # r == 0 needs no table
+    assert bwd(lib, r=0, rand=0, inv_rows=0, ws_bytes=1) == 5   # r == 0 needs no table (stops at the workspace)
     assert bwd(lib, dq=12 * FAKE + 8) == 8              # BB_ERR_ALIGN
     assert bwd(lib, lse=7 * FAKE + 2) == 8
     assert bwd(lib, dq=FAKE) == 7                       # dq == q
