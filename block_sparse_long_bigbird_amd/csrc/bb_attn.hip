@@ -1793,11 +1793,12 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
 //   W: [N][K], the [out][in] layout of a linear layer.
 //   C: MODE 0 q, k and v in the attention's layout [B][H][L][64] (columns
 //      n of [q | k | v], N = 3*hidden); MODE 1 y [M][N].
-// Workgroup tile 128 rows of A x 128 rows of W; K in steps of 64 through a
-// two-stage LDS ring filled by the same DMA as the attention.  4 waves of
-// 64 x 64 (2 x 2 subtiles of 32 x 32), computed transposed (C^T = W A^T):
-// lane = row of A, 16 accumulators = 2 runs of 8 consecutive columns, so
-// the epilogue writes 16-byte runs with the bias added.
+// Workgroup tile 64 WMW rows of A x 64 SN rows of W, with 2 WMW waves of
+// 64 x 32 SN (2 x SN subtiles of 32 x 32 each); K in steps of 64 through a
+// two-stage LDS ring filled by the same DMA as the attention.  Computed
+// transposed (C^T = W A^T): lane = row of A, 16 accumulators = 2 runs of 8
+// consecutive columns, so the epilogue writes 16-byte runs with the bias
+// added.
 
 struct ProjArgs {
   const char* a;
@@ -1809,49 +1810,94 @@ struct ProjArgs {
   int hidden;
 };
 
-template <int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) bb_proj_kernel(ProjArgs g) {
-  constexpr int MT = 128 * 128;                  // bytes per matrix per stage: 128 rows x 64 bf16
-  __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * MT];   // [stage][A, W]
+// Two DMAs of 64 x 16 bytes from one wave-uniform base (see dma16x4).
+__device__ __forceinline__ void dma16x2(gchar_ptr base, uint32_t o0, uint32_t o1, uint32_t m0a, uint32_t m0b) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4"
+      :
+      : "v"(o0), "v"(o1), "s"(m0a), "s"(m0b), "s"(base)
+      : "memory", "m0");
+}
+
+template <int MODE, int WMW, int SN>
+__global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(2))) bb_proj_kernel(ProjArgs g) {
+  constexpr int NW = 2 * WMW;                      // waves: WMW along A rows x 2 along W rows
+  constexpr int TM = 64 * WMW, TN = 64 * SN;       // rows of A and of W per tile
+  constexpr int AB = TM * 128, SB = AB + TN * 128;  // bytes per stage (128-byte rows): A part, whole
+  constexpr int NA = AB / 1024 / NW, NWI = TN * 128 / 1024 / NW;   // DMAs per wave per stage
+  static_assert(NA % 2 == 0 && NA * NW * 1024 == AB && NWI * NW * 1024 == TN * 128, "DMAs split evenly");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * SB];   // [stage][A rows | W rows]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WMW, wn = wave / WMW;
   const int j = lane & 31, gh = lane >> 5;
-  const int tiles_n = g.N / 128;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-  const int m0 = tm * 128, n0 = tn * 128;
+  const int tiles_n = g.N / TN;
+  const int tiles_m = g.M / TM;
+  // Tile order.  Consecutive workgroups go round-robin to the 8 XCDs, each
+  // with its own L2: when the row panels split evenly, XCD x takes panels
+  // [x pm, (x+1) pm) and walks them in groups of GM panels, column tile by
+  // column tile, so the A panels and W tiles its resident workgroups share
+  // stay in its L2 (one read of the layer's A per XCD instead of per tile
+  // column).
+  int tm, tn;
+  if ((tiles_m & 7) == 0) {
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int pm = tiles_m >> 3;
+    const int GM = pm % 8 == 0 ? 8 : (pm % 4 == 0 ? 4 : 1);
+    const int grp = idx / (GM * tiles_n), rr = idx - grp * (GM * tiles_n);
+    tm = xcd * pm + grp * GM + rr % GM;
+    tn = rr / GM;
+  } else {
+    tm = blockIdx.x / tiles_n;
+    tn = blockIdx.x - tm * tiles_n;
+  }
+  const int m0 = tm * TM, n0 = tn * TN;
   const int nk = g.K / 64;
-  // A rows of this tile: MODE 1 reads head ks of batch b, rows l0 .. l0+127
+  // A rows of this tile: MODE 1 reads head ks of batch b, rows l0 .. l0+TM-1
   const int b0 = m0 / g.L, l0 = m0 - b0 * g.L;
   const size_t a_row = MODE == 0 ? static_cast<size_t>(g.K) * 2 : 128;
-  // per-lane DMA offsets (4 instructions per wave per matrix) and LDS slots
-  uint32_t ao[4], wo[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int ins = wave + 4 * jj;
-    const int slot = ins * 64 + lane;
-    const int row = slot >> 3, p = slot & 7;
-    ao[jj] = static_cast<uint32_t>(row * a_row + ((p ^ (row & 7)) << 4));
-    wo[jj] = static_cast<uint32_t>(static_cast<size_t>(row) * g.K * 2 + ((p ^ swz_k(row)) << 4));
-  }
+  // This wave's DMA instructions per stage: A instructions wave + NW jj, W
+  // instructions wave + NW jj.  Lane l of instruction i fills physical chunk
+  // slot 64 i + l: row (64 i + l) / 8, chunk l % 8, with the logical chunk
+  // the swizzle puts there (A: row & 7, W: swz_k, as the operand reads below).
+  uint32_t ao[NA], wo[NWI], am[NA], wmo[NWI];
   const uint32_t lds0 = lds_addr(lds);
+#pragma unroll
+  for (int jj = 0; jj < NA; ++jj) {
+    const int ins = wave + NW * jj;
+    const int row = (ins * 64 + lane) >> 3, p = lane & 7;
+    ao[jj] = static_cast<uint32_t>(row * a_row + ((p ^ (row & 7)) << 4));
+    am[jj] = ins * 1024;
+  }
+#pragma unroll
+  for (int jj = 0; jj < NWI; ++jj) {
+    const int ins = wave + NW * jj;
+    const int row = (ins * 64 + lane) >> 3, p = lane & 7;
+    wo[jj] = static_cast<uint32_t>(static_cast<size_t>(row) * g.K * 2 + ((p ^ swz_k(row)) << 4));
+    wmo[jj] = AB + ins * 1024;
+  }
   auto issue = [&](int ks, int st) {
     const gchar_ptr ab = MODE == 0
         ? (gchar_ptr)(g.a) + static_cast<size_t>(m0) * g.K * 2 + static_cast<size_t>(ks) * 128
         : (gchar_ptr)(g.a) + ((static_cast<size_t>(b0) * g.H + ks) * g.L + l0) * 128;
     const gchar_ptr wb = (gchar_ptr)(g.w) + static_cast<size_t>(n0) * g.K * 2 + static_cast<size_t>(ks) * 128;
-    const uint32_t la = lds0 + st * 2 * MT, lw = la + MT;
+    const uint32_t base = lds0 + st * SB;
 #pragma unroll
-    for (int jj = 0; jj < 4; jj += 2) {
-      const int i0 = wave + 4 * jj, i1 = wave + 4 * (jj + 1);
-      dma16x4(ab, wb, ao[jj], wo[jj], ao[jj + 1], wo[jj + 1], __builtin_amdgcn_readfirstlane(la + i0 * 1024),
-              __builtin_amdgcn_readfirstlane(lw + i0 * 1024), __builtin_amdgcn_readfirstlane(la + i1 * 1024),
-              __builtin_amdgcn_readfirstlane(lw + i1 * 1024));
-    }
+    for (int jj = 0; jj < NA; jj += 2)
+      dma16x2(ab, ao[jj], ao[jj + 1], __builtin_amdgcn_readfirstlane(base + am[jj]),
+              __builtin_amdgcn_readfirstlane(base + am[jj + 1]));
+#pragma unroll
+    for (int jj = 0; jj + 1 < NWI; jj += 2)
+      dma16x2(wb, wo[jj], wo[jj + 1], __builtin_amdgcn_readfirstlane(base + wmo[jj]),
+              __builtin_amdgcn_readfirstlane(base + wmo[jj + 1]));
+    if constexpr (NWI % 2 == 1)
+      dma16x1(wb, wo[NWI - 1], __builtin_amdgcn_readfirstlane(base + wmo[NWI - 1]));
   };
-  f32x16 acc[2][2];
+  f32x16 acc[SN][2];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < SN; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y)
 #pragma unroll
@@ -1862,39 +1908,37 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) b
     __builtin_amdgcn_s_waitcnt(7 << 4);
     ring_barrier();
     if (ks + 1 < nk) issue(ks + 1, st ^ 1);
-    const char* la = lds + st * 2 * MT;
-    const char* lw = la + MT;
-    u32x4 bop[2][4];
+    const char* la = lds + st * SB;
+    const char* lw = la + AB;
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const int row = wm * 64 + ms * 32 + j;
+    for (int x = 0; x < 4; ++x) {
+      u32x4 bop[2], aop[SN];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        bop[ms][x] = *reinterpret_cast<const u32x4*>(la + row * 128 + (((2 * x + gh) ^ (row & 7)) << 4));
-    }
+      for (int ms = 0; ms < 2; ++ms) {
+        const int row = wm * 64 + ms * 32 + j;
+        bop[ms] = *reinterpret_cast<const u32x4*>(la + row * 128 + (((2 * x + gh) ^ (row & 7)) << 4));
+      }
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-      const int row = wn * 64 + ns * 32 + perm_row(j);
-      u32x4 aop[4];
+      for (int ns = 0; ns < SN; ++ns) {
+        const int row = wn * (32 * SN) + ns * 32 + perm_row(j);
+        aop[ns] = *reinterpret_cast<const u32x4*>(lw + row * 128 + (((2 * x + gh) ^ swz_k(row)) << 4));
+      }
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        aop[x] = *reinterpret_cast<const u32x4*>(lw + row * 128 + (((2 * x + gh) ^ swz_k(row)) << 4));
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int ns = 0; ns < SN; ++ns)
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms)
-          acc[ns][ms] = mfma_qk(aop[x], bop[ms][x], acc[ns][ms], static_cast<__bf16*>(nullptr));
+          acc[ns][ms] = mfma_qk(aop[ns], bop[ms], acc[ns][ms], static_cast<__bf16*>(nullptr));
     }
   }
   // epilogue: lane (j, gh) holds C[m][n] for m = its row, n in two runs of 8
 #pragma unroll
-  for (int ns = 0; ns < 2; ++ns)
+  for (int ns = 0; ns < SN; ++ns)
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms) {
       const int m = m0 + wm * 64 + ms * 32 + j;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int n = n0 + wn * 64 + ns * 32 + 16 * h + 8 * gh;
+        const int n = n0 + wn * (32 * SN) + ns * 32 + 16 * h + 8 * gh;
         const f32x4 b0v = *reinterpret_cast<const f32x4*>(g.bias + n);
         const f32x4 b1v = *reinterpret_cast<const f32x4*>(g.bias + n + 4);
         float x8[8];
@@ -1916,6 +1960,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) b
         store_row8(dst, x8, static_cast<__bf16*>(nullptr));
       }
     }
+}
+
+// Launch C = A W^T + bias for one projection: tiles of 128 rows of A by 192
+// rows of W where N allows (3 hidden always does), else 128.  (Tiles of 256
+// rows of A, one 8-wave workgroup per CU, measured within noise of these.)
+template <int MODE>
+void launch_proj(const ProjArgs& a, hipStream_t s) {
+  if (a.N % 192 == 0)
+    hipLaunchKernelGGL((bb_proj_kernel<MODE, 2, 3>), dim3(static_cast<unsigned>((a.M / 128) * (a.N / 192))),
+                       dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((bb_proj_kernel<MODE, 2, 2>), dim3(static_cast<unsigned>((a.M / 128) * (a.N / 128))),
+                       dim3(256), 0, s, a);
 }
 
 // ---------------------------------------------------------------- host side --
@@ -2322,8 +2379,7 @@ extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b
   pa.L = L;
   pa.H = H;
   pa.hidden = hidden;
-  hipLaunchKernelGGL((bb_proj_kernel<0>), dim3(static_cast<unsigned>((M / 128) * (3 * hidden / 128))), dim3(256), 0,
-                     s, pa);
+  launch_proj<0>(pa, s);
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   const int fst = forward_impl(ws + w.q, ws + w.k, ws + w.v, pad_mask, rand_idx, B, H, L, kD, block, r, ws + w.o,
                                BB_BF16, ws + w.attn, workspace_bytes - w.attn, stream, BB_LAUNCH_FUSED, nullptr,
@@ -2335,8 +2391,7 @@ extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b
   po.bias = b_o;
   po.out = static_cast<char*>(y);
   po.N = hidden;
-  hipLaunchKernelGGL((bb_proj_kernel<1>), dim3(static_cast<unsigned>((M / 128) * (hidden / 128))), dim3(256), 0, s,
-                     po);
+  launch_proj<1>(po, s);
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   return BB_OK;
 }
