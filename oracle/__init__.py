@@ -14,6 +14,7 @@ from .bigbird_oracle import (  # noqa: F401
     block_adjacency,
     check_rand_idx,
     layer_forward,
+    layer_rows,
     num_blocks,
     token_mask,
 )

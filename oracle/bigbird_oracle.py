@@ -303,3 +303,32 @@ def layer_forward(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, H: int, block: 
     o = attention_forward(q, k, v, pad_mask, rand_idx, block)
     o = o.transpose(0, 2, 1, 3).reshape(B, L, hid)
     return o @ np.asarray(w_o, np.float64).T + np.asarray(b_o, np.float64)
+
+
+def layer_rows(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, H: int, block: int, rows) -> np.ndarray:
+    """Rows `rows` (token indices, the same in every sequence) of layer_forward's
+    output, fp64 [B, len(rows), hidden].
+
+    The same steps as layer_forward: the projections of every token (keys and
+    values need them all), attention_rows for the selected query rows of every
+    head, and the output projection of those rows.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, L, hid = x.shape
+    d = hid // H
+    nb = num_blocks(L, block)
+    rows = np.asarray(rows, dtype=np.int64)
+    rand_idx = np.asarray(rand_idx)
+    r = rand_idx.shape[2] if rand_idx.ndim == 3 else 0
+    check_rand_idx(rand_idx, H, L, block, r)
+    proj = x @ np.asarray(w_qkv, np.float64).T + np.asarray(b_qkv, np.float64)
+    def heads(t):                                        # [B, L, hid] -> [B, H, L, d]
+        return t.reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    q, k, v = (heads(proj[..., i * hid:(i + 1) * hid]) for i in range(3))
+    o = np.empty((B, len(rows), H, d))
+    for h in range(H):
+        adj = block_adjacency(rand_idx[h], nb)
+        for b in range(B):
+            pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
+            o[b, :, h, :] = attention_rows(q[b, h], k[b, h], v[b, h], pad_b, adj, block, rows)
+    return o.reshape(B, len(rows), hid) @ np.asarray(w_o, np.float64).T + np.asarray(b_o, np.float64)

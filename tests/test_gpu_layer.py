@@ -15,7 +15,7 @@ import torch
 
 from block_sparse_long_bigbird_amd import binding as bb
 from block_sparse_long_bigbird_amd.workloads import WORKLOADS, make_layer_inputs, small
-from oracle import layer_forward
+from oracle import layer_forward, layer_rows
 
 pytestmark = pytest.mark.gpu
 REL = 2e-2
@@ -86,3 +86,25 @@ def test_layer_full_size_one_sequence(dev):
     w = small("layer_base_B1", B=1, H=base.H, L=base.L, block=base.block, r=base.r,
               pad="fixed", valid_len=base.L - 1000, value_scale=base.value_scale, data_seed=75)
     check(w, dev)
+
+
+def test_layer_full_size_bench_configuration_sampled(dev):
+    """The benchmark's layer configuration exactly (BigBird-base shape, B 4, L 4096,
+    hidden 768, 12 heads, per-sequence padding, the benchmark's inputs and
+    table): sampled output rows of every sequence against the oracle's
+    layer_rows (global blocks, block edges, padded rows, random picks)."""
+    w = WORKLOADS["base_B4_H12_L4096_pad"]
+    inputs = make_layer_inputs(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    got = run_layer(w, dev, inputs, ri)
+    assert not np.isnan(got).any(), "unwritten (NaN) outputs"
+    rng = np.random.default_rng(76)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 127, 2047, 2048, 2049, 4031, 4032, 4095],
+                                     rng.integers(0, w.L, 8)]))
+    x, w_qkv, b_qkv, w_o, b_o, pad = inputs
+    exp = layer_rows(f64(x), f64(w_qkv), b_qkv.numpy().astype(np.float64), f64(w_o),
+                     b_o.numpy().astype(np.float64), None if pad is None else pad.numpy(), ri, w.H,
+                     w.block, rows)
+    err, scale = np.abs(got[:, rows] - exp).max(), np.abs(exp).max()
+    say(f"  {len(rows)} rows x {w.B} sequences: max err {err:.3e}  max |ref| {scale:.3e}  rel {err / scale:.3e}")
+    assert err <= REL * scale

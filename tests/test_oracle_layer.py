@@ -5,13 +5,15 @@ attention), CPU only:
     pinned, attention, and per pair for one row);
   - the projections against torch.nn.functional.linear in float64 on the
     same weights (independent library code), with the attention between them;
-  - linearity in the output projection: scaling W_o and b_o scales y.
+  - linearity in the output projection: scaling W_o and b_o scales y;
+  - layer_rows (selected output rows, used for the full-size GPU check) against
+    the same torch.nn.functional.linear composition, row by row.
 """
 
 import numpy as np
 import torch
 
-from oracle import attention_forward, layer_forward
+from oracle import attention_forward, layer_forward, layer_rows
 
 
 def sample_rand_idx(rng, H, nb, r):
@@ -73,3 +75,17 @@ def test_output_projection_is_linear():
     y1 = layer_forward(x, w_qkv, b_qkv, w_o, b_o, None, ri, 3, 4)
     y2 = layer_forward(x, w_qkv, b_qkv, 2.5 * w_o, 2.5 * b_o, None, ri, 3, 4)
     assert np.abs(y2 - 2.5 * y1).max() <= 1e-12
+
+
+def test_layer_rows_match_torch_linear_composition():
+    x, w_qkv, b_qkv, w_o, b_o, pad, ri = case(4)
+    B, L, hid = x.shape
+    H, d = 3, hid // 3
+    t = torch.nn.functional.linear(torch.tensor(x), torch.tensor(w_qkv), torch.tensor(b_qkv)).numpy()
+    qkv = [t[..., i * hid:(i + 1) * hid].reshape(B, L, H, d).transpose(0, 2, 1, 3) for i in range(3)]
+    att = attention_forward(*qkv, pad, ri, 4).transpose(0, 2, 1, 3).reshape(B, L, hid)
+    exp = torch.nn.functional.linear(torch.tensor(att), torch.tensor(w_o), torch.tensor(b_o)).numpy()
+    rows = np.array([0, 1, 3, 4, 17, 40, 44, 47])      # global blocks, band rows, padded rows
+    got = layer_rows(x, w_qkv, b_qkv, w_o, b_o, pad, ri, H, 4, rows)
+    assert got.shape == (B, len(rows), hid)
+    assert np.abs(got - exp[:, rows]).max() <= 1e-12
