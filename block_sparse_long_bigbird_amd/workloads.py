@@ -39,7 +39,7 @@ class Workload:
     r: int
     dtype: str                 # "fp32" or "bf16"
     value_scale: float         # N(0,1) draws are multiplied by this
-    pad: str                   # "none" | "per_seq_blocks" | "fixed"
+    pad: str                   # "none" | "per_seq_blocks" | "fixed" | "scattered"
     valid_len: int = 0         # for pad == "fixed"
     pad_lo_blocks: int = 0     # for pad == "per_seq_blocks": valid = block*U{lo..hi}
     pad_hi_blocks: int = 0
@@ -114,6 +114,16 @@ def draw(w: Workload):
     elif w.pad == "fixed":
         pad = np.zeros((w.B, w.L), dtype=np.uint8)
         pad[:, : w.valid_len] = 1
+    elif w.pad == "scattered":
+        # holes anywhere, from their own stream (PCG64 seeded with data_seed + 3000):
+        # each token padded with probability 0.3, plus one padded span of 1.5 blocks
+        # per sequence (whole padded 32-key subtiles between valid ones)
+        prng = np.random.Generator(np.random.PCG64(w.data_seed + 3000))
+        pad = (prng.random((w.B, w.L)) >= 0.3).astype(np.uint8)
+        span = 3 * w.block // 2
+        for b in range(w.B):
+            s0 = int(prng.integers(0, w.L - span + 1))
+            pad[b, s0:s0 + span] = 0
     elif w.pad != "none":
         raise ValueError(f"unknown pad mode {w.pad!r}")
     if w.outlier_frac > 0.0:

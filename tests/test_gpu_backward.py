@@ -119,6 +119,14 @@ BWD_CASES = [
           valid_len=9 * 64 - 70, data_seed=67),
     small("bwd_fp32_nb17_r3", B=1, H=2, L=17 * 64, block=64, r=3, dtype="fp32", data_seed=68),
     small("bwd_fp32_bs128_nb7_r2", B=1, H=2, L=7 * 128, block=128, r=2, dtype="fp32", data_seed=69),
+    small("bwd_nb10_r3_scattered_pad", B=2, H=2, L=10 * 64, block=64, r=3, pad="scattered",
+          data_seed=70),
+    small("bwd_bs128_nb7_r2_scattered_pad", B=1, H=2, L=7 * 128, block=128, r=2, pad="scattered",
+          data_seed=71),
+    small("bwd_fp32_nb8_r2_scattered_pad", B=1, H=2, L=8 * 64, block=64, r=2, dtype="fp32",
+          pad="scattered", data_seed=72),
+    small("bwd_nb8_r2_all_padded", B=2, H=2, L=8 * 64, block=64, r=2, pad="fixed", valid_len=0,
+          data_seed=73),
 ]
 
 

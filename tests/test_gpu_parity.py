@@ -130,6 +130,15 @@ SMALL = [
     small("nb24_r16_pad_two_trips", B=2, H=2, L=24 * 64, block=64, r=16, pad="per_seq_blocks",
           pad_lo_blocks=10, pad_hi_blocks=24, data_seed=27),
     small("fp32_bs128_nb22_r16", B=1, H=1, L=22 * 128, block=128, r=16, dtype="fp32", data_seed=28),
+    # pad masks with holes (mixed and fully padded subtiles between valid ones)
+    small("nb10_r3_scattered_pad", B=2, H=2, L=10 * 64, block=64, r=3, pad="scattered", data_seed=29),
+    small("bs128_nb7_r2_scattered_pad", B=1, H=2, L=7 * 128, block=128, r=2, pad="scattered",
+          data_seed=30),
+    small("fp32_nb8_r2_scattered_pad", B=1, H=2, L=8 * 64, block=64, r=2, dtype="fp32",
+          pad="scattered", data_seed=32),
+    # every key of every row padded: the offset is uniform per row and cancels
+    small("nb8_r2_all_padded", B=2, H=2, L=8 * 64, block=64, r=2, pad="fixed", valid_len=0,
+          data_seed=33),
 ]
 
 
