@@ -157,6 +157,23 @@ def make_inputs(w: Workload):
     return tq, tk, tv, tpad
 
 
+def make_inputs_device(w: Workload, dev):
+    """q, k, v drawn on the device, for shapes too large to draw on the host:
+    N(0, 1) from torch's device generator seeded with data_seed (q, then k,
+    then v), times value_scale, rounded to the compute dtype.  No padding, no
+    outliers.  Returns (q, k, v) device tensors [B, H, L, d]."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.data_seed)
+    out = []
+    for _ in range(3):
+        t = torch.randn((w.B, w.H, w.L, w.d), generator=g, device=dev, dtype=torch.float32)
+        t.mul_(w.value_scale)
+        out.append(t.to(torch_dtype(w.dtype)))
+        del t
+    return tuple(out)
+
+
 def small(name: str, B: int, H: int, L: int, block: int, r: int, dtype: str = "bf16",
           d: int = 64, value_scale: float = 1.0, pad: str = "none", valid_len: int = 0,
           pad_lo_blocks: int = 0, pad_hi_blocks: int = 0, outlier_frac: float = 0.0,

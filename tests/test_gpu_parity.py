@@ -15,7 +15,8 @@ import pytest
 import torch
 
 from block_sparse_long_bigbird_amd import binding as bb
-from block_sparse_long_bigbird_amd.workloads import STRESS_LONG, WORKLOADS, make_inputs, small
+from block_sparse_long_bigbird_amd.workloads import (STRESS_LONG, WORKLOADS, make_inputs,
+                                                      make_inputs_device, small)
 from oracle import attention_forward, attention_rows, block_adjacency
 
 pytestmark = pytest.mark.gpu
@@ -256,6 +257,35 @@ def test_stress_unscaled_outliers(dev):
     say(f"case {w.name}")
     got, inputs, ri = run_gpu(w, dev)
     compare_sampled(w, got, inputs, ri, [(0, 3)])
+
+
+def test_tensors_over_4gib_sampled(dev):
+    """64-bit addressing: q, k, v and out of 4.56 GB each, past 2^32 bytes (B 64,
+    H 17, L 32768, block 128, r 4; global-row partials of 2.3 GB), drawn on the
+    device.  The first, a middle and the last (batch, head) are compared on
+    sampled query blocks."""
+    w = small("big_B64_H17_L32768_bs128", B=64, H=17, L=32768, block=128, r=4,
+              value_scale=0.125, data_seed=34)
+    assert w.B * w.H * w.L * w.d * 2 > 2**32
+    q, k, v = make_inputs_device(w, dev)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    out = torch.full_like(q, float("nan"))
+    ws = poisoned_workspace(w, dev)
+    say(f"  launch {w.name} ({q.numel() * 2 / 2**30:.2f} GiB per tensor)")
+    bb.bb_attn_forward(q, k, v, None, torch.from_numpy(ri).to(dev), w.B, w.H, w.L, w.d, w.block,
+                       w.r, out, ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "unwritten (NaN) outputs"
+    rows = sampled_rows(w, None)
+    worst = 0.0
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, 7)]:
+        adj = block_adjacency(ri[h], w.nb)
+        exp = attention_rows(f64(q[b, h].cpu()), f64(k[b, h].cpu()), f64(v[b, h].cpu()), None, adj,
+                             w.block, rows)
+        got = out[b, h, rows].float().cpu().numpy()
+        worst = max(worst, float(np.abs(got - exp).max()))
+    say(f"  max err over 3 units x {len(rows)} rows: {worst:.3e}")
+    assert worst <= TOL[w.dtype], worst
 
 
 # --------------------------------------------------------------- error paths ---
