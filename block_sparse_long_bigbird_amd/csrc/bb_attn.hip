@@ -1694,7 +1694,7 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
       kbias_c = pv == 0 ? kMaskRaw * kScaleLog2 : 0.0f;
     }
     const gchar_ptr qbh = (gchar_ptr)(b->f.q) + cu.off, gbh = (gchar_ptr)(b->dout) + cu.off;
-    const gchar_ptr rs_bh = (gchar_ptr)(b->rowstat + cu.bh * b->f.L);
+    const gchar_ptr rs_bh = (gchar_ptr)(b->rowstat + static_cast<size_t>(cu.bh) * b->f.L);
     issue_tile<T, BS, 0>(qbh, gbh, kv_tile_at(cu.tl, 0), wave, lane);
     issue_rowstats<BS, 0>(rs_bh, kv_tile_at(cu.tl, 0), wave, lane);
     KvState st;

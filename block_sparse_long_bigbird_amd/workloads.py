@@ -174,6 +174,17 @@ def make_inputs_device(w: Workload, dev):
     return tuple(out)
 
 
+def make_dout_device(w: Workload, dev):
+    """Upstream gradient drawn on the device for the shapes of make_inputs_device:
+    N(0, 1) from torch's device generator seeded with data_seed + 1000, rounded
+    to the compute dtype.  Returns a device tensor [B, H, L, d]."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.data_seed + 1000)
+    t = torch.randn((w.B, w.H, w.L, w.d), generator=g, device=dev, dtype=torch.float32)
+    return t.to(torch_dtype(w.dtype))
+
+
 def small(name: str, B: int, H: int, L: int, block: int, r: int, dtype: str = "bf16",
           d: int = 64, value_scale: float = 1.0, pad: str = "none", valid_len: int = 0,
           pad_lo_blocks: int = 0, pad_hi_blocks: int = 0, outlier_frac: float = 0.0,

@@ -21,7 +21,8 @@ import pytest
 import torch
 
 from block_sparse_long_bigbird_amd import binding as bb
-from block_sparse_long_bigbird_amd.workloads import WORKLOADS, make_dout, make_inputs, small
+from block_sparse_long_bigbird_amd.workloads import (WORKLOADS, make_dout, make_dout_device, make_inputs,
+                                                      make_inputs_device, small)
 from oracle import attention_backward, attention_forward, attention_lse
 
 pytestmark = pytest.mark.gpu
@@ -232,3 +233,40 @@ def test_backward_pathx_sampled_unit(dev):
     # padded keys get no gradient
     valid = int(pad[0].sum())
     assert np.abs(got[1][0, :, valid:]).max() == 0.0 and np.abs(got[2][0, :, valid:]).max() == 0.0
+
+
+def test_backward_tensors_over_4gib_sampled_units(dev):
+    """64-bit addressing in both passes and the reduce: q, k, v, out, dout and
+    the three gradients of 4.25 GiB each, past 2^32 bytes (B 64, H 17,
+    L 32768, block 128, r 4), drawn on the device.  Gradients scanned for NaN
+    on the device; the first and the last (batch, head) compared in full with
+    the oracle."""
+    w = small("big_bwd_B64_H17_L32768_bs128", B=64, H=17, L=32768, block=128, r=4,
+              value_scale=0.125, data_seed=35)
+    assert w.B * w.H * w.L * w.d * 2 > 2**32
+    q, k, v = make_inputs_device(w, dev)
+    g = make_dout_device(w, dev)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    dri = torch.from_numpy(ri).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+    ws = bb.alloc_workspace(w.B, w.H, w.L, w.d, w.block, dev)
+    say(f"  forward+lse {w.name} ({q.numel() * 2 / 2**30:.2f} GiB per tensor)")
+    bb.bb_attn_forward_lse(q, k, v, None, dri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws, lse)
+    off, rows = bb.bb_rand_idx_invert(ri, w.H, w.L, w.block, w.r)
+    gq, gk, gv = (torch.full_like(q, float("nan")) for _ in range(3))
+    n = bb.bb_attn_backward_workspace_bytes(w.B, w.H, w.L, w.d, w.block)
+    bws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
+    say(f"  backward {w.name}")
+    bb.bb_attn_backward(q, k, v, None, dri, torch.from_numpy(off).to(dev), torch.from_numpy(rows).to(dev),
+                        w.B, w.H, w.L, w.d, w.block, w.r, out, g, lse, gq, gk, gv, bws)
+    torch.cuda.synchronize()
+    for name, t in (("dq", gq), ("dk", gk), ("dv", gv)):
+        assert not torch.isnan(t).any().item(), f"unwritten (NaN) {name}"
+    for b, h in [(0, 0), (w.B - 1, w.H - 1)]:
+        def sub(t):
+            return f64(t[b:b + 1, h:h + 1].cpu())
+        say(f"  oracle unit ({b}, {h})")
+        exp = attention_backward(sub(q), sub(k), sub(v), None, ri[h:h + 1], w.block, sub(g))
+        got = [t[b:b + 1, h:h + 1].float().cpu().numpy() for t in (gq, gk, gv)]
+        check_grads(got, exp, dtype=w.dtype)
