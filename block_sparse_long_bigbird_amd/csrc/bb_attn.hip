@@ -1793,8 +1793,8 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
 //   W: [N][K], the [out][in] layout of a linear layer.
 //   C: MODE 0 q, k and v in the attention's layout [B][H][L][64] (columns
 //      n of [q | k | v], N = 3*hidden); MODE 1 y [M][N].
-// Workgroup tile 64 WMW rows of A x 64 SN rows of W, with 2 WMW waves of
-// 64 x 32 SN (2 x SN subtiles of 32 x 32 each); K in steps of 64 through a
+// Workgroup tile 32 SMW WMW rows of A x 64 SN rows of W, with 2 WMW waves of
+// 32 SMW x 32 SN (SMW x SN subtiles of 32 x 32 each); K in steps of 64 through a
 // two-stage LDS ring filled by the same DMA as the attention.  Computed
 // transposed (C^T = W A^T): lane = row of A, 16 accumulators = 2 runs of 8
 // consecutive columns, so the epilogue writes 16-byte runs with the bias
@@ -1821,10 +1821,11 @@ __device__ __forceinline__ void dma16x2(gchar_ptr base, uint32_t o0, uint32_t o1
       : "memory", "m0");
 }
 
-template <int MODE, int WMW, int SN>
-__global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(2))) bb_proj_kernel(ProjArgs g) {
+template <int MODE, int WMW, int SMW, int SN>
+__global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(SMW > 2 ? 1 : 2)))
+bb_proj_kernel(ProjArgs g) {
   constexpr int NW = 2 * WMW;                      // waves: WMW along A rows x 2 along W rows
-  constexpr int TM = 64 * WMW, TN = 64 * SN;       // rows of A and of W per tile
+  constexpr int TM = 32 * SMW * WMW, TN = 64 * SN;  // rows of A and of W per tile
   constexpr int AB = TM * 128, SB = AB + TN * 128;  // bytes per stage (128-byte rows): A part, whole
   constexpr int NA = AB / 1024 / NW, NWI = TN * 128 / 1024 / NW;   // DMAs per wave per stage
   static_assert(NA % 2 == 0 && NA * NW * 1024 == AB && NWI * NW * 1024 == TN * 128, "DMAs split evenly");
@@ -1895,11 +1896,11 @@ __global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(
     if constexpr (NWI % 2 == 1)
       dma16x1(wb, wo[NWI - 1], __builtin_amdgcn_readfirstlane(base + wmo[NWI - 1]));
   };
-  f32x16 acc[SN][2];
+  f32x16 acc[SN][SMW];
 #pragma unroll
   for (int x = 0; x < SN; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < SMW; ++y)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
   issue(0, 0);
@@ -1912,10 +1913,10 @@ __global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(
     const char* lw = la + AB;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      u32x4 bop[2], aop[SN];
+      u32x4 bop[SMW], aop[SN];
 #pragma unroll
-      for (int ms = 0; ms < 2; ++ms) {
-        const int row = wm * 64 + ms * 32 + j;
+      for (int ms = 0; ms < SMW; ++ms) {
+        const int row = wm * (32 * SMW) + ms * 32 + j;
         bop[ms] = *reinterpret_cast<const u32x4*>(la + row * 128 + (((2 * x + gh) ^ (row & 7)) << 4));
       }
 #pragma unroll
@@ -1926,7 +1927,7 @@ __global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int ns = 0; ns < SN; ++ns)
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
+        for (int ms = 0; ms < SMW; ++ms)
           acc[ns][ms] = mfma_qk(aop[ns], bop[ms], acc[ns][ms], static_cast<__bf16*>(nullptr));
     }
   }
@@ -1934,8 +1935,8 @@ __global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int ns = 0; ns < SN; ++ns)
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const int m = m0 + wm * 64 + ms * 32 + j;
+    for (int ms = 0; ms < SMW; ++ms) {
+      const int m = m0 + wm * (32 * SMW) + ms * 32 + j;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int n = n0 + wn * (32 * SN) + ns * 32 + 16 * h + 8 * gh;
@@ -1963,15 +1964,14 @@ __global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(
 }
 
 // Launch C = A W^T + bias for one projection: tiles of 128 rows of A by 192
-// rows of W where N allows (3 hidden always does), else 128.  (Tiles of 256
-// rows of A, one 8-wave workgroup per CU, measured within noise of these.)
+// rows of W where N allows (3 hidden always does), else 128.
 template <int MODE>
 void launch_proj(const ProjArgs& a, hipStream_t s) {
   if (a.N % 192 == 0)
-    hipLaunchKernelGGL((bb_proj_kernel<MODE, 2, 3>), dim3(static_cast<unsigned>((a.M / 128) * (a.N / 192))),
+    hipLaunchKernelGGL((bb_proj_kernel<MODE, 2, 2, 3>), dim3(static_cast<unsigned>((a.M / 128) * (a.N / 192))),
                        dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((bb_proj_kernel<MODE, 2, 2>), dim3(static_cast<unsigned>((a.M / 128) * (a.N / 128))),
+    hipLaunchKernelGGL((bb_proj_kernel<MODE, 2, 2, 2>), dim3(static_cast<unsigned>((a.M / 128) * (a.N / 128))),
                        dim3(256), 0, s, a);
 }
 
