@@ -1772,8 +1772,13 @@ __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
   }
 }
 
+// (bf16, block 64: a register budget of 2 waves per SIMD; the kernel then
+// allocates 168 registers without spilling, which still gives 3 waves per
+// SIMD -- a budget of 3 made the compiler fit 168 with 4 spills at the unit
+// boundaries, 1.6% slower.  Block 128 keeps the budget of 3: with 2 its padded
+// form grows to 221 registers, 2 waves per SIMD.)
 template <typename T, int BS, bool HAS_PAD>
-__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : (BS == 64 ? 1 : 2)))) bb_bwd_dq_kernel(BwdArgs, int n_units) {
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 64 ? 2 : 3) : (BS == 64 ? 1 : 2)))) bb_bwd_dq_kernel(BwdArgs, int n_units) {
   run_dq<T, BS, HAS_PAD>(n_units);
 }
 template <typename T, int BS, bool HAS_PAD>
