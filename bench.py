@@ -58,6 +58,7 @@ PEAK_HBM_GBPS = 8000.0
 LLC_BYTES = 256 * 2**20
 COPY_BYTES = 512 * 2**20                        # copy-kernel calibration size
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_long_bigbird_amd", "csrc", "bb_attn.hip")
+BUILD_SCRIPT = os.path.join(ROOT, "block_sparse_long_bigbird_amd", "build.py")
 PROFILES = os.path.join(ROOT, "profiles")
 MAIN_KERNEL = "bb_fused_kernel"
 
@@ -91,11 +92,14 @@ FORWARD_END = b"// =============================================================
 
 
 def source_sha256() -> str:
-    """sha256 of the forward part of the kernel source (up to FORWARD_END)."""
+    """sha256 of the forward part of the kernel source (up to FORWARD_END)
+    followed by the build script (its compiler flags shape the same kernel)."""
     with open(KERNEL_SRC, "rb") as f:
         text = f.read()
     cut = text.find(FORWARD_END)
-    return hashlib.sha256(text if cut < 0 else text[:cut]).hexdigest()
+    with open(BUILD_SCRIPT, "rb") as f:
+        build = f.read()
+    return hashlib.sha256((text if cut < 0 else text[:cut]) + build).hexdigest()
 
 
 def traffic_path(workload: str) -> str:

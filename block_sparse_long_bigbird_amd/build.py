@@ -43,6 +43,10 @@ def build(verbose: bool = False) -> str:
         # inputs are finite (documented in bb_attn.h): no NaN quieting before
         # every max of the row-max reductions
         "-fno-honor-nans",
+        # the scheduler's AMDGPU-specific register-pressure trackers: a better
+        # schedule for the two backward passes (3.5% on the backward call),
+        # the forward unchanged in speed
+        "-mllvm", "-amdgpu-use-amdgpu-trackers",
         os.path.join(CSRC, "bb_attn.hip"),
         os.path.join(CSRC, "bb_adjacency.cpp"),
         "-o", tmp,
