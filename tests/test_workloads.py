@@ -1,0 +1,56 @@
+"""The seeded input recipe (CPU only): what the workload generator promises
+about its draws, so a change to it shows up here rather than as a shifted
+benchmark or parity input."""
+
+import numpy as np
+import torch
+
+from block_sparse_long_bigbird_amd.workloads import WORKLOADS, draw, make_inputs, small
+
+
+def test_draws_are_reproducible_and_seed_dependent():
+    w = small("w", B=2, H=2, L=8 * 64, block=64, r=2, pad="scattered", data_seed=5)
+    a, b = draw(w), draw(w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    c = draw(small("w", B=2, H=2, L=8 * 64, block=64, r=2, pad="scattered", data_seed=6))
+    assert not np.array_equal(a[0], c[0]) and not np.array_equal(a[3], c[3])
+
+
+def test_scattered_mask_has_its_own_stream():
+    # q, k, v are the same draws whatever the pad mode
+    kw = dict(B=2, H=2, L=8 * 64, block=64, r=2, data_seed=7)
+    q0, k0, v0, _ = draw(small("a", pad="none", **kw))
+    q1, k1, v1, pad = draw(small("b", pad="scattered", **kw))
+    assert np.array_equal(q0, q1) and np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    assert pad.dtype == np.uint8 and set(np.unique(pad)) <= {0, 1}
+
+
+def test_scattered_mask_shape():
+    w = small("w", B=4, H=1, L=64 * 64, block=64, r=3, pad="scattered", data_seed=8)
+    pad = draw(w)[3]
+    span = 3 * w.block // 2
+    for b in range(w.B):
+        z = np.concatenate([[1], pad[b], [1]])
+        edges = np.flatnonzero(np.diff(z))            # starts and ends of zero runs
+        longest = (edges[1::2] - edges[0::2]).max()
+        assert longest >= span                         # the padded span of 1.5 blocks
+    assert abs(pad.mean() - 0.7 * (1 - span / w.L)) < 0.02
+
+
+def test_per_sequence_block_padding():
+    w = WORKLOADS["base_B4_H12_L4096_pad"]
+    pad = draw(w)[3]
+    valid = pad.sum(axis=1)
+    assert np.all(valid % w.block == 0)
+    assert np.all((valid >= w.pad_lo_blocks * w.block) & (valid <= w.pad_hi_blocks * w.block))
+    for b in range(w.B):                              # a prefix of valid tokens
+        assert np.all(pad[b, : valid[b]] == 1) and np.all(pad[b, valid[b]:] == 0)
+
+
+def test_inputs_rounded_once_to_the_compute_dtype():
+    w = small("w", B=1, H=2, L=4 * 64, block=64, r=0, value_scale=0.125, data_seed=9)
+    q, _, _, _ = make_inputs(w)
+    assert q.dtype == torch.bfloat16
+    raw = draw(w)[0]
+    assert torch.equal(q, torch.from_numpy(raw).to(torch.bfloat16))
