@@ -57,6 +57,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBPS = 8000.0
 LLC_BYTES = 256 * 2**20
 COPY_BYTES = 512 * 2**20                        # copy-kernel calibration size
+MFMA_CALIB_N = 8192                             # bf16 GEMM calibration: 2 n^3 FLOPs
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_long_bigbird_amd", "csrc", "bb_attn.hip")
 BUILD_SCRIPT = os.path.join(ROOT, "block_sparse_long_bigbird_amd", "build.py")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -196,63 +197,137 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, command: str) -> 
     print("\n".join(lines))
 
 
-def cpu_baseline(w, inputs, ri, budget_s: float):
-    """Time the fp64 oracle on (b, h) units until `budget_s` is spent (at least one unit)."""
-    from threadpoolctl import threadpool_info
-
-    from oracle import attention_forward
-    q, k, v, pad = inputs
-    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
-    pd = None if pad is None else pad.numpy()
+def _oracle_waves(w, run_units, budget_s: float):
+    """Run the oracle on (b, h) units in waves of one unit per worker thread
+    until `budget_s` is spent (at least one wave).  Returns (units done, seconds,
+    workers)."""
+    from oracle.parallel import host_workers
     units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    n = host_workers()
     done = 0
     t0 = time.perf_counter()
-    for bh in units:
-        attention_forward(qd, kd, vd, pd, ri, w.block, units=[bh])
-        done += 1
+    while done < len(units):
+        run_units(units[done:done + n], n)
+        done = min(len(units), done + n)
         if time.perf_counter() - t0 >= budget_s:
             break
-    el = time.perf_counter() - t0
-    frac = done / len(units)
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return done, time.perf_counter() - t0, n
+
+
+def _baseline_fields(w, done, el, n, flops_per_job, what):
+    frac = done / (w.B * w.H)
     return {
-        "value": round(useful_flops(w) * frac / el / 1e12, 6),
+        "value": round(flops_per_job * frac / el / 1e12, 6),
         "unit": "TFLOP/s",
         "tokens_per_s": round(w.tokens * frac / el, 1),
-        "cores": int(threads),
+        "cores": int(n),
         "kind": "oracle",
-        "sample": f"{done} of {len(units)} (batch, head) units of {w.name}, all {w.L} query rows each, "
-                  f"fp64 numpy, {el:.1f} s",
+        "sample": f"{done} of {w.B * w.H} (batch, head) units of {w.name}, {what} of all {w.L} query rows "
+                  f"each, fp64 numpy, {el:.1f} s",
+        "parallelism": f"{n} worker threads over (batch, head) units, BLAS 1 thread each",
+        "host_cpus_visible": len(os.sched_getaffinity(0)),
     }
+
+
+def mfma_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"mfma_counters_{MAIN_KERNEL}_{workload}.txt")
+
+
+def pmc_mfma_summary(csv_path: str, workload: str, command: str) -> None:
+    """Turn one rocprofv3 --pmc CSV (MFMA, VALU, SALU and clock counters of a
+    bench run with --mfma-calibration) into the committed MFMA summary.
+
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 is converted to FLOPs with the factor that
+    makes it read exactly 2 n^3 for the calibration GEMM (torch.matmul, n =
+    MFMA_CALIB_N); the kernel's duration is End - Start of each dispatch;
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so GUI_ACTIVE / 8 / duration is
+    the engine clock during the kernel and SQ_VALU_MFMA_BUSY_CYCLES over
+    (SIMDs x GUI_ACTIVE / 8) the fraction of SIMD cycles the MFMA pipe is busy.
+    """
+    import csv
+    import statistics
+
+    from block_sparse_long_bigbird_amd.workloads import WORKLOADS
+    w = WORKLOADS[workload]
+    disp = {}
+    for row in csv.DictReader(open(csv_path)):
+        key = (row["Dispatch_Id"], row["Kernel_Name"])
+        d = disp.setdefault(key, {"dur_ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+        d[row["Counter_Name"]] = float(row["Counter_Value"])
+
+    def select(match):
+        return [d for (_, name), d in disp.items() if match(name)]
+
+    gemm = select(lambda n: n.startswith("Cijk") or "gemm" in n.lower())
+    kern = select(lambda n: MAIN_KERNEL in n)
+    if not gemm or not kern:
+        raise SystemExit("need dispatches of the calibration GEMM and of the main kernel")
+    n = MFMA_CALIB_N
+    flop_per_mop = statistics.median(2.0 * n ** 3 / d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in gemm)
+    simds = 256 * 4
+
+    def stats(ds):
+        dur = statistics.mean(d["dur_ns"] for d in ds)
+        flops = statistics.mean(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds) * flop_per_mop
+        gui = statistics.mean(d["GRBM_GUI_ACTIVE"] for d in ds) / 8
+        busy = statistics.mean(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds)
+        return dur, flops, gui, busy
+
+    kd, kf, kg, kb = stats(kern)
+    gd, gf, gg, gb = stats(gemm)
+    useful = useful_flops(w)
+    waves = statistics.mean(d.get("SQ_WAVES", 0.0) for d in kern)
+    lines = [
+        f"# MFMA counters of {MAIN_KERNEL} on {workload} (rocprofv3 --pmc, one run)",
+        f"command: {command}",
+        f"source_sha256: {source_sha256()}",
+        f"dispatches: {len(kern)} of the kernel, {len(gemm)} of the calibration GEMM (bf16, n = {n})",
+        f"flop_per_mops_bf16: {flop_per_mop:.3f}   (2 n^3 / SQ_INSTS_VALU_MFMA_MOPS_BF16 of the GEMM)",
+        f"kernel_duration_us: {kd / 1e3:.3f}   (mean End - Start)",
+        f"kernel_mfma_flop_per_launch: {kf:.6g}   (counter)",
+        f"useful_flop_per_launch: {useful}   (algorithmic: 4 d per attended pair)",
+        f"counter_over_useful: {kf / useful:.6f}",
+        f"achieved_mfma_tflops: {kf / kd / 1e3:.1f}   (counter FLOPs / duration)",
+        f"achieved_frac_of_peak: {kf / kd / 1e3 / PEAK_TFLOPS['bf16']:.4f}   (peak {PEAK_TFLOPS['bf16']} TFLOP/s at 2.4 GHz)",
+        f"engine_clock_ghz: {kg / kd:.3f}   (GRBM_GUI_ACTIVE / 8 XCDs / duration)",
+        f"mfma_busy_frac: {kb / (simds * kg):.4f}   (SQ_VALU_MFMA_BUSY_CYCLES / ({simds} SIMDs x cycles))",
+        f"valu_insts_per_launch: {statistics.mean(d['SQ_INSTS_VALU'] for d in kern):.0f}",
+        f"salu_insts_per_launch: {statistics.mean(d['SQ_INSTS_SALU'] for d in kern):.0f}",
+        f"mfma_insts_per_launch: {statistics.mean(d['SQ_INSTS_MFMA'] for d in kern):.0f}",
+        f"gemm_duration_us: {gd / 1e3:.1f}",
+        f"gemm_achieved_tflops: {gf / gd / 1e3:.1f}",
+        f"gemm_engine_clock_ghz: {gg / gd:.3f}",
+        f"gemm_mfma_busy_frac: {gb / (simds * gg):.4f}",
+    ]
+    if waves:
+        lines.append(f"waves_per_launch: {waves:.0f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(mfma_path(workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_baseline(w, inputs, ri, budget_s: float):
+    """Time the fp64 oracle on (b, h) units until `budget_s` is spent."""
+    from oracle.parallel import forward_units
+    q, k, v, pad = inputs
+    qd, kd, vd = (t.float().numpy() for t in (q, k, v))
+    pd = None if pad is None else pad.numpy()
+    done, el, n = _oracle_waves(
+        w, lambda units, n: forward_units(qd, kd, vd, pd, ri, w.block, units=units, workers=n), budget_s)
+    return _baseline_fields(w, done, el, n, useful_flops(w), "forward")
 
 
 def cpu_baseline_backward(w, inputs, dout, ri, budget_s: float):
     """Time the fp64 oracle's backward on (b, h) units until `budget_s` is spent."""
-    from threadpoolctl import threadpool_info
-
-    from oracle import attention_backward
+    from oracle.parallel import backward_units
     q, k, v, pad = inputs
-    qd, kd, vd, gd = (t.double().numpy() for t in (q, k, v, dout))
+    qd, kd, vd, gd = (t.float().numpy() for t in (q, k, v, dout))
     pd = None if pad is None else pad.numpy()
-    units = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done = 0
-    t0 = time.perf_counter()
-    for bh in units:
-        attention_backward(qd, kd, vd, pd, ri, w.block, gd, units=[bh])
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    frac = done / len(units)
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    return {
-        "value": round(2.5 * useful_flops(w) * frac / el / 1e12, 6),
-        "unit": "TFLOP/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{done} of {len(units)} (batch, head) units of {w.name}, backward of all {w.L} rows "
-                  f"each, fp64 numpy, {el:.1f} s",
-    }
+    done, el, n = _oracle_waves(
+        w, lambda units, n: backward_units(qd, kd, vd, pd, ri, w.block, gd, units=units, workers=n),
+        budget_s)
+    return _baseline_fields(w, done, el, n, 2.5 * useful_flops(w), "backward")
 
 
 def bench_layer(args, w, dev):
@@ -415,13 +490,20 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed passes, run a plain device copy of a known size "
                          "(reference point for the HBM byte counters)")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="after the timed passes, run a plain bf16 GEMM of a known size "
+                         "(reference point for the MFMA counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--pmc-mfma-summary", metavar="COUNTER_CSV")
     ap.add_argument("--command", default="", help="profiling command recorded by --pmc-summary")
     ap.add_argument("--pass", dest="which", choices=["forward", "backward", "layer"], default="forward")
     args = ap.parse_args()
 
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.command)
+        return
+    if args.pmc_mfma_summary:
+        pmc_mfma_summary(args.pmc_mfma_summary, args.workload, args.command)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -508,6 +590,16 @@ def main():
         torch.cuda.synchronize()
         for _ in range(3):
             dst.copy_(src)
+        torch.cuda.synchronize()
+    if args.mfma_calibration:
+        # a plain bf16 GEMM of known size (torch.matmul): the reference point that
+        # turns MFMA counter readings into FLOPs
+        n = MFMA_CALIB_N
+        a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.matmul(a, b)
         torch.cuda.synchronize()
 
     flops = useful_flops(w)

@@ -113,7 +113,15 @@ def bb_rand_idx_build(seed: int, H: int, L: int, block: int, r: int) -> np.ndarr
                                  out.ctypes.data if out.size else None)
     if st != BB_OK:
         raise BBError(st, "bb_rand_idx_build")
+    _check_built(out, H, L, block, r)
     return out
+
+
+def _check_built(table, H, L, block, r):
+    """Every table the binding builds goes through the checker too."""
+    st = bb_rand_idx_check(table, H, L, block, r)
+    if st != BB_OK:
+        raise BBError(st, "bb_rand_idx_check")
 
 
 def bb_rand_idx_build_capped(seed: int, H: int, L: int, block: int, r: int, last_idx: int) -> np.ndarray:
@@ -124,6 +132,7 @@ def bb_rand_idx_build_capped(seed: int, H: int, L: int, block: int, r: int, last
                                         out.ctypes.data if out.size else None)
     if st != BB_OK:
         raise BBError(st, "bb_rand_idx_build_capped")
+    _check_built(out, H, L, block, r)
     return out
 
 
@@ -173,43 +182,150 @@ def _check_device_tensor(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
+# ----------------------------------------------------------------- checks ---
+# The C ABI takes raw pointers, so a tensor of the wrong dtype or shape would be
+# read or written past its end.  Every wrapper below checks what the pointers
+# stand for against the sizes it passes, before anything reaches the library:
+# a mismatch raises ValueError and nothing is launched.
+
+def _expect(name, t, shape, dtypes):
+    """t must have exactly `shape` and one of `dtypes` (torch dtypes)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        names = " or ".join(str(d) for d in dtypes)
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {names}")
+
+
+def _same_dtype_as(first, t_name_pairs):
+    for name, t in t_name_pairs:
+        if t is not None and t.dtype != first.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, but q has {first.dtype}: "
+                             "q, k, v and the outputs share one dtype")
+
+
+def _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r):
+    """pad_mask: None or uint8/bool [B, L]; rand_idx: int32 [H, L/block - 2, r]
+    (None only when r == 0).  Returns True when the table's contents are to be
+    checked too (_check_table_contents, after the device checks)."""
+    import torch
+    if pad_mask is not None:
+        _expect("pad_mask", pad_mask, (B, L), (torch.uint8, torch.bool))
+    if block <= 0 or L % block != 0 or L // block < 3 or r < 0:
+        return False                     # sizes the library rejects (BB_ERR_SHAPE)
+    nb = L // block
+    if rand_idx is None:
+        if r > 0 and B * H > 0:
+            raise ValueError(f"rand_idx is required when r = {r} > 0")
+        return False
+    _expect("rand_idx", rand_idx, (H, nb - 2, r), (torch.int32,))
+    return True
+
+
+def _check_rand_idx_contents(rand_idx, H, L, block, r):
+    """Run the library's table checker (bb_rand_idx_check) on a device table.
+
+    Once per table: the result is remembered on the tensor object together
+    with its version counter (bumped by every in-place write through torch),
+    so later calls with the same, unmodified table cost nothing.  The first
+    check copies the table to the host and synchronises; inside a HIP graph
+    capture that is impossible, so an unchecked table raises there (check it
+    before capturing: upload_rand_idx, or one eager call).  Returns the host
+    copy when it was made (the backward also checks its inverse against it).
+    """
+    import torch
+    key = (rand_idx._version, H, L, block, r)
+    if getattr(rand_idx, "_bb_checked", None) == key:
+        return None
+    if rand_idx.is_cuda and torch.cuda.is_current_stream_capturing():
+        raise ValueError("rand_idx has not been checked yet and cannot be copied to the host "
+                         "during graph capture: pass it through upload_rand_idx() or one eager "
+                         "call before capturing")
+    host = rand_idx.detach().to("cpu").numpy()
+    st = bb_rand_idx_check(host, H, L, block, r)
+    if st != BB_OK:
+        raise BBError(st, "bb_rand_idx_check")
+    rand_idx._bb_checked = key
+    return host
+
+
+def upload_rand_idx(table, H: int, L: int, block: int, r: int, device):
+    """Check a host random-block table with bb_rand_idx_check and copy it to
+    `device` as an int32 tensor [H, L/block - 2, r], marked as checked (the
+    wrappers below then accept it without copying it back).  None when r == 0."""
+    import torch
+    a = np.ascontiguousarray(np.asarray(table), dtype=np.int32)
+    st = bb_rand_idx_check(a, H, L, block, r)
+    if st != BB_OK:
+        raise BBError(st, "bb_rand_idx_check")
+    if r == 0:
+        return None
+    t = torch.from_numpy(a).to(device)
+    t._bb_checked = (t._version, H, L, block, r)
+    return t
+
+
+def _check_qkv_out(B, H, L, d, q, rest):
+    """q, k, v and the outputs: [B, H, L, d], one dtype (q's).  An unsupported q
+    dtype is left to the library (BB_ERR_DTYPE)."""
+    _expect("q", q, (B, H, L, d), (q.dtype,))
+    _same_dtype_as(q, rest)
+    for name, t in rest:
+        _expect(name, t, (B, H, L, d), (q.dtype,))
+
+
 def bb_attn_forward(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int,
                     r: int, out, workspace, stream=None, flags: int = BB_LAUNCH_FUSED,
                     events=None) -> None:
     """Enqueue the forward on `stream` (default: torch's current stream).
 
-    q, k, v, out: device tensors [B, H, L, d] (bf16 or fp32); pad_mask: uint8
-    device tensor [B, L] or None; rand_idx: int32 device tensor [H, L/block-2, r]
-    (or None when r == 0); workspace: uint8 device tensor from alloc_workspace.
+    q, k, v, out: device tensors [B, H, L, d] (bf16 or fp32, one dtype);
+    pad_mask: uint8 (or bool) device tensor [B, L] or None; rand_idx: int32
+    device tensor [H, L/block-2, r] (None when r == 0), checked with
+    bb_rand_idx_check once per table; workspace: uint8 device tensor from
+    alloc_workspace.
+    With the default flags this calls the library's bb_attn_forward; other
+    flags go through bb_attn_forward_ex.
     events: optional (start, stop) pair of timing-enabled torch.cuda.Event that
     the kernel launches themselves record (bb_attn_forward_timed); each must
     have been recorded once before, so that its HIP event exists.
     """
+    _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out)))
+    table = _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("pad_mask", pad_mask),
                     ("rand_idx", rand_idx), ("workspace", workspace)):
         _check_device_tensor(name, t)
+    if table:
+        _check_rand_idx_contents(rand_idx, H, L, block, r)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if events is None:
-        st = lib().bb_attn_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
-                                      B, H, L, d, block, r, _ptr(out), _dtype_code(q),
-                                      _ptr(workspace), ws_bytes, _stream_handle(q, stream), flags)
-    else:
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx), B, H, L, d, block, r,
+            _ptr(out), _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(q, stream))
+    if events is not None:
         e0, e1 = (int(e.cuda_event) for e in events)
         if not e0 or not e1:
             raise ValueError("events must have been recorded once (their HIP events do not exist yet)")
-        st = lib().bb_attn_forward_timed(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
-                                         B, H, L, d, block, r, _ptr(out), _dtype_code(q),
-                                         _ptr(workspace), ws_bytes, _stream_handle(q, stream), flags,
-                                         e0, e1)
+        st = lib().bb_attn_forward_timed(*args, flags, e0, e1)
+    elif flags == BB_LAUNCH_FUSED:
+        st = lib().bb_attn_forward(*args)
+    else:
+        st = lib().bb_attn_forward_ex(*args, flags)
     if st != BB_OK:
         raise BBError(st, "bb_attn_forward")
 
 
 def forward(q, k, v, rand_idx, pad_mask=None, block: int = 64, out=None, workspace=None,
             stream=None, flags: int = BB_LAUNCH_FUSED):
-    """Convenience wrapper: sizes from q's shape, allocates out/workspace if not given."""
+    """Convenience wrapper: sizes from q's shape, allocates out/workspace if not
+    given.  rand_idx may be a host table (numpy, checked and uploaded here) or a
+    device tensor."""
     import torch
     B, H, L, d = q.shape
+    if rand_idx is not None and not isinstance(rand_idx, torch.Tensor):
+        table = np.asarray(rand_idx)
+        r = int(table.shape[-1]) if table.ndim == 3 else 0
+        rand_idx = upload_rand_idx(table, H, L, block, r, q.device)
     r = 0 if rand_idx is None else int(rand_idx.shape[-1])
     if out is None:
         out = torch.empty_like(q)
@@ -224,9 +340,15 @@ def bb_attn_forward_lse(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: 
                         r: int, out, workspace, lse, stream=None) -> None:
     """The forward that also writes the row log-sum-exp: lse is a float32
     device tensor [B, H, L] (natural log)."""
+    import torch
+    _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out)))
+    _expect("lse", lse, (B, H, L), (torch.float32,))
+    table = _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("pad_mask", pad_mask),
                     ("rand_idx", rand_idx), ("workspace", workspace), ("lse", lse)):
         _check_device_tensor(name, t)
+    if table:
+        _check_rand_idx_contents(rand_idx, H, L, block, r)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().bb_attn_forward_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
                                    B, H, L, d, block, r, _ptr(out), _dtype_code(q),
@@ -258,11 +380,20 @@ def bb_attn_backward(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B: int, H: 
                      d: int, block: int, r: int, out, dout, lse, dq, dk, dv, workspace,
                      stream=None) -> None:
     """Enqueue the backward on `stream` (default: torch's current stream).
-    inv_off / inv_rows: int32 device tensors from bb_rand_idx_invert."""
+    inv_off / inv_rows: int32 device tensors from bb_rand_idx_invert of the same
+    table (checked against it once per table, as rand_idx itself)."""
+    import torch
+    _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
+                                   ("dk", dk), ("dv", dv)))
+    _expect("lse", lse, (B, H, L), (torch.float32,))
+    table = _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r)
+    _check_inverse_shapes(inv_off, inv_rows, H, L, block, r)
     for name, t in (("q", q), ("k", k), ("v", v), ("pad_mask", pad_mask), ("rand_idx", rand_idx),
                     ("inv_off", inv_off), ("inv_rows", inv_rows), ("out", out), ("dout", dout),
                     ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv), ("workspace", workspace)):
         _check_device_tensor(name, t)
+    host = _check_rand_idx_contents(rand_idx, H, L, block, r) if table else None
+    _check_inverse(rand_idx, host, inv_off, inv_rows, H, L, block, r)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().bb_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
                                 _ptr(inv_off), _ptr(inv_rows), B, H, L, d, block, r, _ptr(out),
@@ -273,16 +404,63 @@ def bb_attn_backward(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B: int, H: 
         raise BBError(st, "bb_attn_backward")
 
 
+def _check_inverse_shapes(inv_off, inv_rows, H, L, block, r):
+    """inv_off int32 [H, nb+1]; inv_rows int32 [H*(nb-2)*r] (may be None when r == 0)."""
+    import torch
+    if block <= 0 or L % block != 0 or L // block < 3 or r < 0:
+        return
+    nb = L // block
+    _expect("inv_off", inv_off, (H, nb + 1), (torch.int32,))
+    if r > 0 or inv_rows is not None:
+        _expect("inv_rows", inv_rows, (H * (nb - 2) * r,), (torch.int32,))
+
+
+def _check_inverse(rand_idx, host, inv_off, inv_rows, H, L, block, r):
+    """inv_off / inv_rows equal to bb_rand_idx_invert of the table: checked once per
+    (table, inverse) versions, like the table.  `host`: the table's host copy when
+    it was just made."""
+    import torch
+    if rand_idx is None or inv_off is None or block <= 0 or L % block != 0 or L // block < 3:
+        return
+    key = (rand_idx._version, inv_off._version, None if inv_rows is None else inv_rows._version,
+           H, L, block, r)
+    if getattr(inv_off, "_bb_checked", None) == key:
+        return
+    if inv_off.is_cuda and torch.cuda.is_current_stream_capturing():
+        raise ValueError("inv_off / inv_rows have not been checked yet and cannot be copied to the "
+                         "host during graph capture: make one eager call before capturing")
+    if host is None:
+        host = rand_idx.detach().to("cpu").numpy()
+    off, rows = bb_rand_idx_invert(host, H, L, block, r)
+    if not np.array_equal(inv_off.detach().to("cpu").numpy(), off) or (
+            inv_rows is not None and not np.array_equal(inv_rows.detach().to("cpu").numpy(), rows)):
+        raise ValueError("inv_off / inv_rows are not bb_rand_idx_invert of rand_idx")
+    inv_off._bb_checked = key
+
+
 def bb_layer_workspace_bytes(B: int, L: int, hidden: int, H: int, block: int) -> int:
     return int(lib().bb_layer_workspace_bytes(B, L, hidden, H, block))
 
 
 def bb_layer_forward(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, B: int, L: int, hidden: int, H: int,
                      block: int, r: int, y, workspace, stream=None) -> None:
-    """Enqueue the attention layer (projections + block-sparse attention)."""
+    """Enqueue the attention layer (projections + block-sparse attention).
+    x, y: bf16 [B, L, hidden]; w_qkv: bf16 [3*hidden, hidden]; b_qkv: float32
+    [3*hidden]; w_o: bf16 [hidden, hidden]; b_o: float32 [hidden]."""
+    import torch
+    _expect("x", x, (B, L, hidden), (x.dtype,))
+    _same_dtype_as(x, (("w_qkv", w_qkv), ("w_o", w_o), ("y", y)))
+    _expect("w_qkv", w_qkv, (3 * hidden, hidden), (x.dtype,))
+    _expect("b_qkv", b_qkv, (3 * hidden,), (torch.float32,))
+    _expect("w_o", w_o, (hidden, hidden), (x.dtype,))
+    _expect("b_o", b_o, (hidden,), (torch.float32,))
+    _expect("y", y, (B, L, hidden), (x.dtype,))
+    table = _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r)
     for name, t in (("x", x), ("w_qkv", w_qkv), ("b_qkv", b_qkv), ("w_o", w_o), ("b_o", b_o),
                     ("pad_mask", pad_mask), ("rand_idx", rand_idx), ("y", y), ("workspace", workspace)):
         _check_device_tensor(name, t)
+    if table:
+        _check_rand_idx_contents(rand_idx, H, L, block, r)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().bb_layer_forward(_ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_o), _ptr(b_o), _ptr(pad_mask),
                                 _ptr(rand_idx), B, L, hidden, H, block, r, _ptr(y), _dtype_code(x),

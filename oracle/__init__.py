@@ -7,6 +7,7 @@ never does.
 from .bigbird_oracle import (  # noqa: F401
     MASK_OFFSET,
     attention_backward,
+    attention_backward_unit,
     attention_forward,
     attention_lse,
     attention_probs,

@@ -252,32 +252,40 @@ def attention_backward(q, k, v, pad_mask, rand_idx, block: int, dout, units=None
     dv = np.full((B, H, L, d), np.nan, dtype=np.float64)
     if units is None:
         units = [(b, h) for b in range(B) for h in range(H)]
-    scale = 1.0 / math.sqrt(d)
     for b, h in units:
         adj = block_adjacency(rand_idx[h], nb)
         pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
-        qb = np.asarray(q[b, h], np.float64)
-        kb = np.asarray(k[b, h], np.float64)
-        vb = np.asarray(v[b, h], np.float64)
-        gb = np.asarray(dout[b, h], np.float64)
-        dk_acc = np.zeros((L, d))
-        dv_acc = np.zeros((L, d))
-        for r0 in range(0, L, row_group):
-            rows = np.arange(r0, min(L, r0 + row_group))
-            s = _logits_rows(qb, kb, pad_b, adj, block, rows)
-            s = s - s.max(axis=1, keepdims=True)
-            p = np.exp(s)
-            p = p / p.sum(axis=1, keepdims=True)          # P, rows of the softmax
-            o = p @ vb                                     # O
-            g = gb[rows]                                   # dO
-            dv_acc += p.T @ g                              # dV = P^T dO
-            dp = g @ vb.T                                  # dP = dO V^T
-            dsum = (g * o).sum(axis=1, keepdims=True)      # D = rowsum(dO * O)
-            ds = p * (dp - dsum)                           # dS = P (dP - D)
-            dq[b, h, rows] = (ds @ kb) * scale             # dQ = dS K / sqrt(d)
-            dk_acc += (ds.T @ qb[rows]) * scale            # dK = dS^T Q / sqrt(d)
-        dk[b, h] = dk_acc
-        dv[b, h] = dv_acc
+        dq[b, h], dk[b, h], dv[b, h] = attention_backward_unit(q[b, h], k[b, h], v[b, h], dout[b, h],
+                                                               pad_b, adj, block, row_group)
+    return dq, dk, dv
+
+
+def attention_backward_unit(q_bh, k_bh, v_bh, dout_bh, pad_b, adj, block: int, row_group: int = 4096):
+    """attention_backward for one (batch, head): q_bh, k_bh, v_bh, dout_bh [L, d];
+    pad_b [L] or None; adj the head's block adjacency.  Returns (dq, dk, dv), fp64 [L, d]."""
+    qb = np.asarray(q_bh, np.float64)
+    kb = np.asarray(k_bh, np.float64)
+    vb = np.asarray(v_bh, np.float64)
+    gb = np.asarray(dout_bh, np.float64)
+    L, d = kb.shape
+    scale = 1.0 / math.sqrt(d)
+    dq = np.empty((L, d))
+    dk = np.zeros((L, d))
+    dv = np.zeros((L, d))
+    for r0 in range(0, L, row_group):
+        rows = np.arange(r0, min(L, r0 + row_group))
+        s = _logits_rows(qb, kb, pad_b, adj, block, rows)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)          # P, rows of the softmax
+        o = p @ vb                                     # O
+        g = gb[rows]                                   # dO
+        dv += p.T @ g                                  # dV = P^T dO
+        dp = g @ vb.T                                  # dP = dO V^T
+        dsum = (g * o).sum(axis=1, keepdims=True)      # D = rowsum(dO * O)
+        ds = p * (dp - dsum)                           # dS = P (dP - D)
+        dq[rows] = (ds @ kb) * scale                   # dQ = dS K / sqrt(d)
+        dk += (ds.T @ qb[rows]) * scale                # dK = dS^T Q / sqrt(d)
     return dq, dk, dv
 
 

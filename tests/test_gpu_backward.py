@@ -15,6 +15,7 @@ every output is scanned for NaN.
 """
 
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -24,6 +25,7 @@ from block_sparse_long_bigbird_amd import binding as bb
 from block_sparse_long_bigbird_amd.workloads import (WORKLOADS, make_dout, make_dout_device, make_inputs,
                                                       make_inputs_device, small)
 from oracle import attention_backward, attention_forward, attention_lse
+from oracle.parallel import backward_units
 
 pytestmark = pytest.mark.gpu
 
@@ -174,20 +176,20 @@ def test_backward_matches_oracle(dev, w):
     check_grads(got, exp, dtype=w.dtype)
 
 
-def test_backward_full_size_sampled_units(dev):
-    """The benchmark shape (4 x 12 x 4096, padded): every output scanned for
-    NaN, three (batch, head) units compared in full with the oracle."""
+def test_backward_full_size_every_output(dev):
+    """The benchmark shape (4 x 12 x 4096, padded): every gradient of every
+    (batch, head) unit compared with the oracle (units spread over host threads)."""
     w = WORKLOADS["base_B4_H12_L4096_pad"]
     inputs = make_inputs(w)
     dout = make_dout(w)
     ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
     got = run_backward(w, dev, inputs, ri, dout)
-    for a in got:
-        assert not np.isnan(a).any()
-    units = [(0, 0), (1, 7), (3, 11)]
     q, k, v, pad = inputs
-    exp = attention_backward(f64(q), f64(k), f64(v), pad.numpy(), ri, w.block, f64(dout), units=units)
-    check_grads(got, exp, units=units)
+    t0 = time.perf_counter()
+    exp = backward_units(q.float().numpy(), k.float().numpy(), v.float().numpy(), pad.numpy(), ri, w.block,
+                         dout.float().numpy())
+    say(f"  oracle on {w.B * w.H} units in {time.perf_counter() - t0:.1f} s")
+    check_grads(got, exp)
 
 
 def test_capped_random_range_forward_and_backward(dev):
@@ -213,23 +215,22 @@ def test_capped_random_range_forward_and_backward(dev):
     assert e <= 2e-2
 
 
-def test_backward_pathx_sampled_unit(dev):
+def test_backward_pathx_every_output(dev):
     """The Path-X shape (1 x 8 x 16384): blocks 240..255 are padding, the
     global key block 255 included (its dK and dV rows are zero; the padded
-    query rows follow the same rule).  Every output scanned for NaN, one
-    (batch, head) unit compared in full with the oracle."""
+    query rows follow the same rule).  Every gradient of every (batch, head)
+    unit compared with the oracle."""
     w = WORKLOADS["pathx_B1_H8_L16384_pad"]
     inputs = make_inputs(w)
     dout = make_dout(w)
     ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
     got = run_backward(w, dev, inputs, ri, dout)
-    for a in got:
-        assert not np.isnan(a).any()
-    units = [(0, 3)]
     q, k, v, pad = inputs
-    exp = attention_backward(f64(q), f64(k), f64(v), pad.numpy(), ri, w.block, f64(dout), units=units,
-                             row_group=2048)
-    check_grads(got, exp, units=units)
+    t0 = time.perf_counter()
+    exp = backward_units(q.float().numpy(), k.float().numpy(), v.float().numpy(), pad.numpy(), ri, w.block,
+                         dout.float().numpy())
+    say(f"  oracle on {w.B * w.H} units in {time.perf_counter() - t0:.1f} s")
+    check_grads(got, exp)
     # padded keys get no gradient
     valid = int(pad[0].sum())
     assert np.abs(got[1][0, :, valid:]).max() == 0.0 and np.abs(got[2][0, :, valid:]).max() == 0.0

@@ -15,6 +15,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 from scipy import stats
 
 from block_sparse_long_bigbird_amd import binding as bb
@@ -306,6 +307,16 @@ def test_capped_builder_respects_cap(lib, nb, block, r, last_idx):
     assert t.max() <= last_idx // block - 1
 
 
+@pytest.mark.parametrize("block,last_idx", [(64, 640), (64, 650), (64, 639), (1, 9)])
+def test_capped_builder_reaches_the_cap_boundary(lib, block, last_idx):
+    """The cap's boundary block (last_idx/block - 1: its last token is below last_idx) is
+    drawn, the next one never: over many heads the table's largest entry is exactly it."""
+    nb, r, H = 20, 2, 64
+    t = bb.bb_rand_idx_build_capped(11, H, nb * block, block, r, last_idx)
+    assert t.max() == last_idx // block - 1
+    assert (t == last_idx // block - 1).sum() > 0 and not (t >= last_idx // block).any()
+
+
 def test_capped_builder_without_binding_cap_is_the_plain_builder(lib):
     a = bb.bb_rand_idx_build(77, 4, 4096, 64, 3)
     for cap in (0, -5, 63 * 64, 64 * 64, 1 << 20):
@@ -366,3 +377,100 @@ def test_layer_validation_errors(lib):
     assert need == 4 * plane + lib.bb_attn_workspace_bytes(1, 4, 512, 64, 64)
     assert layer(lib, ws_bytes=need - 1) == 5
     assert layer(lib, B=0, x=0, y=0, ws=0) == 0
+
+
+# ------------------------------------------- binding checks before any launch ---
+# The wrappers check shapes and dtypes of what the raw pointers stand for, then
+# that every tensor is on the device, then the table's contents: with host
+# tensors every one of these raises before anything reaches the library.
+
+def _fwd_args(dtype=torch.bfloat16, B=2, H=3, L=10 * 64, block=64, r=2):
+    q, k, v, out = (torch.zeros(B, H, L, 64, dtype=dtype) for _ in range(4))
+    pad = torch.ones(B, L, dtype=torch.uint8)
+    ri = torch.from_numpy(bb.bb_rand_idx_build(0, H, L, block, r))
+    ws = torch.zeros(256, dtype=torch.uint8)
+    return dict(q=q, k=k, v=v, pad_mask=pad, rand_idx=ri, B=B, H=H, L=L, d=64, block=block, r=r,
+                out=out, workspace=ws)
+
+
+@pytest.mark.parametrize("change,match", [
+    (lambda a: a.update(k=a["k"].float()), "k has dtype"),
+    (lambda a: a.update(out=a["out"].float()), "out has dtype"),
+    (lambda a: a.update(v=a["v"][:, :2].contiguous()), "v has shape"),
+    (lambda a: a.update(out=a["out"][:1].contiguous()), "out has shape"),
+    (lambda a: a.update(q=a["q"][:1].contiguous()), "q has shape"),
+    (lambda a: a.update(pad_mask=a["pad_mask"].int()), "pad_mask has dtype"),
+    (lambda a: a.update(pad_mask=a["pad_mask"][:, :64].contiguous()), "pad_mask has shape"),
+    (lambda a: a.update(rand_idx=a["rand_idx"].long()), "rand_idx has dtype"),
+    (lambda a: a.update(rand_idx=a["rand_idx"][:2].contiguous()), "rand_idx has shape"),
+    (lambda a: a.update(r=3), "rand_idx has shape"),
+    (lambda a: a.update(rand_idx=None), "rand_idx is required"),
+    (lambda a: None, "must be a device tensor"),          # everything right, but host tensors
+])
+def test_forward_wrapper_rejects_mismatched_tensors(lib, change, match):
+    a = _fwd_args()
+    change(a)
+    with pytest.raises(ValueError, match=match):
+        bb.bb_attn_forward(**a)
+
+
+def test_lse_backward_layer_wrappers_reject_mismatched_tensors(lib):
+    a = _fwd_args()
+    lse = torch.zeros(a["B"], a["H"], a["L"], dtype=torch.float32)
+    with pytest.raises(ValueError, match="lse has dtype"):
+        bb.bb_attn_forward_lse(**a, lse=lse.double())
+    with pytest.raises(ValueError, match="lse has shape"):
+        bb.bb_attn_forward_lse(**a, lse=lse[:, :, :64].contiguous())
+    with pytest.raises(ValueError, match="v has dtype"):
+        bb.bb_attn_forward_lse(**{**a, "v": a["v"].float()}, lse=lse)
+    off, rows = bb.bb_rand_idx_invert(a["rand_idx"].numpy(), a["H"], a["L"], a["block"], a["r"])
+    g = {n: torch.zeros_like(a["q"]) for n in ("dout", "dq", "dk", "dv")}
+    bw = dict(q=a["q"], k=a["k"], v=a["v"], pad_mask=a["pad_mask"], rand_idx=a["rand_idx"],
+              inv_off=torch.from_numpy(off), inv_rows=torch.from_numpy(rows), B=a["B"], H=a["H"],
+              L=a["L"], d=64, block=64, r=a["r"], out=a["out"], lse=lse, workspace=a["workspace"], **g)
+    with pytest.raises(ValueError, match="dk has dtype"):
+        bb.bb_attn_backward(**{**bw, "dk": g["dk"].float()})
+    with pytest.raises(ValueError, match="dout has shape"):
+        bb.bb_attn_backward(**{**bw, "dout": g["dout"][:1].contiguous()})
+    with pytest.raises(ValueError, match="inv_off has shape"):
+        bb.bb_attn_backward(**{**bw, "inv_off": bw["inv_off"][:, :3].contiguous()})
+    with pytest.raises(ValueError, match="must be a device tensor"):
+        bb.bb_attn_backward(**bw)
+    B, L, hid, H = 1, 256, 128, 2
+    x, y = torch.zeros(B, L, hid, dtype=torch.bfloat16), torch.zeros(B, L, hid, dtype=torch.bfloat16)
+    lw = dict(x=x, w_qkv=torch.zeros(3 * hid, hid, dtype=torch.bfloat16), b_qkv=torch.zeros(3 * hid),
+              w_o=torch.zeros(hid, hid, dtype=torch.bfloat16), b_o=torch.zeros(hid), pad_mask=None,
+              rand_idx=None, B=B, L=L, hidden=hid, H=H, block=64, r=0, y=y,
+              workspace=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="w_qkv has shape"):
+        bb.bb_layer_forward(**{**lw, "w_qkv": lw["w_o"]})
+    with pytest.raises(ValueError, match="b_o has dtype"):
+        bb.bb_layer_forward(**{**lw, "b_o": lw["b_o"].bfloat16()})
+    with pytest.raises(ValueError, match="y has dtype"):
+        bb.bb_layer_forward(**{**lw, "y": y.float()})
+    with pytest.raises(ValueError, match="must be a device tensor"):
+        bb.bb_layer_forward(**lw)
+
+
+def test_table_contents_checked_once_per_version(lib):
+    H, L, block, r = 2, 12 * 64, 64, 3
+    good = bb.bb_rand_idx_build(4, H, L, block, r)
+    t = torch.from_numpy(good.copy())
+    assert bb._check_rand_idx_contents(t, H, L, block, r) is not None     # checked: host copy made
+    assert bb._check_rand_idx_contents(t, H, L, block, r) is None         # remembered
+    t[0, 3, 0] = 4                                                        # block 4 is in row 3's window
+    with pytest.raises(bb.BBError, match="BB_ERR_RAND_IDX"):              # the write bumped the version
+        bb._check_rand_idx_contents(t, H, L, block, r)
+    bad = good.copy()
+    bad[1, 0, 1] = bad[1, 0, 0]                                           # a repeat
+    with pytest.raises(bb.BBError, match="BB_ERR_RAND_IDX"):
+        bb.upload_rand_idx(bad, H, L, block, r, "cpu")
+    up = bb.upload_rand_idx(good, H, L, block, r, "cpu")
+    assert up.dtype == torch.int32 and bb._check_rand_idx_contents(up, H, L, block, r) is None
+    # the backward's inverse table is compared with the library's inverse of the table
+    off, rows = bb.bb_rand_idx_invert(good, H, L, block, r)
+    bb._check_inverse(up, None, torch.from_numpy(off), torch.from_numpy(rows), H, L, block, r)
+    rows2 = rows.copy()
+    rows2[[0, 1]] = rows2[[1, 0]] if rows2[0] != rows2[1] else rows2[[0, 2]] + 1
+    with pytest.raises(ValueError, match="not bb_rand_idx_invert"):
+        bb._check_inverse(up, None, torch.from_numpy(off), torch.from_numpy(rows2), H, L, block, r)

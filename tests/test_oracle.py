@@ -373,3 +373,30 @@ def test_every_valid_table_enumerated_is_accepted():
             else:
                 with pytest.raises(ValueError):
                     check_rand_idx(ri, 1, nb * block, block, r)
+
+
+def test_check_rand_idx_cap_boundary():
+    """The random-range cap (page "models 仓库中的 BigBird…", section "随机块掩码是如何生成的":
+    random blocks are drawn only below token last_idx), pinned on both sides of its
+    boundary with hand-picked values: with block 64, a block e lies inside the cap
+    when its last token e*64 + 63 is below last_idx, i.e. e <= last_idx/64 - 1."""
+    nb, block, r = 20, 64, 2
+    L = nb * block
+
+    def table(first_row_entries):
+        ri = np.zeros((1, nb - 2, r), dtype=np.int64)
+        for j in range(1, nb - 1):                 # every other row: blocks 1..5, off the window
+            cand = [c for c in range(1, 6) if c not in (j - 1, j, j + 1)]
+            ri[0, j - 1] = cand[:r]
+        ri[0, 1] = first_row_entries               # row of middle block 2 (window 1, 2, 3)
+        return ri
+
+    for last_idx, inside, outside in [(640, 9, 10), (639, 8, 9), (650, 9, 10), (704, 10, 11),
+                                      (384, 5, 6)]:
+        check_rand_idx(table([inside, 4]), 1, L, block, r, last_idx=last_idx)
+        with pytest.raises(ValueError, match="beyond token"):
+            check_rand_idx(table([outside, 4]), 1, L, block, r, last_idx=last_idx)
+        with pytest.raises(ValueError, match="beyond token"):
+            check_rand_idx(table([4, outside]), 1, L, block, r, last_idx=last_idx)
+    # no cap (last_idx = 0): the whole middle range, up to block nb - 2 = 18
+    check_rand_idx(table([18, 4]), 1, L, block, r)

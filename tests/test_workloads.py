@@ -48,9 +48,38 @@ def test_per_sequence_block_padding():
         assert np.all(pad[b, : valid[b]] == 1) and np.all(pad[b, valid[b]:] == 0)
 
 
-def test_inputs_rounded_once_to_the_compute_dtype():
+def bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of finite float32 values, rounded to nearest, ties to even,
+    written from the format's definition: keep the top 16 bits of the float32 word,
+    adding half a unit of the kept last place minus one, plus that last bit (so an
+    exact half rounds towards an even last bit)."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    return ((bits + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def test_rne_reference_on_hand_picked_ties():
+    # float32 words -> bfloat16 words, worked by hand: 1.0 is 0x3F80, the next
+    # bfloat16 values up are 0x3F81 (1 + 2^-7) and 0x3F82 (1 + 2^-6)
+    cases = {0x3F808000: 0x3F80,   # 1 + 2^-8: exact half, last bit 0 stays
+             0x3F818000: 0x3F82,   # 1 + 3*2^-8: exact half, last bit 1 rounds up
+             0x3F808001: 0x3F81,   # just above the half
+             0x3F807FFF: 0x3F80,   # just below the half
+             0xBF818000: 0xBF82,   # the same tie, negative
+             0x3F80FFFF: 0x3F81}   # just below 0x3F81's upper half-way point
+    words = np.array(list(cases), dtype=np.uint32)
+    got = bf16_bits_rne(words.view(np.float32))
+    assert got.tolist() == list(cases.values())
+
+
+def test_inputs_rounded_once_to_nearest_even_bf16():
     w = small("w", B=1, H=2, L=4 * 64, block=64, r=0, value_scale=0.125, data_seed=9)
-    q, _, _, _ = make_inputs(w)
+    q, k, v, _ = make_inputs(w)
     assert q.dtype == torch.bfloat16
-    raw = draw(w)[0]
-    assert torch.equal(q, torch.from_numpy(raw).to(torch.bfloat16))
+    raw = draw(w)[:3]
+    for got, x in zip((q, k, v), raw):
+        assert np.array_equal(got.view(torch.int16).numpy().view(np.uint16), bf16_bits_rne(x))
+    # ties occur among these draws only by chance: add explicit ties through the same path
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF818000, 0x3E018000], dtype=np.uint32).view(np.float32)
+    conv = torch.from_numpy(ties.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(conv, bf16_bits_rne(ties))
