@@ -1046,6 +1046,486 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
   run<T, BS, 2, HAS_PAD>(n_units);
 }
 
+// ============================================ forward, bf16, block 128 ==
+// The bf16 work-unit kernel for block 128.  The work units (64 query rows of
+// a block; a key block streams as two 64-key tiles, b -> 2b and 2b+1),
+// tile lists, operand layouts and split-K partials are those of run() above;
+// what differs is the shape of the work per wave and the softmax:
+//   - a workgroup is 2 waves, the two 32-row query groups of a 64-row unit,
+//     and each wave owns complete query rows: every step covers one 32-key
+//     subtile with both waves, so a unit ends without any merge between
+//     waves (for block 128, run() merges four key groups in two LDS rounds);
+//   - a ring stage holds one 32-key subtile of K and of V (8 KiB), so a
+//     workgroup needs 16 KiB of LDS and a CU holds 8 of them: 4 waves per
+//     SIMD at up to 128 registers each;
+//   - the softmax takes every probability of a row in a unit against one
+//     fixed reference (below), with no rescale branch in the step.
+//
+// Softmax with a fixed reference.  Within a unit, each row's probabilities
+// are taken against one reference m: the row max of the unit's first 32-key
+// subtile (pad offsets included).  m is a score of the row, so the largest
+// probability of the row is at least 1 (no underflow of the dominant terms).
+// Each subtile checks that its probabilities stay bounded: the lane's sum of
+// them (computed anyway for the row sum) must not exceed 2^32, so no single
+// one does; then O and l are far inside fp32 range and need no rescaling.
+// When some lane's sum exceeds the bound (scores more than 32/c above m, or
+// an all-padding first subtile against valid later ones), that wave
+// recomputes its rows of the unit at the end, exactly, in two passes from
+// global memory (redo_unit_w).
+
+constexpr int kTile64 = 64 * kD * 2;               // one 64-key bf16 tile of K (or V): 8 KiB
+constexpr float kProbBound = 4294967296.0f;        // 2^32: the largest probability the fast path keeps
+
+// A wave's softmax state per query row (fixed-reference softmax).
+struct WaveStateW {
+  f32x16 o[2];     // O^T, dims [0,32) and [32,64)
+  float m;         // the unit's reference max (q.k units)
+  float l;         // this lane's part of the row sum
+  float big;       // largest per-subtile probability sum of this lane (the bound check)
+};
+
+// Probabilities of one 32-key subtile against the reference m (q.k units)
+// and uniform offset `bias`: P = 2^((s + bias - m) c), rounded to the bf16
+// PV operands; returns this lane's sum of the rounded values.
+__device__ __forceinline__ float probs_w(const f32x16& s, float m, float bias, bf16x8 (&pb)[2]) {
+  const float mc = (m - bias) * kScaleLog2;
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float lsum = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      f32x2 pr = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], kScaleLog2, -mc)),
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e + 1], kScaleLog2, -mc))};
+      const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, lsum, false);
+      pb[h][e] = c2[0];
+      pb[h][e + 1] = c2[1];
+    }
+  return lsum;
+}
+
+// O^T += V^T P^T for one subtile (4 MFMAs: 2 dim halves x 2 16-key halves).
+__device__ __forceinline__ void pv_w(WaveStateW& ws, const VOp<__bf16>& vo, const bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+      ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[dh][mm], pb[mm], ws.o[dh], 0, 0, 0);
+}
+
+// Pad offsets of one 32-key subtile, classified on the scalar unit before the
+// score products (the classes of apply_pad()): the uniform offset `bias` (0,
+// or -10000 on the logit when all 32 keys are padding) and, for a subtile
+// with both kinds of keys, `mixed` = the per-key mask (bit k: key k padded),
+// added after the products by add_pad_bias(); 0 otherwise.
+struct PadClass {
+  float bias;
+  uint32_t mixed;
+};
+__device__ __forceinline__ PadClass classify_pad(const PadWords& w) {
+  PadClass c;
+  c.bias = 0.0f;
+  c.mixed = 0u;
+  if ((zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0)
+    return c;
+  if ((w.p[0] | w.p[1] | w.p[2] | w.p[3]) == 0) {
+    c.bias = kMaskRaw;
+    return c;
+  }
+  c.mixed = zero_byte_mask(w.p[0]) | (zero_byte_mask(w.p[1]) << 8) | (zero_byte_mask(w.p[2]) << 16) |
+            (zero_byte_mask(w.p[3]) << 24);
+  return c;
+}
+
+// The per-key offsets of a mixed subtile, added to the score accumulator by
+// one fp32 32x32x2 MFMA (as in apply_pad()).
+__device__ __forceinline__ void add_pad_bias(f32x16& acc, uint32_t mixed, int lane) {
+  const int j = lane & 31;
+  const bool lo = lane < 32;
+  const bool padded = (mixed >> perm_row(j)) & 1u;
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? 1.0f : 0.0f, acc, 0, 0, 0);
+}
+
+// 64-key tile id of entry i of a unit's tile list (block-level list, TPB
+// 64-key tiles per key block).
+template <int TPB>
+__device__ __forceinline__ int tile64_at(const TileList& tl, int i) {
+  if constexpr (TPB == 1) return tile_at(tl, i);
+  return TPB * tile_at(tl, i / TPB) + i % TPB;
+}
+
+// Scores of one 32-key subtile read straight from global memory (the slow
+// path): S^T = K Q^T with K rows perm_row-ordered as in scores(), the
+// subtile's pad offsets added per key in fp32.
+__device__ __forceinline__ f32x16 scores_global(const char* kt, const uint8_t* pt, const u32x4 (&qop)[4], int kbase,
+                                                int lane) {
+  const int j = lane & 31, g = lane >> 5;
+  const char* krow = kt + (kbase + perm_row(j)) * (kD * 2);
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    acc = mfma_qk(*reinterpret_cast<const u32x4*>(krow + (2 * x + g) * 16), qop[x], acc, static_cast<__bf16*>(nullptr));
+  if (pt != nullptr) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)   // element v holds key kbase + 16 (v / 8) + 8 g + v % 8
+      if (pt[kbase + 16 * (v >> 3) + 8 * g + (v & 7)] == 0) acc[v] += kMaskRaw;
+  }
+  return acc;
+}
+
+// Slow path of a unit in which some lane of this wave saw a probability sum
+// above the bound: this wave's 32 rows of the unit are recomputed exactly,
+// in two passes over the unit's tiles read straight from global memory --
+// the row max over every allowed key first, then the probabilities against
+// it (all at most 1) and O, l.  Registers and global loads only (no LDS, no
+// barrier), so the other wave of the workgroup does not take part.
+template <int TPB, bool HAS_PAD>
+__device__ __forceinline__ void redo_unit_w(WaveStateW& ws, const Unit& cu, int ntiles, int wq, int lane) {
+  const kargs_ptr a = kargs();
+  const char* kbh = a->k + cu.off;
+  const char* vbh = a->v + cu.off;
+  const uint8_t* pad_b = HAS_PAD ? a->pad + static_cast<size_t>(cu.b) * a->L : nullptr;
+  u32x4 q[4];
+  load_q<__bf16, 64>(a->q + cu.off + static_cast<size_t>(cu.q0) * (kD * 2), wq, lane, q);
+  float lm = -__builtin_inff();
+#pragma unroll 1
+  for (int i = 0; i < 2 * ntiles; ++i) {
+    const int t = tile64_at<TPB>(cu.tl, i >> 1), kb = 32 * (i & 1);
+    const char* kt = kbh + static_cast<size_t>(t) * kTile64;
+    const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
+    lm = lane_max(scores_global(kt, pt, q, kb, lane), lm);
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+  ws.m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  ws.l = 0.0f;
+  ws.big = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    ws.o[0][v] = 0.0f;
+    ws.o[1][v] = 0.0f;
+  }
+  const int j = lane & 31, g = lane >> 5;
+#pragma unroll 1
+  for (int i = 0; i < 2 * ntiles; ++i) {
+    const int t = tile64_at<TPB>(cu.tl, i >> 1), kb = 32 * (i & 1);
+    const char* kt = kbh + static_cast<size_t>(t) * kTile64;
+    const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
+    const f32x16 s = scores_global(kt, pt, q, kb, lane);
+    bf16x8 pb[2];
+    ws.l += probs_w(s, ws.m, 0.0f, pb);
+    // V^T operand: dim dh*32 + perm_row(j), keys kb + 16 mm + 8 g + e (e = 0..7),
+    // gathered two keys at a time
+    const uint16_t* vcol = reinterpret_cast<const uint16_t*>(vbh + static_cast<size_t>(t) * kTile64) +
+                           (kb + 8 * g) * kD + perm_row(j);
+    VOp<__bf16> vo;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const uint16_t* c = vcol + 16 * mm * kD + 32 * dh;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = static_cast<uint32_t>(c[(2 * e) * kD]) | (static_cast<uint32_t>(c[(2 * e + 1) * kD]) << 16);
+        vo.a[dh][mm] = __builtin_bit_cast(bf16x8, w);
+      }
+    pv_w(ws, vo, pb);
+  }
+}
+
+// End of a unit: each wave holds complete rows.  Middle unit: out = O / l in
+// bf16 (and the row log-sum-exp when asked for); global unit: the
+// unnormalised partial (max, sum, O) in the layout of partial_slot().
+__device__ __forceinline__ void finalize_w(const WaveStateW& ws, const Unit& w, int wq, int lane) {
+  const int j = lane & 31, g = lane >> 5;
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ws.l), __float_as_uint(ws.l), false, false);
+  const float l = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);   // both lane halves of the row
+  if (w.gsel < 0) {
+    const float inv = __builtin_amdgcn_rcpf(l);
+    char* dst = kargs()->out + w.off + static_cast<size_t>(w.q0 + wq * 32 + j) * (kD * 2);
+    float* lse = kargs()->lse;
+    if (g == 0 && lse != nullptr)
+      lse[w.off / (kD * 2) + w.q0 + wq * 32 + j] = (ws.m * kScaleLog2 + __builtin_amdgcn_logf(l)) * kLn2;
+#pragma unroll
+    for (int keep = 0; keep < 2; ++keep)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = ws.o[keep][8 * h8 + e] * inv;
+        store_row8(dst + (keep * 32 + 16 * h8 + 8 * g) * 2, x, static_cast<__bf16*>(nullptr));
+      }
+    return;
+  }
+  const kargs_ptr a = kargs();
+  const size_t pidx = w.pbase + wq * 32 + j;
+  float* blk = a->po + w.pbase * kD;
+#pragma unroll
+  for (int keep = 0; keep < 2; ++keep)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v4 = {ws.o[keep][4 * q], ws.o[keep][4 * q + 1], ws.o[keep][4 * q + 2], ws.o[keep][4 * q + 3]};
+      *reinterpret_cast<f32x4*>(blk + partial_slot(wq, keep, q, lane)) = v4;
+    }
+  if (g == 0) {
+    a->pm[pidx] = ws.m;
+    a->pl[pidx] = l;
+  }
+}
+
+// The 32-key-step kernel: its ring, step and persistent workgroup.  A
+// unit's subtile count is even, so its last step always sits in stage 1 and
+// the next unit's first subtile and Q rows are always prefetched during it.
+
+constexpr int kSub32NW = 2;                   // waves per workgroup
+constexpr int kSub32NT = 64 * kSub32NW;
+constexpr int kSub = 32 * kD * 2;              // one 32-key bf16 subtile of K (or V): 4 KiB
+
+// The 2-stage ring of 32-key stages (K subtile, then V subtile).
+template <int S>
+struct SubStage {
+  static __device__ __forceinline__ char* buf() {
+    __shared__ __attribute__((aligned(1024))) char b[2 * kSub];
+    return b;
+  }
+  static __device__ __forceinline__ char* k() { return buf(); }
+  static __device__ __forceinline__ char* v() { return buf() + kSub; }
+};
+
+// DMA of 32-key subtile `sub` (keys [32 sub, 32 sub + 32)) of K and V into
+// stage S: 4 instructions per matrix, 2 per wave; the swizzled chunk
+// placement of issue_tile().
+template <int S>
+__device__ __forceinline__ void issue_sub(gchar_ptr kbh, gchar_ptr vbh, int sub, int wave, int lane) {
+  constexpr int CPR = kD * 2 / 16;
+  const gchar_ptr kt = kbh + static_cast<size_t>(sub) * kSub;
+  const gchar_ptr vt = vbh + static_cast<size_t>(sub) * kSub;
+  const uint32_t lk = lds_addr(SubStage<S>::k()), lv = lk + kSub;
+  uint32_t ko[2], vo[2], mk[2], mv[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int ins = wave + kSub32NW * jj;
+    const int slot = ins * 64 + lane;
+    const int row = slot / CPR, p = slot % CPR;
+    ko[jj] = row * (kD * 2) + ((p ^ swz_k(row)) << 4);
+    vo[jj] = row * (kD * 2) + ((p ^ swz_v(row)) << 4);
+    mk[jj] = __builtin_amdgcn_readfirstlane(lk + ins * 1024);
+    mv[jj] = __builtin_amdgcn_readfirstlane(lv + ins * 1024);
+  }
+  dma16x4(kt, vt, ko[0], vo[0], ko[1], vo[1], mk[0], mv[0], mk[1], mv[1]);
+}
+
+// S^T = K . Q^T for the 32-key subtile in stage S (K rows perm_row-ordered
+// as in scores()).
+template <int S>
+__device__ __forceinline__ f32x16 scores_n(const u32x4 (&qop)[4], int lane) {
+  const int j = lane & 31, g = lane >> 5;
+  const char* sk = SubStage<S>::k();
+  const int row = perm_row(j);
+  const int sw = swz_k(row);
+  u32x4 a[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    a[x] = *reinterpret_cast<const u32x4*>(sk + row * (kD * 2) + (((2 * x + g) ^ sw) << 4));
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) acc = mfma_qk(a[x], qop[x], acc, static_cast<__bf16*>(nullptr));
+  return acc;
+}
+
+// V^T operands of the subtile in stage S (the transposing reads of load_v()).
+template <int S>
+__device__ __forceinline__ VOp<__bf16> load_v_n(int lane) {
+  const char* sv = SubStage<S>::v();
+  VOp<__bf16> vo;
+  const int g = lane >> 5, e4 = (lane >> 2) & 3;
+  const int r0 = 8 * g + e4;
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh) {
+    const int dstart = dh * 32 + perm_row(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    const int dchunk = dstart >> 3, dbyte = (dstart & 7) * 2;
+    const char* base = sv + r0 * (kD * 2) + ((dchunk ^ swz_v(r0)) << 4) + dbyte;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + 16 * mm * (kD * 2)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + (16 * mm + 4) * (kD * 2)));
+      vo.a[dh][mm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+  return vo;
+}
+
+// Step i of a unit's subtile loop: subtile i sits in stage S = i % 2; sub_u
+// and sub_fill are the ids of subtiles i and i+1.  FIRST: the unit's first
+// subtile, whose row max is the reference.  On the last step (always in
+// stage 1) the next unit's first subtile and Q rows are prefetched.
+template <int S, bool HAS_PAD, bool FIRST>
+__device__ __forceinline__ void step_n(WaveStateW& ws, u32x4 (&qop)[4], bool last, int sub_u, int sub_fill,
+                                       gchar_ptr kbh, gchar_ptr vbh, const uint8_t* pad_b, int wave, int lane,
+                                       const NextUnit& nx) {
+  // The pad bytes first, so that their scalar load completes under the wait
+  // and the barrier (see step()).
+  PadWords pw;
+  if constexpr (HAS_PAD) {
+    pw = load_pad(pad_b + static_cast<size_t>(sub_u) * 32, 0);
+    asm volatile("" ::: "memory");
+  }
+  __builtin_amdgcn_s_waitcnt(7 << 4);
+  ring_barrier();
+  f32x16 s = scores_n<S>(qop, lane);
+  const VOp<__bf16> vo = load_v_n<S>(lane);
+  if (!last) {
+    issue_sub<S ^ 1>(kbh, vbh, sub_fill, wave, lane);
+  } else if (S == 1 && nx.pf) {
+    const kargs_ptr a = kargs();
+    issue_sub<0>((gchar_ptr)(a->k) + nx.off, (gchar_ptr)(a->v) + nx.off, nx.tile0, wave, lane);
+  }
+  PadClass c;
+  c.bias = 0.0f;
+  c.mixed = 0u;
+  if constexpr (HAS_PAD) {
+    c = classify_pad(pw);
+    if (c.mixed) add_pad_bias(s, c.mixed, lane);
+  }
+  if (S == 1 && last && nx.pf) {
+    // Q is dead after the score products: refill it for the next unit
+    asm volatile("" : "+v"(s) : : "memory");
+    load_q<__bf16, 64>(kargs()->q + nx.off + static_cast<size_t>(nx.q0) * (kD * 2), wave, lane, qop);
+  }
+  if constexpr (FIRST) {
+    const float lm = lane_max(s, s[15]) + c.bias;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+    ws.m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  bf16x8 pb[2];
+  const float lsum = probs_w(s, ws.m, c.bias, pb);
+  ws.l += lsum;
+  ws.big = fmaxf(ws.big, lsum);
+  pv_w(ws, vo, pb);
+}
+
+// The persistent workgroup of the 32-key-step kernel: run() above with its
+// steps (and no merge between waves).
+template <int BS, int kind, bool HAS_PAD>
+__device__ __forceinline__ void run_n(int n_units) {
+  constexpr int TPB = BS / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int first, stride, end;
+  {
+    const int G = gridDim.x, x = blockIdx.x;
+    if ((G & 7) == 0) {
+      const int X = x & 7;
+      first = static_cast<int>((static_cast<long long>(n_units) * X) >> 3) + (x >> 3);
+      end = static_cast<int>((static_cast<long long>(n_units) * (X + 1)) >> 3);
+      stride = G >> 3;
+    } else {
+      first = x;
+      end = n_units;
+      stride = G;
+    }
+  }
+  if (first >= end) return;
+
+  Cursor cur = cursor_at<__bf16, BS, kind>(kargs(), first);
+  Unit cu = decode_unit<__bf16, BS, kind>(kargs(), cur);
+  u32x4 qop[4];
+  {
+    const kargs_ptr a = kargs();
+    issue_sub<0>((gchar_ptr)(a->k) + cu.off, (gchar_ptr)(a->v) + cu.off, 2 * tile64_at<TPB>(cu.tl, 0), wave, lane);
+    load_q<__bf16, 64>(a->q + cu.off + static_cast<size_t>(cu.q0) * (kD * 2), wave, lane, qop);
+  }
+  for (;;) {
+    int lane_u = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+    asm volatile("" : "+v"(lane_u));
+    const Cursor nxt = cursor_advance<__bf16, BS, kind>(kargs(), cur, stride);
+    const bool has_next = nxt.unit < end;
+    const int ntiles = TPB * cu.ntiles;        // 64-key tiles
+    const int nsub = 2 * ntiles;               // 32-key steps (even)
+    NextUnit nx;
+    {
+      const Unit nu = decode_unit<__bf16, BS, kind>(kargs(), nxt);
+      nx.off = nu.off;
+      nx.q0 = nu.q0;
+      nx.tile0 = 2 * TPB * (nu.tl.global ? nu.tl.first : 0);   // its first 32-key subtile
+      nx.pf = has_next ? 1 : 0;
+      nx.unused = 0;
+    }
+    gchar_ptr kbh, vbh;
+    const uint8_t* pad_b;
+    {
+      const kargs_ptr a = kargs();
+      kbh = (gchar_ptr)(a->k) + cu.off;
+      vbh = (gchar_ptr)(a->v) + cu.off;
+      pad_b = HAS_PAD ? a->pad + static_cast<size_t>(cu.b) * a->L : nullptr;
+    }
+    WaveStateW ws;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      ws.o[0][v] = 0.0f;
+      ws.o[1][v] = 0.0f;
+    }
+    ws.m = -__builtin_inff();
+    ws.l = 0.0f;
+    ws.big = 0.0f;
+
+    // trips of TRIP straight-line steps (TRIP / 2 tiles)
+    constexpr int TRIP = 8;
+    static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
+    for (int u = 0; u < nsub; u += TRIP) {
+      int rem = nsub - u;
+      asm volatile("" : "+s"(rem));
+      // the trip's 64-key tiles and the one after it, two 16-bit ids per
+      // scalar register (L / 64 < 65536)
+      const int t0 = u >> 1, tleft = ntiles - t0;
+      uint32_t tp[(TRIP / 2 + 2) / 2];
+#pragma unroll
+      for (int k = 0; k < (TRIP / 2 + 2) / 2; ++k) {
+        const uint32_t ta = 2 * k < tleft ? static_cast<uint32_t>(tile64_at<TPB>(cu.tl, t0 + 2 * k)) : 0u;
+        const uint32_t tb = 2 * k + 1 < tleft ? static_cast<uint32_t>(tile64_at<TPB>(cu.tl, t0 + 2 * k + 1)) : 0u;
+        tp[k] = ta | (tb << 16);
+      }
+#define BB_SUB(k) (2 * static_cast<int>((tp[(k) >> 2] >> (16 * (((k) >> 1) & 1))) & 0xffffu) + ((k) & 1))
+#define BB_STEPN(k, F)                                                                                           \
+  step_n<(k) % 2, HAS_PAD, F>(ws, qop, (k) + 1 == rem, BB_SUB(k), BB_SUB((k) + 1), kbh, vbh, pad_b, wave, lane_u, \
+                              nx)
+      if (u == 0)
+        BB_STEPN(0, true);
+      else
+        BB_STEPN(0, false);
+#define BB_STEPN_IF(k) \
+  if ((k) < rem) BB_STEPN(k, false);
+      BB_STEPN_IF(1) BB_STEPN_IF(2) BB_STEPN_IF(3) BB_STEPN_IF(4) BB_STEPN_IF(5) BB_STEPN_IF(6) BB_STEPN_IF(7)
+#undef BB_STEPN_IF
+#undef BB_STEPN
+#undef BB_SUB
+    }
+    if (__any(ws.big > kProbBound)) redo_unit_w<TPB, HAS_PAD>(ws, cu, ntiles, wave, lane_u);
+    finalize_w(ws, cu, wave, lane_u);
+    if (!has_next) break;
+    cur = nxt;
+    cu = decode_unit<__bf16, BS, kind>(kargs(), cur);
+  }
+}
+
+template <int BS, bool HAS_PAD>
+__global__ void __launch_bounds__(kSub32NT) __attribute__((amdgpu_waves_per_eu(4))) bb_sub32_fused_kernel(Args, int n_units) {
+  run_n<BS, 0, HAS_PAD>(n_units);
+}
+template <int BS, bool HAS_PAD>
+__global__ void __launch_bounds__(kSub32NT) __attribute__((amdgpu_waves_per_eu(4))) bb_sub32_global_rows_kernel(Args, int n_units) {
+  run_n<BS, 1, HAS_PAD>(n_units);
+}
+template <int BS, bool HAS_PAD>
+__global__ void __launch_bounds__(kSub32NT) __attribute__((amdgpu_waves_per_eu(4))) bb_sub32_middle_rows_kernel(Args, int n_units) {
+  run_n<BS, 2, HAS_PAD>(n_units);
+}
+
 // ================================================================ backward ==
 // Gradients of the same attention (dQ, dK, dV of sum(out * dO)), the
 // textbook softmax-attention backward restricted to the block pattern:
@@ -2005,7 +2485,7 @@ int check_shape(int B, int H, int L, int d, int block, int r, int* nb_out) {
   if (block != 64 && block != 128) return BB_ERR_SHAPE;
   if (L % block != 0) return BB_ERR_SHAPE;
   const int nb = L / block;
-  if (nb < 3 || nb > 65535) return BB_ERR_SHAPE;
+  if (nb < 3 || L / 64 > 65535) return BB_ERR_SHAPE;   // 64-key tile ids fit in 16 bits
   const int r_max = nb - 5 > 0 ? nb - 5 : 0;
   if (r > r_max || r > kMaxR) return BB_ERR_SHAPE;
   const int n_s = (nb + kChunkTiles - 1) / kChunkTiles;
@@ -2051,25 +2531,38 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags, hipE
   const bool merge = !(flags & BB_PHASE_UNITS) || (flags & BB_PHASE_MERGE);
   unsigned grid = 0;
   int st = BB_OK;
+  // bf16 at block 128: the 32-key-step kernels (2 waves of complete rows);
+  // otherwise the key-group kernels of run() (32 x 32 subtiles per wave)
+  typedef void (*UnitKernel)(Args, int);
+  UnitKernel k_fused, k_global, k_middle;
+  int nt;
+  if constexpr (sizeof(T) == 2 && BS == 128) {
+    k_fused = bb_sub32_fused_kernel<BS, HAS_PAD>;
+    k_global = bb_sub32_global_rows_kernel<BS, HAS_PAD>;
+    k_middle = bb_sub32_middle_rows_kernel<BS, HAS_PAD>;
+    nt = kSub32NT;
+  } else {
+    k_fused = bb_fused_kernel<T, BS, HAS_PAD>;
+    k_global = bb_global_rows_kernel<T, BS, HAS_PAD>;
+    k_middle = bb_middle_rows_kernel<T, BS, HAS_PAD>;
+    nt = C::NT;
+  }
   if (units) {
     hipEvent_t e1 = merge ? nullptr : ev1;
     if (flags & BB_LAUNCH_SPLIT) {
-      st = persistent_grid(reinterpret_cast<const void*>(&bb_global_rows_kernel<T, BS, HAS_PAD>), C::NT,
-                           bhs * per_g, &grid);
+      st = persistent_grid(reinterpret_cast<const void*>(k_global), nt, bhs * per_g, &grid);
       if (st != BB_OK) return st;
-      hipExtLaunchKernelGGL(bb_global_rows_kernel<T, BS, HAS_PAD>, dim3(grid), dim3(C::NT), 0, stream, ev0,
-                            nullptr, 0, a, static_cast<int>(bhs * per_g));
+      hipExtLaunchKernelGGL(k_global, dim3(grid), dim3(nt), 0, stream, ev0, nullptr, 0, a,
+                            static_cast<int>(bhs * per_g));
       if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-      st = persistent_grid(reinterpret_cast<const void*>(&bb_middle_rows_kernel<T, BS, HAS_PAD>), C::NT,
-                           bhs * per_m, &grid);
+      st = persistent_grid(reinterpret_cast<const void*>(k_middle), nt, bhs * per_m, &grid);
       if (st != BB_OK) return st;
-      hipExtLaunchKernelGGL(bb_middle_rows_kernel<T, BS, HAS_PAD>, dim3(grid), dim3(C::NT), 0, stream, nullptr,
-                            e1, 0, a, static_cast<int>(bhs * per_m));
+      hipExtLaunchKernelGGL(k_middle, dim3(grid), dim3(nt), 0, stream, nullptr, e1, 0, a,
+                            static_cast<int>(bhs * per_m));
     } else {
-      st = persistent_grid(reinterpret_cast<const void*>(&bb_fused_kernel<T, BS, HAS_PAD>), C::NT,
-                           bhs * (per_g + per_m), &grid);
+      st = persistent_grid(reinterpret_cast<const void*>(k_fused), nt, bhs * (per_g + per_m), &grid);
       if (st != BB_OK) return st;
-      hipExtLaunchKernelGGL(bb_fused_kernel<T, BS, HAS_PAD>, dim3(grid), dim3(C::NT), 0, stream, ev0, e1, 0, a,
+      hipExtLaunchKernelGGL(k_fused, dim3(grid), dim3(nt), 0, stream, ev0, e1, 0, a,
                             static_cast<int>(bhs * (per_g + per_m)));
     }
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;

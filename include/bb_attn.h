@@ -127,7 +127,8 @@ size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block);
  *              May be NULL when r == 0.
  *   B, H, L    batch, heads, sequence length (B == 0 or H == 0: no-op, BB_OK).
  *   d          head dimension; must be 64.
- *   block      block size; 64 or 128; L % block == 0; nb = L/block >= 3.
+ *   block      block size; 64 or 128; L % block == 0; nb = L/block >= 3;
+ *              L <= 64 * 65535 (64-key tile ids are 16-bit).
  *   r          random blocks per middle row, 0 <= r <= min(16, max(0, nb-5)).
  *   out        DEVICE [B][H][L][d] in `dtype`, 16-byte aligned, fully
  *              overwritten; must not overlap q, k or v.

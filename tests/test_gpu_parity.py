@@ -127,6 +127,12 @@ SMALL = [
     # every key of every row padded: the offset is uniform per row and cancels
     small("nb8_r2_all_padded", B=2, H=2, L=8 * 64, block=64, r=2, pad="fixed", valid_len=0,
           data_seed=33),
+    # logits tens of nats apart between tiles (5% of key rows x24, unscaled values):
+    # rows whose later tiles exceed the first tile's max by far, recomputed exactly
+    small("huge_logit_gaps", B=1, H=2, L=12 * 64, block=64, r=3, outlier_frac=0.05,
+          outlier_mult=24.0, data_seed=35),
+    small("huge_logit_gaps_bs128_pad", B=2, H=2, L=8 * 128, block=128, r=2, outlier_frac=0.05,
+          outlier_mult=24.0, pad="fixed", valid_len=8 * 128 - 100, data_seed=36),
 ]
 
 
