@@ -34,7 +34,7 @@ EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_
            "bb_attn_workspace_bytes", "bb_attn_forward", "bb_attn_forward_ex",
            "bb_attn_forward_timed", "bb_attn_forward_lse", "bb_rand_idx_invert",
            "bb_attn_backward_workspace_bytes", "bb_attn_backward", "bb_layer_workspace_bytes",
-           "bb_layer_forward")
+           "bb_layer_forward", "bb_attn_forward_noalloc")
 
 _lib = None
 
@@ -82,6 +82,8 @@ def lib():
     L.bb_attn_forward_timed.argtypes = fwd + [ctypes.c_uint, vp, vp]
     L.bb_attn_forward_lse.restype = c_int
     L.bb_attn_forward_lse.argtypes = fwd + [vp]
+    L.bb_attn_forward_noalloc.restype = c_int
+    L.bb_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, c_int, vp]
     L.bb_rand_idx_invert.restype = c_int
     L.bb_rand_idx_invert.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp]
     L.bb_attn_backward_workspace_bytes.restype = c_size
@@ -334,6 +336,30 @@ def forward(q, k, v, rand_idx, pad_mask=None, block: int = 64, out=None, workspa
     bb_attn_forward(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, workspace,
                     stream=stream, flags=flags)
     return out
+
+
+# Size of the library's own scratch area per GPU (BB_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def bb_attn_forward_noalloc(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int,
+                            r: int, out, stream=None) -> None:
+    """The forward without a workspace argument (for callers that cannot
+    allocate): the split-K partials go to the library's own scratch area on
+    the device.  Calls that overlap on one GPU race on that area.  Arguments
+    and checks as bb_attn_forward."""
+    _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out)))
+    table = _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("pad_mask", pad_mask),
+                    ("rand_idx", rand_idx)):
+        _check_device_tensor(name, t)
+    if table:
+        _check_rand_idx_contents(rand_idx, H, L, block, r)
+    st = lib().bb_attn_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
+                                       B, H, L, d, block, r, _ptr(out), _dtype_code(q),
+                                       _stream_handle(q, stream))
+    if st != BB_OK:
+        raise BBError(st, "bb_attn_forward_noalloc")
 
 
 def bb_attn_forward_lse(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int,

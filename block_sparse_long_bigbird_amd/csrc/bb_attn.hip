@@ -46,6 +46,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "bb_attn.h"
 
 namespace {
@@ -2690,6 +2692,54 @@ extern "C" int bb_attn_forward(const void* q, const void* k, const void* v, cons
                                void* stream) {
   return bb_attn_forward_ex(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace,
                             workspace_bytes, stream, BB_LAUNCH_FUSED);
+}
+
+
+// --------------------------------------------- forward without allocation --
+// bb_attn_forward_noalloc keeps the split-K partials in `scratch`, a device
+// array of the library's own (each GPU holds its copy from the library's
+// load until the process ends).  Host code never passes the array's name to
+// a kernel: its device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is kept per device.
+static __device__ __align__(256) char scratch[BB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use).
+int scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BB_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BB_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BB_OK;
+}
+
+}  // namespace
+
+extern "C" int bb_attn_forward_noalloc(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                       const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                                       void* out, int dtype, void* stream) {
+  // sizes first (no HIP call on a rejected call), then the scratch address
+  int nb = 0;
+  if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
+  int st = check_shape(B, H, L, d, block, r, &nb);
+  if (st != BB_OK) return st;
+  if (B == 0 || H == 0) return BB_OK;
+  if (workspace_layout(B, H, nb, block).total > BB_NOALLOC_SCRATCH_BYTES) return BB_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != BB_OK) return st;
+  return forward_impl(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, ws, BB_NOALLOC_SCRATCH_BYTES,
+                      stream, BB_LAUNCH_FUSED, nullptr, nullptr, nullptr);
 }
 
 // ------------------------------------------------------------ backward host --

@@ -149,6 +149,28 @@ int bb_attn_forward(const void* q, const void* k, const void* v, const uint8_t* 
                     void* out, int dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc -- the
+ * forward of bb_attn_forward without a workspace argument: its split-K
+ * partials go to a scratch area the library holds in each GPU's memory (a
+ * file-scope device array of BB_NOALLOC_SCRATCH_BYTES, present from the
+ * library's load until the process ends).  The call allocates and frees
+ * nothing; the first call on a device looks the area's address up once
+ * (hipGetSymbolAddress) and keeps it.
+ *   Arguments as bb_attn_forward (the fused launch), without workspace.
+ *   Errors as bb_attn_forward; BB_ERR_WORKSPACE when these sizes need more
+ *   than BB_NOALLOC_SCRATCH_BYTES of partials (bb_attn_workspace_bytes()).
+ * Every call on a GPU shares that GPU's area: calls that overlap on one GPU
+ * (on other streams or from other threads) race and give undefined results;
+ * order them on one stream.  Nothing needs clearing between calls (every
+ * byte a call reads is written earlier in the same call).
+ */
+#define BB_NOALLOC_SCRATCH_BYTES (64u << 20)
+int bb_attn_forward_noalloc(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                            const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                            void* out, int dtype, void* stream);
+
 /* bb_attn_forward with flags: a launch mode (BB_LAUNCH_FUSED or BB_LAUNCH_SPLIT,
  * which give the same result bit for bit) and optionally one phase
  * (BB_PHASE_UNITS or BB_PHASE_MERGE) for callers that time the phases or
