@@ -24,6 +24,7 @@ BB_LAUNCH_FUSED = 0
 BB_LAUNCH_SPLIT = 1
 BB_PHASE_UNITS = 2
 BB_PHASE_MERGE = 4
+BB_QUERY_MASK = 8
 STATUS_NAMES = {0: "BB_OK", 1: "BB_ERR_NULL", 2: "BB_ERR_SHAPE", 3: "BB_ERR_DTYPE",
                 4: "BB_ERR_RAND_IDX", 5: "BB_ERR_WORKSPACE", 6: "BB_ERR_HIP",
                 7: "BB_ERR_ALIAS", 8: "BB_ERR_ALIGN"}

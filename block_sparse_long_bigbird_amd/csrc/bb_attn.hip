@@ -110,6 +110,7 @@ struct Args {
                    // block is stored lane-major (partial_slot())
   float* lse;      // [B*H][L] natural-log row log-sum-exp of the logits, or null (not written)
   int H, L, nb, r, n_s;
+  int qmask;       // 1: pairs are masked when the query or the key is padding (pad != null)
 };
 
 // LDS ring: one object per (dtype, block, stage) holding that stage's K and V
@@ -235,6 +236,7 @@ struct WaveState {
   f32x16 o[2];   // O^T, dims [0,32) and [32,64)
   float m;       // running row max in q.k units (may lag the true max by < tau/scale)
   float l;       // this lane's part of the row sum
+  float qs;      // key offsets apply to this row: 1, or 0 for a padded query row under pair masking
 };
 
 // V^T operands of one subtile for the PV MFMAs: [dim half][16-key half].
@@ -314,9 +316,13 @@ __device__ __forceinline__ uint32_t zero_byte_mask(uint64_t w) {
 //   mixed          -> the per-key bias enters the score accumulator through
 //                     one more product, an fp32 32x32x2 MFMA (one register
 //                     per operand): row i of A (key perm_row(i)) carries the
-//                     key's bias in k-slot 0 (lanes 0..31), B holds 1 there
+//                     key's bias in k-slot 0 (lanes 0..31), B holds qs there
 //                     for every query, k-slot 1 is zero; -80000 * 1 is exact,
 //                     so this is the fp32 add of the bias.  Returns 0.
+// qs (per lane, i.e. per query row): 1, or 0 for a padded query row under
+// pair masking, where every pair of the row gets the offset: a row-uniform
+// offset cancels in the softmax, so such a row takes no key offsets at all
+// (the caller scales the returned uniform offset by qs too).
 // The zero-byte test per word is exact: a byte b sets bit 7 of
 // (b - 1) & ~b only when b == 0, and a borrow leaves a byte only from a zero
 // byte, which is flagged already.
@@ -324,7 +330,7 @@ __device__ __forceinline__ uint64_t zero_bytes_any(uint64_t x) {
   return (x - 0x0101010101010101ull) & ~x & 0x8080808080808080ull;
 }
 
-__device__ __forceinline__ float apply_pad(f32x16& acc, const PadWords& w, int lane) {
+__device__ __forceinline__ float apply_pad(f32x16& acc, const PadWords& w, int lane, float qs = 1.0f) {
   if ((zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0)
     return 0.0f;
   if ((w.p[0] | w.p[1] | w.p[2] | w.p[3]) == 0) return kMaskRaw;
@@ -333,7 +339,7 @@ __device__ __forceinline__ float apply_pad(f32x16& acc, const PadWords& w, int l
   const int j = lane & 31;
   const bool lo = lane < 32;                        // lanes holding k-slot 0
   const bool padded = (m >> perm_row(j)) & 1u;
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? 1.0f : 0.0f, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? qs : 0.0f, acc, 0, 0, 0);
   return 0.0f;
 }
 
@@ -649,7 +655,7 @@ __device__ __forceinline__ void step(WaveState& ws, u32x4 (&qop)[Cfg<T, BS>::QC]
     issue_tile<T, BS, 0>((gchar_ptr)(a->k) + nx.off, (gchar_ptr)(a->v) + nx.off, nx.tile0, wave, lane);
   }
   float pbias = 0.0f;
-  if constexpr (HAS_PAD) pbias = apply_pad(s, pw, lane);
+  if constexpr (HAS_PAD) pbias = apply_pad(s, pw, lane, ws.qs) * ws.qs;
   if (S == 1 && last && nx.pf) {
     // Q is dead after the score products: refill it for the next unit.  The
     // empty asm ties the loads after those products.
@@ -907,6 +913,10 @@ __device__ __forceinline__ void run(int n_units) {
     }
     ws.m = -__builtin_inff();
     ws.l = 0.0f;
+    ws.qs = 1.0f;
+    if constexpr (HAS_PAD) {
+      if (kargs()->qmask) ws.qs = pad_b[cu.q0 + wq * 32 + (lane_u & 31)] != 0 ? 1.0f : 0.0f;
+    }
 
     // ---- tile loop: trips of 12 straight-line steps ---------------------------
     // Units of the usual shapes have at most 12 tiles, so one trip covers them.
@@ -1084,6 +1094,7 @@ struct WaveStateW {
   float m;         // the unit's reference max (q.k units)
   float l;         // this lane's part of the row sum
   float big;       // largest per-subtile probability sum of this lane (the bound check)
+  float qs;        // key offsets apply to this row: 1, or 0 for a padded query row under pair masking
 };
 
 // Probabilities of one 32-key subtile against the reference m (q.k units)
@@ -1141,12 +1152,12 @@ __device__ __forceinline__ PadClass classify_pad(const PadWords& w) {
 }
 
 // The per-key offsets of a mixed subtile, added to the score accumulator by
-// one fp32 32x32x2 MFMA (as in apply_pad()).
-__device__ __forceinline__ void add_pad_bias(f32x16& acc, uint32_t mixed, int lane) {
+// one fp32 32x32x2 MFMA (as in apply_pad(), with its per-query factor qs).
+__device__ __forceinline__ void add_pad_bias(f32x16& acc, uint32_t mixed, int lane, float qs) {
   const int j = lane & 31;
   const bool lo = lane < 32;
   const bool padded = (mixed >> perm_row(j)) & 1u;
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? 1.0f : 0.0f, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? qs : 0.0f, acc, 0, 0, 0);
 }
 
 // 64-key tile id of entry i of a unit's tile list (block-level list, TPB
@@ -1159,9 +1170,9 @@ __device__ __forceinline__ int tile64_at(const TileList& tl, int i) {
 
 // Scores of one 32-key subtile read straight from global memory (the slow
 // path): S^T = K Q^T with K rows perm_row-ordered as in scores(), the
-// subtile's pad offsets added per key in fp32.
+// subtile's pad offsets added per key in fp32 (times the row's factor qs).
 __device__ __forceinline__ f32x16 scores_global(const char* kt, const uint8_t* pt, const u32x4 (&qop)[4], int kbase,
-                                                int lane) {
+                                                int lane, float qs) {
   const int j = lane & 31, g = lane >> 5;
   const char* krow = kt + (kbase + perm_row(j)) * (kD * 2);
   f32x16 acc;
@@ -1173,7 +1184,7 @@ __device__ __forceinline__ f32x16 scores_global(const char* kt, const uint8_t* p
   if (pt != nullptr) {
 #pragma unroll
     for (int v = 0; v < 16; ++v)   // element v holds key kbase + 16 (v / 8) + 8 g + v % 8
-      if (pt[kbase + 16 * (v >> 3) + 8 * g + (v & 7)] == 0) acc[v] += kMaskRaw;
+      if (pt[kbase + 16 * (v >> 3) + 8 * g + (v & 7)] == 0) acc[v] += kMaskRaw * qs;
   }
   return acc;
 }
@@ -1198,7 +1209,7 @@ __device__ __forceinline__ void redo_unit_w(WaveStateW& ws, const Unit& cu, int 
     const int t = tile64_at<TPB>(cu.tl, i >> 1), kb = 32 * (i & 1);
     const char* kt = kbh + static_cast<size_t>(t) * kTile64;
     const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
-    lm = lane_max(scores_global(kt, pt, q, kb, lane), lm);
+    lm = lane_max(scores_global(kt, pt, q, kb, lane, ws.qs), lm);
   }
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
   ws.m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -1215,7 +1226,7 @@ __device__ __forceinline__ void redo_unit_w(WaveStateW& ws, const Unit& cu, int 
     const int t = tile64_at<TPB>(cu.tl, i >> 1), kb = 32 * (i & 1);
     const char* kt = kbh + static_cast<size_t>(t) * kTile64;
     const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
-    const f32x16 s = scores_global(kt, pt, q, kb, lane);
+    const f32x16 s = scores_global(kt, pt, q, kb, lane, ws.qs);
     bf16x8 pb[2];
     ws.l += probs_w(s, ws.m, 0.0f, pb);
     // V^T operand: dim dh*32 + perm_row(j), keys kb + 16 mm + 8 g + e (e = 0..7),
@@ -1392,7 +1403,8 @@ __device__ __forceinline__ void step_n(WaveStateW& ws, u32x4 (&qop)[4], bool las
   c.mixed = 0u;
   if constexpr (HAS_PAD) {
     c = classify_pad(pw);
-    if (c.mixed) add_pad_bias(s, c.mixed, lane);
+    if (c.mixed) add_pad_bias(s, c.mixed, lane, ws.qs);
+    c.bias *= ws.qs;
   }
   if (S == 1 && last && nx.pf) {
     // Q is dead after the score products: refill it for the next unit
@@ -1475,6 +1487,10 @@ __device__ __forceinline__ void run_n(int n_units) {
     ws.m = -__builtin_inff();
     ws.l = 0.0f;
     ws.big = 0.0f;
+    ws.qs = 1.0f;
+    if constexpr (HAS_PAD) {
+      if (kargs()->qmask) ws.qs = pad_b[cu.q0 + wave * 32 + (lane_u & 31)] != 0 ? 1.0f : 0.0f;
+    }
 
     // trips of TRIP straight-line steps (TRIP / 2 tiles)
     constexpr int TRIP = 8;
@@ -2611,7 +2627,7 @@ int forward_impl(const void* q, const void* k, const void* v, const uint8_t* pad
                  size_t workspace_bytes, void* stream, unsigned flags, void* start_event, void* stop_event,
                  float* lse) {
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
-  if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE)) return BB_ERR_SHAPE;
+  if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE | BB_QUERY_MASK)) return BB_ERR_SHAPE;
   int nb = 0;
   const int st = check_shape(B, H, L, d, block, r, &nb);
   if (st != BB_OK) return st;
@@ -2645,6 +2661,7 @@ int forward_impl(const void* q, const void* k, const void* v, const uint8_t* pad
   a.nb = nb;
   a.r = r;
   a.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
+  a.qmask = (flags & BB_QUERY_MASK) && pad_mask != nullptr ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
   const bool p = pad_mask != nullptr;
@@ -2836,6 +2853,7 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   a.f.nb = nb;
   a.f.r = r;
   a.f.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
+  a.f.qmask = 0;
   a.o = static_cast<const char*>(out);
   a.dout = static_cast<const char*>(dout);
   a.lse = lse;

@@ -55,6 +55,15 @@ typedef enum { BB_FP32 = 0, BB_BF16 = 1 } bb_dtype;
                               follow a BB_PHASE_UNITS call with the same arguments and workspace
                               on the same stream */
                            /* neither phase bit, or both: the whole forward */
+#define BB_QUERY_MASK 8u   /* pair masking: an attended pair gets the -10000 offset when its query
+                              or its key is padding (default: when its key is).  Page "models 仓库中的
+                              BigBird：线性复杂度稀疏注意力与长序列训练的完整实践", section
+                              "随机块掩码是如何生成的": the layer receives the blocked mask and a band mask
+                              built from it by an einsum of the query and key sides.  Rows of valid
+                              queries are unchanged; a padded query row has the same offset on every
+                              pair, which cancels in its softmax: it is the unmasked attention row.
+                              No effect when pad_mask is NULL.  Forward output only (not
+                              bb_attn_forward_lse or the backward). */
 
 /* Version of this ABI (BB_ABI_VERSION of the built library). */
 int bb_abi_version(void);
@@ -172,9 +181,10 @@ int bb_attn_forward_noalloc(const void* q, const void* k, const void* v, const u
                             void* out, int dtype, void* stream);
 
 /* bb_attn_forward with flags: a launch mode (BB_LAUNCH_FUSED or BB_LAUNCH_SPLIT,
- * which give the same result bit for bit) and optionally one phase
+ * which give the same result bit for bit), optionally one phase
  * (BB_PHASE_UNITS or BB_PHASE_MERGE) for callers that time the phases or
- * enqueue other work between them.  Unknown flags: BB_ERR_SHAPE. */
+ * enqueue other work between them, and optionally BB_QUERY_MASK (the pair
+ * masking variant).  Unknown flags: BB_ERR_SHAPE. */
 int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
                        const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
                        void* out, int dtype, void* workspace, size_t workspace_bytes,

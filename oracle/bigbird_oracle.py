@@ -132,11 +132,27 @@ def _mask_rows(adj: np.ndarray, block: int, rows: np.ndarray) -> np.ndarray:
     return np.repeat(adj[rows // block], block, axis=1)
 
 
-def attention_rows(q_bh, k_bh, v_bh, pad_b, adj, block: int, rows) -> np.ndarray:
+def pair_masked(pad_b, rows, query_mask: bool) -> np.ndarray:
+    """Which (query row, key) pairs get the offset: bool [len(rows), L].
+
+    [P2-randmask]: the layer receives the blocked mask and a band mask made
+    from it by an einsum, i.e. from the validity of the query side and of
+    the key side.  Default (key side only): a pair is masked when its key
+    is padding.  query_mask=True: when its query or its key is padding.
+    """
+    key_pad = np.asarray(pad_b) == 0
+    m = np.broadcast_to(key_pad[None, :], (len(rows), key_pad.size))
+    if query_mask:
+        m = m | key_pad[np.asarray(rows)][:, None]
+    return m
+
+
+def attention_rows(q_bh, k_bh, v_bh, pad_b, adj, block: int, rows, query_mask: bool = False) -> np.ndarray:
     """Output rows `rows` of one (batch, head): fp64 [len(rows), d].
 
     q_bh/k_bh/v_bh: [L, d]; pad_b: [L] (nonzero = valid token) or None;
     adj: the head's block adjacency.  Dense masked softmax attention in fp64.
+    query_mask: the offset on pairs whose query or key is padding (pair_masked).
     """
     q = np.asarray(q_bh, dtype=np.float64)
     k = np.asarray(k_bh, dtype=np.float64)
@@ -145,8 +161,7 @@ def attention_rows(q_bh, k_bh, v_bh, pad_b, adj, block: int, rows) -> np.ndarray
     rows = np.asarray(rows, dtype=np.int64)
     s = (q[rows] @ k.T) / math.sqrt(d)
     if pad_b is not None:
-        padded = (np.asarray(pad_b) == 0).astype(np.float64)
-        s = s + MASK_OFFSET * padded[None, :]
+        s = s + MASK_OFFSET * pair_masked(pad_b, rows, query_mask).astype(np.float64)
     allowed = _mask_rows(adj, block, rows)
     s = np.where(allowed, s, -np.inf)
     s = s - s.max(axis=1, keepdims=True)
@@ -170,13 +185,14 @@ def attention_probs(q_bh, k_bh, pad_b, adj, block: int) -> np.ndarray:
 
 
 def attention_forward(q, k, v, pad_mask, rand_idx, block: int,
-                      row_group: int = 4096, units=None) -> np.ndarray:
+                      row_group: int = 4096, units=None, query_mask: bool = False) -> np.ndarray:
     """BigBird block-sparse attention forward in fp64.
 
     q, k, v: [B, H, L, d] (any real dtype; upcast to fp64 exactly as given);
     pad_mask: [B, L] (nonzero = valid) or None (no padding);
     rand_idx: [H, nb-2, r] integer table (validated first).
     units: optional iterable of (b, h) pairs to evaluate; other units are NaN.
+    query_mask: pairs are masked when the query or the key is padding.
     Returns fp64 [B, H, L, d].
     """
     B, H, L, d = np.shape(q)
@@ -195,20 +211,20 @@ def attention_forward(q, k, v, pad_mask, rand_idx, block: int,
         for r0 in range(0, L, row_group):
             rows = np.arange(r0, min(L, r0 + row_group))
             out[b, h, rows] = attention_rows(q[b, h], k[b, h], v[b, h], pad_b,
-                                             adjs[h], block, rows)
+                                             adjs[h], block, rows, query_mask)
     return out
 
 
-def _logits_rows(q, k, pad_b, adj, block: int, rows) -> np.ndarray:
+def _logits_rows(q, k, pad_b, adj, block: int, rows, query_mask: bool = False) -> np.ndarray:
     """Scaled, biased logits of rows `rows`, -inf off the pattern: fp64 [len(rows), L]."""
     L, d = k.shape
     s = (q[rows] @ k.T) / math.sqrt(d)
     if pad_b is not None:
-        s = s + MASK_OFFSET * (np.asarray(pad_b) == 0).astype(np.float64)[None, :]
+        s = s + MASK_OFFSET * pair_masked(pad_b, rows, query_mask).astype(np.float64)
     return np.where(_mask_rows(adj, block, rows), s, -np.inf)
 
 
-def attention_lse(q, k, pad_mask, rand_idx, block: int, units=None) -> np.ndarray:
+def attention_lse(q, k, pad_mask, rand_idx, block: int, units=None, query_mask: bool = False) -> np.ndarray:
     """Row log-sum-exp of the logits over the allowed keys: fp64 [B, H, L].
 
     LSE_t = log sum_u exp(s_tu), natural log, s as in the forward.
@@ -226,7 +242,7 @@ def attention_lse(q, k, pad_mask, rand_idx, block: int, units=None) -> np.ndarra
         adj = block_adjacency(rand_idx[h], nb)
         pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
         s = _logits_rows(np.asarray(q[b, h], np.float64), np.asarray(k[b, h], np.float64),
-                         pad_b, adj, block, np.arange(L))
+                         pad_b, adj, block, np.arange(L), query_mask)
         m = s.max(axis=1, keepdims=True)
         out[b, h] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
     return out

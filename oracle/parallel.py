@@ -30,7 +30,7 @@ def host_workers() -> int:
 
 
 def forward_units(q, k, v, pad, rand_idx, block: int, units=None, workers: int = 0,
-                  out=None, rows_per_group: int = 0):
+                  out=None, rows_per_group: int = 0, query_mask: bool = False):
     """Oracle output of `units` ((b, h) pairs; default all) into `out`
     (float64 [B, H, L, d], allocated as NaN when None).  q, k, v: arrays
     [B, H, L, d] (any real dtype, upcast per unit); pad: [B, L] or None."""
@@ -53,7 +53,7 @@ def forward_units(q, k, v, pad, rand_idx, block: int, units=None, workers: int =
         pb = None if pad is None else np.asarray(pad[b])
         for r0 in range(0, L, group):
             rows = np.arange(r0, min(L, r0 + group))
-            out[b, h, rows] = attention_rows(qb, kb, vb, pb, adj[h], block, rows)
+            out[b, h, rows] = attention_rows(qb, kb, vb, pb, adj[h], block, rows, query_mask)
         return bh
 
     n = workers or host_workers()

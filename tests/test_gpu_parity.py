@@ -349,3 +349,42 @@ def test_errors_raise_before_launch(dev):
         bb.bb_attn_forward(dq.half(), dk.half(), dv.half(), None, ri, w.B, w.H, w.L, w.d, w.block,
                            w.r, out.half(), ws)
     torch.cuda.synchronize()
+
+
+# --------------------------------------------------- pair masking (flag) ---
+
+QMASK_CASES = [SMALL[6], SMALL[7], SMALL[11], SMALL[13], SMALL[16], SMALL[18], SMALL[19], SMALL[20], SMALL[21]]
+
+
+@pytest.mark.parametrize("w", QMASK_CASES, ids=[w.name for w in QMASK_CASES])
+def test_query_mask_flag_matches_oracle(dev, w):
+    """BB_QUERY_MASK: every output against the oracle's pair-masked attention;
+    the rows of valid queries are bit-identical to the default (key-only) call."""
+    say(f"case query mask {w.name}")
+    inputs = make_inputs(w)
+    plain, _, ri = run_gpu(w, dev, inputs=inputs)
+    got, _, _ = run_gpu(w, dev, flags=bb.BB_QUERY_MASK, inputs=inputs)
+    q, k, v, pad = inputs
+    exp = attention_forward(f64(q), f64(k), f64(v), pad.numpy(), ri, w.block, query_mask=True)
+    assert not np.isnan(got).any()
+    err = np.abs(got - exp).max()
+    valid = pad.numpy() != 0
+    same = all(np.array_equal(got[b][:, valid[b]], plain[b][:, valid[b]]) for b in range(w.B))
+    say(f"  max err {err:.3e}; valid query rows identical to the key-only call: {same}")
+    assert err <= TOL[w.dtype]
+    assert same
+
+
+def test_query_mask_flag_full_shape(dev):
+    """The padded 4 x 12 x 4096 shape with pair masking, every output."""
+    w = WORKLOADS["base_B4_H12_L4096_pad"]
+    say(f"case query mask {w.name}")
+    inputs = make_inputs(w)
+    got, _, ri = run_gpu(w, dev, flags=bb.BB_QUERY_MASK, inputs=inputs)
+    q, k, v, pad = inputs
+    exp = forward_units(q.float().numpy(), k.float().numpy(), v.float().numpy(), pad.numpy(), ri, w.block,
+                        query_mask=True)
+    assert not np.isnan(got).any()
+    err = np.abs(got - exp).max()
+    say(f"  max err {err:.3e}")
+    assert err <= TOL[w.dtype]

@@ -18,6 +18,7 @@ import torch
 
 from oracle import (
     attention_forward,
+    attention_lse,
     attention_probs,
     block_adjacency,
     check_rand_idx,
@@ -51,8 +52,9 @@ def allowed_pred(t, u, block, nb, rand_row_of):
     return bu in rand_row_of(bt)         # random blocks of this middle block
 
 
-def brute_force(q, k, v, pad, rand_idx_h, block):
-    """Pure-Python loops with math.exp, one (batch, head)."""
+def brute_force(q, k, v, pad, rand_idx_h, block, query_mask=False):
+    """Pure-Python loops with math.exp, one (batch, head).  query_mask: a pair
+    gets the offset when its query or its key is padding."""
     L, d = len(q), len(q[0])
     nb = L // block
     rows = {i: set(int(x) for x in rand_idx_h[i - 1]) for i in range(1, nb - 1)}
@@ -63,7 +65,7 @@ def brute_force(q, k, v, pad, rand_idx_h, block):
             if not allowed_pred(t, u, block, nb, lambda b: rows[b]):
                 continue
             s = sum(q[t][c] * k[u][c] for c in range(d)) / math.sqrt(d)
-            if pad is not None and pad[u] == 0:
+            if pad is not None and (pad[u] == 0 or (query_mask and pad[t] == 0)):
                 s += -10000.0
             logits.append((u, s))
         m = max(s for _, s in logits)
@@ -400,3 +402,59 @@ def test_check_rand_idx_cap_boundary():
             check_rand_idx(table([4, outside]), 1, L, block, r, last_idx=last_idx)
     # no cap (last_idx = 0): the whole middle range, up to block nb - 2 = 18
     check_rand_idx(table([18, 4]), 1, L, block, r)
+
+
+# --------------------------------------------- query-side (pair) masking ---
+# Page "models 仓库中的 BigBird…", section on the random mask: the layer gets
+# the blocked [B, L] mask and a band mask built from it by an einsum (query
+# side x key side).  With query_mask the offset goes on every pair whose
+# query or key is padding.
+
+@pytest.mark.parametrize("block,nb,r,d", [(1, 5, 0, 2), (2, 6, 1, 2), (1, 8, 3, 2), (4, 5, 0, 3),
+                                          (1, 10, 5, 2)])
+def test_query_mask_brute_force_tiny(block, nb, r, d):
+    rng = np.random.default_rng(5000 + 7 * nb + block + 31 * r)
+    B, H, L = 2, 2, nb * block
+    q, k, v = rand_inputs(rng, B, H, L, d, scale=1.5)
+    ri = sample_rand_idx(rng, H, nb, r)
+    pad = np.ones((B, L), dtype=np.uint8)
+    pad[0, L - max(1, L // 3):] = 0
+    pad[1, rng.choice(L, size=max(1, L // 4), replace=False)] = 0
+    pad[:, 0] = 1
+    out = attention_forward(q, k, v, pad, ri, block, query_mask=True)
+    for b in range(B):
+        for h in range(H):
+            exp = brute_force(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), pad[b].tolist(), ri[h],
+                              block, query_mask=True)
+            np.testing.assert_allclose(out[b, h], exp, rtol=0, atol=1e-12)
+
+
+def test_query_mask_valid_rows_unchanged_padded_rows_unmasked():
+    """Closed forms of the pair rule: a valid query row is masked exactly as by
+    the key-only rule (the same logits, bit for bit); on a padded query row
+    every allowed logit gets the same offset, which cancels, so the row is
+    the unmasked attention row; its log-sum-exp is the unmasked one - 10000."""
+    rng = np.random.default_rng(77)
+    B, H, nb, block, r, d = 2, 3, 9, 4, 3, 3
+    L = nb * block
+    q, k, v = rand_inputs(rng, B, H, L, d, scale=1.5)
+    ri = sample_rand_idx(rng, H, nb, r)
+    pad = np.ones((B, L), dtype=np.uint8)
+    pad[0, 23:] = 0                                          # ragged suffix
+    pad[1, rng.choice(L, size=12, replace=False)] = 0       # holes
+    pad[:, 0] = 1
+    pm = attention_forward(q, k, v, pad, ri, block, query_mask=True)
+    km = attention_forward(q, k, v, pad, ri, block)
+    um = attention_forward(q, k, v, None, ri, block)
+    for b in range(B):
+        valid = pad[b] != 0
+        assert np.array_equal(pm[b][:, valid], km[b][:, valid])
+        np.testing.assert_allclose(pm[b][:, ~valid], um[b][:, ~valid], rtol=0, atol=1e-9)
+        assert np.abs(pm[b][:, ~valid] - km[b][:, ~valid]).max() > 1e-3   # the rule changes them
+    lp = attention_lse(q, k, pad, ri, block, query_mask=True)
+    lk = attention_lse(q, k, pad, ri, block)
+    lu = attention_lse(q, k, None, ri, block)
+    for b in range(B):
+        valid = pad[b] != 0
+        assert np.array_equal(lp[b][:, valid], lk[b][:, valid])
+        np.testing.assert_allclose(lp[b][:, ~valid], lu[b][:, ~valid] - 10000.0, rtol=0, atol=1e-8)
