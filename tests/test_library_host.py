@@ -166,7 +166,7 @@ def fwd(lib, q=FAKE, k=2 * FAKE, v=3 * FAKE, pad=None, rand=4 * FAKE, B=2, H=3, 
 
 def test_forward_validation_errors(lib):
     assert fwd(lib, dtype=7) == 3                       # BB_ERR_DTYPE
-    assert fwd(lib, flags=8) == 2                       # unknown flags
+    assert fwd(lib, flags=32) == 2                      # unknown flags (8 is BB_QUERY_MASK)
     assert fwd(lib, flags=16 | 1) == 2
     assert fwd(lib, d=128) == 2
     assert fwd(lib, block=32) == 2
