@@ -8,6 +8,9 @@
 `--pass layer` times bb_layer_forward: the QKV projection, the attention and
 the output projection of the layer (hidden = H*64, synthetic weights); its
 useful FLOPs add 2*M*N*K per projection (M = B*L) to the attention's.
+`--pass stack` times bb_layer_stack_forward over --layers layers (default 12,
+BigBird-base's depth), layer l with its own weights and the random table
+seeded with l; the layers feed each other, so the call is timed warm.
 
 `--pass backward` times bb_attn_backward instead (the default is the forward,
 the headline): one step = one backward call over the whole batch (the dQ
@@ -330,31 +333,43 @@ def cpu_baseline_backward(w, inputs, dout, ri, budget_s: float):
     return _baseline_fields(w, done, el, n, 2.5 * useful_flops(w), "backward")
 
 
-def bench_layer(args, w, dev):
-    """One JSON line for bb_layer_forward (see the module docstring)."""
+def bench_layer(args, w, dev, stack=False):
+    """One JSON line for bb_layer_forward, or with stack=True for
+    bb_layer_stack_forward over args.layers layers (see the module docstring)."""
     import torch
 
     from block_sparse_long_bigbird_amd import binding as bb
-    from block_sparse_long_bigbird_amd.workloads import make_layer_inputs
+    from block_sparse_long_bigbird_amd.workloads import make_layer_inputs, make_stack_weights
 
     hid = w.H * w.d
-    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
     x, w_qkv, b_qkv, w_o, b_o, pad = make_layer_inputs(w)
     dpad = None if pad is None else pad.to(dev)
-    dri = torch.from_numpy(ri).to(dev) if w.r > 0 else None
-    weights = [t.to(dev) for t in (w_qkv, b_qkv, w_o, b_o)]
+    n_layers = args.layers if stack else 1
+    if stack:
+        tables = [bb.bb_rand_idx_build(l, w.H, w.L, w.block, w.r) for l in range(n_layers)]
+        layers = [tuple(t.to(dev) for t in lw) + (torch.from_numpy(ri).to(dev) if w.r > 0 else None,)
+                  for lw, ri in zip(make_stack_weights(w, n_layers), tables)]
+        n = bb.bb_layer_stack_workspace_bytes(w.B, w.L, hid, w.H, w.block)
+    else:
+        ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+        dri = torch.from_numpy(ri).to(dev) if w.r > 0 else None
+        weights = [t.to(dev) for t in (w_qkv, b_qkv, w_o, b_o)]
+        n = bb.bb_layer_workspace_bytes(w.B, w.L, hid, w.H, w.block)
     x0 = x.to(dev)
     footprint = 2 * x0.numel() * x0.element_size()
-    n_sets = 1 if args.mode == "warm" else max(2, math.ceil(2.1 * LLC_BYTES / footprint))
+    n_sets = 1 if args.mode == "warm" or stack else max(2, math.ceil(2.1 * LLC_BYTES / footprint))
     sets = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0)) for i in range(n_sets)]
-    n = bb.bb_layer_workspace_bytes(w.B, w.L, hid, w.H, w.block)
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def call(i):
         xi, yi = sets[i % n_sets]
-        bb.bb_layer_forward(xi, *weights, dpad, dri, w.B, w.L, hid, w.H, w.block, w.r, yi, ws,
-                            stream=stream.cuda_stream)
+        if stack:
+            bb.bb_layer_stack_forward(xi, layers, dpad, w.B, w.L, hid, w.H, w.block, w.r, yi, ws,
+                                      stream=stream.cuda_stream)
+        else:
+            bb.bb_layer_forward(xi, *weights, dpad, dri, w.B, w.L, hid, w.H, w.block, w.r, yi, ws,
+                                stream=stream.cuda_stream)
 
     for i in range(args.warmup):
         call(i)
@@ -367,11 +382,13 @@ def bench_layer(args, w, dev):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     M = w.B * w.L
-    proj = 2 * M * (3 * hid) * hid + 2 * M * hid * hid
-    flops = useful_flops(w) + proj
+    proj = n_layers * (2 * M * (3 * hid) * hid + 2 * M * hid * hid)
+    flops = n_layers * useful_flops(w) + proj
     value = flops / (ms * 1e-3) / 1e12
+    what = (f"stack of {n_layers} attention layers, per-layer random tables" if stack
+            else "attention layer")
     out = {
-        "metric": f"useful TFLOP/s, BigBird attention layer fwd (projections + attn) L={w.L} hidden={w.H * w.d} bf16, 1 GPU",
+        "metric": f"useful TFLOP/s, BigBird {what} fwd (projections + attn) L={w.L} hidden={w.H * w.d} bf16, 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "tokens_per_s": round(w.tokens / (ms * 1e-3), 1),
@@ -384,11 +401,14 @@ def bench_layer(args, w, dev):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/hidden) weights)",
-        "config": {"workload": w.name, "pass": "layer", "B": w.B, "L": w.L, "hidden": hid, "H": w.H,
-                   "block": w.block, "r": w.r, "pad": w.pad, "mode": args.mode, "input_sets": n_sets,
+        "config": {"workload": w.name, "pass": "stack" if stack else "layer", "layers": n_layers,
+                   "B": w.B, "L": w.L, "hidden": hid, "H": w.H,
+                   "block": w.block, "r": w.r, "pad": w.pad, "mode": "warm" if stack else args.mode,
+                   "input_sets": n_sets,
                    "useful_gflop_per_step": round(flops / 1e9, 4),
                    "projection_gflop_per_step": round(proj / 1e9, 4)},
-        "roofline": {"bound": "mfma", "kernel": "whole layer call (2 projections + attention)",
+        "roofline": {"bound": "mfma",
+                     "kernel": f"whole {'stack' if stack else 'layer'} call (2 projections + attention per layer)",
                      "achieved": round(value, 3), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
                      "frac": round(value / PEAK_TFLOPS["bf16"], 4), "traffic": None},
         "cpu_baseline": None,
@@ -496,7 +516,10 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--pmc-mfma-summary", metavar="COUNTER_CSV")
     ap.add_argument("--command", default="", help="profiling command recorded by --pmc-summary")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "layer"], default="forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "layer", "stack"],
+                    default="forward")
+    ap.add_argument("--layers", type=int, default=12,
+                    help="layers in the --pass stack call (BigBird-base has 12)")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -525,8 +548,8 @@ def main():
     if args.which == "backward":
         bench_backward(args, w, dev)
         return
-    if args.which == "layer":
-        bench_layer(args, w, dev)
+    if args.which in ("layer", "stack"):
+        bench_layer(args, w, dev, stack=args.which == "stack")
         return
     launch = bb.BB_LAUNCH_SPLIT if args.launch == "split" else bb.BB_LAUNCH_FUSED
 

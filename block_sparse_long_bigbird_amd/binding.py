@@ -35,7 +35,8 @@ EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_
            "bb_attn_workspace_bytes", "bb_attn_forward", "bb_attn_forward_ex",
            "bb_attn_forward_timed", "bb_attn_forward_lse", "bb_rand_idx_invert",
            "bb_attn_backward_workspace_bytes", "bb_attn_backward", "bb_layer_workspace_bytes",
-           "bb_layer_forward", "bb_attn_forward_noalloc")
+           "bb_layer_forward", "bb_attn_forward_noalloc", "bb_layer_stack_workspace_bytes",
+           "bb_layer_stack_forward")
 
 _lib = None
 
@@ -96,6 +97,10 @@ def lib():
     L.bb_layer_workspace_bytes.argtypes = [c_int] * 5
     L.bb_layer_forward.restype = c_int
     L.bb_layer_forward.argtypes = [vp] * 7 + [c_int] * 6 + [vp, c_int, vp, c_size, vp]
+    L.bb_layer_stack_workspace_bytes.restype = c_size
+    L.bb_layer_stack_workspace_bytes.argtypes = [c_int] * 5
+    L.bb_layer_stack_forward.restype = c_int
+    L.bb_layer_stack_forward.argtypes = [vp] * 7 + [c_int] * 7 + [vp, c_int, vp, c_size, vp]
     _lib = L
     return L
 
@@ -494,3 +499,44 @@ def bb_layer_forward(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, B: int, L: i
                                 _ptr(workspace), ws_bytes, _stream_handle(x, stream))
     if st != BB_OK:
         raise BBError(st, "bb_layer_forward")
+
+
+def bb_layer_stack_workspace_bytes(B: int, L: int, hidden: int, H: int, block: int) -> int:
+    return int(lib().bb_layer_stack_workspace_bytes(B, L, hidden, H, block))
+
+
+def bb_layer_stack_forward(x, layers, pad_mask, B: int, L: int, hidden: int, H: int, block: int, r: int,
+                           y, workspace, stream=None) -> None:
+    """Enqueue a stack of attention layers.  layers: a sequence of
+    (w_qkv, b_qkv, w_o, b_o, rand_idx) per layer, each as bb_layer_forward
+    takes it (rand_idx an int32 device table, None when r == 0)."""
+    import torch
+    n = len(layers)
+    if n < 1:
+        raise ValueError("a stack needs at least one layer")
+    _expect("x", x, (B, L, hidden), (x.dtype,))
+    _expect("y", y, (B, L, hidden), (x.dtype,))
+    tables = []
+    for i, (w_qkv, b_qkv, w_o, b_o, ri) in enumerate(layers):
+        _expect(f"layer {i} w_qkv", w_qkv, (3 * hidden, hidden), (x.dtype,))
+        _expect(f"layer {i} b_qkv", b_qkv, (3 * hidden,), (torch.float32,))
+        _expect(f"layer {i} w_o", w_o, (hidden, hidden), (x.dtype,))
+        _expect(f"layer {i} b_o", b_o, (hidden,), (torch.float32,))
+        tables.append(_check_pad_and_table(pad_mask, ri, B, H, L, block, r))
+        for name, t in (("w_qkv", w_qkv), ("b_qkv", b_qkv), ("w_o", w_o), ("b_o", b_o), ("rand_idx", ri)):
+            _check_device_tensor(f"layer {i} {name}", t)
+    for name, t in (("x", x), ("pad_mask", pad_mask), ("y", y), ("workspace", workspace)):
+        _check_device_tensor(name, t)
+    for (w_qkv, b_qkv, w_o, b_o, ri), table in zip(layers, tables):
+        if table:
+            _check_rand_idx_contents(ri, H, L, block, r)
+
+    def arr(i):
+        return (ctypes.c_void_p * n)(*[layers[j][i].data_ptr() if layers[j][i] is not None else None
+                                       for j in range(n)])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().bb_layer_stack_forward(_ptr(x), arr(0), arr(1), arr(2), arr(3), _ptr(pad_mask),
+                                      arr(4) if r > 0 else None, n, B, L, hidden, H, block, r, _ptr(y),
+                                      _dtype_code(x), _ptr(workspace), ws_bytes, _stream_handle(x, stream))
+    if st != BB_OK:
+        raise BBError(st, "bb_layer_stack_forward")

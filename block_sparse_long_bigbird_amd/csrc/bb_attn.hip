@@ -2520,6 +2520,12 @@ bool overlap(const void* a, const void* b, size_t n) {
   return x < y + n && y < x + n;
 }
 
+// [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 // Persistent grid for a kernel: as many workgroups as the current device
 // holds at once, at most one per unit, rounded down to a multiple of 8 (the
 // XCD count) so that every XCD runs the same number.
@@ -2912,12 +2918,13 @@ extern "C" size_t bb_layer_workspace_bytes(int B, int L, int hidden, int H, int 
   return layer_layout(B, L, hidden, H, block).total;
 }
 
-extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b_qkv, const void* w_o,
-                                const float* b_o, const uint8_t* pad_mask, const int32_t* rand_idx, int B, int L,
-                                int hidden, int H, int block, int r, void* y, int dtype, void* workspace,
-                                size_t workspace_bytes, void* stream) {
-  if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
-  if (dtype != BB_BF16) return BB_ERR_DTYPE;
+namespace {
+
+// Checks of one layer's arguments (no HIP call); BB_OK means layer_launch may run.
+int layer_check(const void* x, const void* w_qkv, const float* b_qkv, const void* w_o, const float* b_o,
+                const uint8_t* pad_mask, const int32_t* rand_idx, int B, int L, int hidden, int H, int block, int r,
+                const void* y, int dtype, const void* workspace, size_t workspace_bytes, size_t need) {
+  if (dtype != BB_BF16) return BB_ERR_DTYPE;   // the layer runs in bf16 only
   const int st = check_layer(B, L, hidden, H, block, r);
   if (st != BB_OK) return st;
   if (B == 0) return BB_OK;
@@ -2929,10 +2936,16 @@ extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b
     return BB_ERR_ALIGN;
   const size_t xbytes = static_cast<size_t>(B) * L * hidden * 2;
   if (overlap(y, x, xbytes)) return BB_ERR_ALIAS;
+  if (workspace_bytes < need) return BB_ERR_WORKSPACE;
+  return BB_OK;
+}
+
+// One layer on `stream` (arguments checked by layer_check): the QKV
+// projection into the workspace, the attention, the output projection into y.
+int layer_launch(const void* x, const void* w_qkv, const float* b_qkv, const void* w_o, const float* b_o,
+                 const uint8_t* pad_mask, const int32_t* rand_idx, int B, int L, int hidden, int H, int block, int r,
+                 void* y, char* ws, size_t workspace_bytes, hipStream_t s) {
   const LayerLayout w = layer_layout(B, L, hidden, H, block);
-  if (workspace_bytes < w.total) return BB_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int M = B * L;
   ProjArgs pa{};
   pa.a = static_cast<const char*>(x);
@@ -2948,7 +2961,7 @@ extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b
   launch_proj<0>(pa, s);
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   const int fst = forward_impl(ws + w.q, ws + w.k, ws + w.v, pad_mask, rand_idx, B, H, L, kD, block, r, ws + w.o,
-                               BB_BF16, ws + w.attn, workspace_bytes - w.attn, stream, BB_LAUNCH_FUSED, nullptr,
+                               BB_BF16, ws + w.attn, workspace_bytes - w.attn, s, BB_LAUNCH_FUSED, nullptr,
                                nullptr, nullptr);
   if (fst != BB_OK) return fst;
   ProjArgs po = pa;
@@ -2959,5 +2972,66 @@ extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b
   po.N = hidden;
   launch_proj<1>(po, s);
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+  return BB_OK;
+}
+
+}  // namespace
+
+extern "C" int bb_layer_forward(const void* x, const void* w_qkv, const float* b_qkv, const void* w_o,
+                                const float* b_o, const uint8_t* pad_mask, const int32_t* rand_idx, int B, int L,
+                                int hidden, int H, int block, int r, void* y, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const size_t need = check_layer(B, L, hidden, H, block, r) == BB_OK && B > 0
+                          ? layer_layout(B, L, hidden, H, block).total : 0;
+  const int st = layer_check(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, B, L, hidden, H, block, r, y, dtype,
+                             workspace, workspace_bytes, need);
+  if (st != BB_OK || B == 0) return st;
+  return layer_launch(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, B, L, hidden, H, block, r, y,
+                      static_cast<char*>(workspace), workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------- layer stack --
+
+extern "C" size_t bb_layer_stack_workspace_bytes(int B, int L, int hidden, int H, int block) {
+  const size_t one = bb_layer_workspace_bytes(B, L, hidden, H, block);
+  if (one == 0) return 0;
+  return align256(one) + static_cast<size_t>(B) * L * hidden * 2;
+}
+
+extern "C" int bb_layer_stack_forward(const void* x, const void* const* w_qkv, const float* const* b_qkv,
+                                      const void* const* w_o, const float* const* b_o, const uint8_t* pad_mask,
+                                      const int32_t* const* rand_idx, int n_layers, int B, int L, int hidden,
+                                      int H, int block, int r, void* y, int dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (n_layers < 0) return BB_ERR_SHAPE;
+  if (dtype != BB_BF16) return BB_ERR_DTYPE;   // the layer runs in bf16 only
+  int st = check_layer(B, L, hidden, H, block, r);
+  if (st != BB_OK) return st;
+  if (B == 0 || n_layers == 0) return n_layers == 0 && B > 0 ? BB_ERR_SHAPE : BB_OK;
+  if (!w_qkv || !b_qkv || !w_o || !b_o || (r > 0 && !rand_idx)) return BB_ERR_NULL;
+  const size_t one = layer_layout(B, L, hidden, H, block).total;
+  const size_t act_off = align256(one);
+  const size_t need = act_off + static_cast<size_t>(B) * L * hidden * 2;
+  if (workspace == nullptr) return BB_ERR_NULL;
+  char* act = static_cast<char*>(workspace) + act_off;   // the activations between layers
+  // layer l writes y when n_layers - 1 - l is even, else act: the last layer
+  // writes y and consecutive layers alternate
+  auto out_of = [&](int l) -> void* { return ((n_layers - 1 - l) & 1) == 0 ? y : static_cast<void*>(act); };
+  for (int l = 0; l < n_layers; ++l) {   // every check before the first launch
+    const void* in = l == 0 ? x : out_of(l - 1);
+    st = layer_check(in, w_qkv[l], b_qkv[l], w_o[l], b_o[l], pad_mask, r > 0 ? rand_idx[l] : nullptr, B, L,
+                     hidden, H, block, r, out_of(l), dtype, workspace, workspace_bytes, need);
+    if (st != BB_OK) return st;
+  }
+  const size_t xbytes = static_cast<size_t>(B) * L * hidden * 2;
+  if (overlap(y, x, xbytes) || overlap(workspace, need, x, xbytes) || overlap(workspace, need, y, xbytes))
+    return BB_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < n_layers; ++l) {
+    st = layer_launch(l == 0 ? x : out_of(l - 1), w_qkv[l], b_qkv[l], w_o[l], b_o[l], pad_mask,
+                      r > 0 ? rand_idx[l] : nullptr, B, L, hidden, H, block, r, out_of(l),
+                      static_cast<char*>(workspace), one, s);
+    if (st != BB_OK) return st;
+  }
   return BB_OK;
 }

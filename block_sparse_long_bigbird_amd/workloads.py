@@ -227,3 +227,23 @@ def make_layer_inputs(w: Workload):
     return (torch.from_numpy(x).to(bf), torch.from_numpy(w_qkv).to(bf), torch.from_numpy(b_qkv),
             torch.from_numpy(w_o).to(bf), torch.from_numpy(b_o),
             None if pad is None else torch.from_numpy(pad))
+
+
+def make_stack_weights(w: Workload, n_layers: int):
+    """Per-layer projection weights for a stack of n_layers attention layers of
+    a workload's shape: layer l draws (w_qkv, b_qkv, w_o, b_o) as
+    make_layer_inputs does, from its own stream (PCG64 seeded with
+    data_seed + 3000 + l).  CPU torch tensors, weights bf16, biases float32."""
+    import torch
+    hid = w.H * w.d
+    s = np.float32(1.0 / np.sqrt(hid))
+    out = []
+    for l in range(n_layers):
+        rng = np.random.Generator(np.random.PCG64(w.data_seed + 3000 + l))
+        w_qkv = rng.standard_normal((3 * hid, hid), dtype=np.float32) * s
+        b_qkv = rng.standard_normal(3 * hid, dtype=np.float32) * np.float32(0.02)
+        w_o = rng.standard_normal((hid, hid), dtype=np.float32) * s
+        b_o = rng.standard_normal(hid, dtype=np.float32) * np.float32(0.02)
+        out.append((torch.from_numpy(w_qkv).to(torch.bfloat16), torch.from_numpy(b_qkv),
+                    torch.from_numpy(w_o).to(torch.bfloat16), torch.from_numpy(b_o)))
+    return out

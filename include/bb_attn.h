@@ -299,6 +299,35 @@ int bb_layer_forward(const void* x, const void* w_qkv, const float* b_qkv, const
                      int block, int r, void* y, int dtype, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/*
+ * A stack of n_layers attention layers (bb_layer_forward's layer), each
+ * with its own weights and its own random-block table: the pages' encoder
+ * stacks its layers and seeds each layer's table with the layer's index
+ * (page "models 仓库中的 BigBird：线性复杂度稀疏注意力与长序列训练的完整实践",
+ * sections "随机块掩码是如何生成的" and "BigBirdEncoder 的关键参数").
+ *   h_0 = x;  h_l = layer_l(h_{l-1}) for l = 1..n_layers;  y = h_{n_layers}.
+ *   w_qkv, b_qkv, w_o, b_o, rand_idx
+ *              HOST arrays of n_layers DEVICE pointers, entry l for layer l+1,
+ *              each as bb_layer_forward takes it (rand_idx may be NULL when
+ *              r == 0).  Build table l with bb_rand_idx_build(seed = l, ...)
+ *              for the pages' convention.
+ *   n_layers   >= 1.
+ *   workspace  DEVICE, >= bb_layer_stack_workspace_bytes(): one layer's
+ *              workspace and one activation buffer [B][L][hidden] bf16.
+ *   y          must overlap neither x nor the workspace, which must not overlap
+ *              x (BB_ERR_ALIAS).
+ *   Everything else as bb_layer_forward (the same pad_mask for every layer).
+ * Activations between layers are stored as bf16.  Every argument of every
+ * layer is checked before the first launch; nothing is launched on an error.
+ * Asynchronous on `stream`.
+ */
+size_t bb_layer_stack_workspace_bytes(int B, int L, int hidden, int H, int block);
+int bb_layer_stack_forward(const void* x, const void* const* w_qkv, const float* const* b_qkv,
+                           const void* const* w_o, const float* const* b_o, const uint8_t* pad_mask,
+                           const int32_t* const* rand_idx, int n_layers, int B, int L, int hidden, int H,
+                           int block, int r, void* y, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,7 @@ from .bigbird_oracle import (  # noqa: F401
     check_rand_idx,
     layer_forward,
     layer_rows,
+    layer_stack_forward,
     num_blocks,
     token_mask,
 )

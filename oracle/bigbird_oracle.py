@@ -356,3 +356,18 @@ def layer_rows(x, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, H: int, block: int
             pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
             o[b, :, h, :] = attention_rows(q[b, h], k[b, h], v[b, h], pad_b, adj, block, rows)
     return o.reshape(B, len(rows), hid) @ np.asarray(w_o, np.float64).T + np.asarray(b_o, np.float64)
+
+
+def layer_stack_forward(x, layers, pad_mask, H: int, block: int) -> np.ndarray:
+    """A stack of attention layers, fp64: h_0 = x, h_l = layer_forward(h_{l-1})
+    with layer l's own weights and random-block table.
+
+    [P2] page, the encoder's construction: the layers are stacked and each
+    layer's random table is seeded with its index (the tables come in with
+    the layers here).  layers: a sequence of (w_qkv, b_qkv, w_o, b_o,
+    rand_idx), in order.  x: [B, L, hidden].  Returns fp64 [B, L, hidden].
+    """
+    h = np.asarray(x, dtype=np.float64)
+    for w_qkv, b_qkv, w_o, b_o, rand_idx in layers:
+        h = layer_forward(h, w_qkv, b_qkv, w_o, b_o, pad_mask, rand_idx, H, block)
+    return h

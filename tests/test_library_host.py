@@ -379,6 +379,38 @@ def test_layer_validation_errors(lib):
     assert layer(lib, B=0, x=0, y=0, ws=0) == 0
 
 
+def stack(lib, n=3, x=FAKE, y=7 * FAKE, ws=8 * FAKE, ws_bytes=1 << 30, entry=None, B=1, L=512, hidden=256,
+          H=4, block=64, r=3, dtype=1):
+    """bb_layer_stack_forward with placeholder pointers; entry = (array, layer,
+    value) replaces one pointer of one layer."""
+    P = ctypes.c_void_p
+    arrs = {name: [base + 16 * l * FAKE for l in range(n)]
+            for name, base in (("wqkv", 2 * FAKE), ("bqkv", 3 * FAKE), ("wo", 4 * FAKE), ("bo", 5 * FAKE),
+                               ("rand", 6 * FAKE))}
+    if entry is not None:
+        arrs[entry[0]][entry[1]] = entry[2]
+    c = {k: (P * max(n, 1))(*v) for k, v in arrs.items()}
+    return lib.bb_layer_stack_forward(P(x), c["wqkv"], c["bqkv"], c["wo"], c["bo"], None, c["rand"], n, B, L,
+                                      hidden, H, block, r, P(y), dtype, P(ws), ws_bytes, None)
+
+
+def test_layer_stack_validation_errors(lib):
+    one = lib.bb_layer_workspace_bytes(1, 512, 256, 4, 64)
+    need = lib.bb_layer_stack_workspace_bytes(1, 512, 256, 4, 64)
+    assert need == (one + 255) // 256 * 256 + 512 * 256 * 2
+    assert stack(lib, n=0) == 2
+    assert stack(lib, n=0, B=0) == 0
+    assert stack(lib, dtype=0) == 3
+    assert stack(lib, ws_bytes=need - 1) == 5
+    assert stack(lib, y=FAKE) == 7                                 # y over x
+    assert stack(lib, ws=FAKE - 256) == 7                          # workspace over x
+    assert stack(lib, ws=7 * FAKE - need + 256) == 7               # workspace over y
+    for name in ("wqkv", "bqkv", "wo", "bo", "rand"):              # a bad pointer in the last layer
+        assert stack(lib, entry=(name, 2, 0)) == 1, name
+    assert stack(lib, entry=("bqkv", 1, 3 * FAKE + 4)) == 8        # misaligned
+    assert stack(lib, r=7) == 2
+
+
 # ------------------------------------------- binding checks before any launch ---
 # The wrappers check shapes and dtypes of what the raw pointers stand for, then
 # that every tensor is on the device, then the table's contents: with host

@@ -7,13 +7,18 @@ attention), CPU only:
     same weights (independent library code), with the attention between them;
   - linearity in the output projection: scaling W_o and b_o scales y;
   - layer_rows (selected output rows, used for the full-size GPU check) against
-    the same torch.nn.functional.linear composition, row by row.
+    the same torch.nn.functional.linear composition, row by row;
+  - the layer stack: a layer whose q/k/v weights are zero attends with
+    constant keys and values, so every row's output is the value bias, and
+    the layer after it sees one constant row: closed forms for the whole
+    stack, worked out with plain matrix-vector products; one layer is the
+    layer itself; the order of the layers matters.
 """
 
 import numpy as np
 import torch
 
-from oracle import attention_forward, layer_forward, layer_rows
+from oracle import attention_forward, layer_forward, layer_rows, layer_stack_forward
 
 
 def sample_rand_idx(rng, H, nb, r):
@@ -89,3 +94,33 @@ def test_layer_rows_match_torch_linear_composition():
     got = layer_rows(x, w_qkv, b_qkv, w_o, b_o, pad, ri, H, 4, rows)
     assert got.shape == (B, len(rows), hid)
     assert np.abs(got - exp[:, rows]).max() <= 1e-12
+
+
+def test_layer_stack_closed_form_after_a_constant_layer():
+    """Layer 1 has zero q/k/v weights: its values are the bias b_v in every row,
+    softmax weights sum to one, so its output row is c = b_v W_o1^T + b_o1 for
+    every token.  Layer 2 then sees the constant row c: its values are
+    c W_v2^T + b_v2 in every row, so y = (c W_v2^T + b_v2) W_o2^T + b_o2 for every
+    token, whatever the masks and tables."""
+    rng = np.random.default_rng(9)
+    B, L, hid, H, block = 2, 48, 12, 3, 4
+    x = rng.standard_normal((B, L, hid))
+    pad = np.ones((B, L), dtype=np.uint8)
+    pad[0, 30:] = 0
+    layers = []
+    for i in range(2):
+        w_qkv = rng.standard_normal((3 * hid, hid)) / np.sqrt(hid)
+        if i == 0:
+            w_qkv[:] = 0.0
+        layers.append((w_qkv, rng.standard_normal(3 * hid), rng.standard_normal((hid, hid)),
+                       rng.standard_normal(hid), sample_rand_idx(rng, H, L // block, 2)))
+    (_, b1, wo1, bo1, _), (w2, b2, wo2, bo2, _) = layers
+    c = b1[2 * hid:] @ wo1.T + bo1
+    v2 = c @ w2[2 * hid:].T + b2[2 * hid:]
+    row = v2 @ wo2.T + bo2
+    y = layer_stack_forward(x, layers, pad, H, block)
+    assert np.abs(y - row[None, None, :]).max() <= 1e-10
+    # one layer is the layer; the other order gives another result
+    assert np.array_equal(layer_stack_forward(x, layers[:1], pad, H, block),
+                          layer_forward(x, *layers[0][:4], pad, layers[0][4], H, block))
+    assert np.abs(layer_stack_forward(x, layers[::-1], pad, H, block) - y).max() > 1e-3
