@@ -56,6 +56,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "useful TFLOP/s + tokens/s, BigBird attn fwd L=4096 H=12 d=64 bf16, 1 GPU"
+DEFAULT_WORKLOAD = "base_B4_H12_L4096_pad"   # the workload METRIC is quoted on
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBPS = 8000.0
 LLC_BYTES = 256 * 2**20
@@ -502,7 +503,7 @@ def main():
     # few milliseconds of load; with only 10 warm-up calls the timed region
     # starts below full clock and reads ~15% low.
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="base_B4_H12_L4096_pad")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--launch", choices=["fused", "split"], default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -575,11 +576,16 @@ def main():
         bb.bb_attn_forward(a, b_, c, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, o, ws,
                            stream=stream.cuda_stream, flags=flags, events=events)
 
+    # the timed calls: arguments checked once per input set (PreparedForward),
+    # so a small problem's call is not bounded by the host-side checks
+    prepared = [bb.PreparedForward(a, b_, c, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, o, ws,
+                                   stream=stream.cuda_stream, flags=launch) for a, b_, c, o in sets]
+
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
     for i in range(args.warmup):
-        call(i, launch)
+        prepared[i % n_sets]()
     torch.cuda.synchronize()
 
     # Pass 1 -- the timed region: K whole steps, device synchronised on both sides.
@@ -587,7 +593,7 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        call(i, launch)
+        prepared[i % n_sets]()
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
@@ -634,7 +640,8 @@ def main():
     traffic = committed_traffic(w.name) if args.launch == "fused" else None
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == DEFAULT_WORKLOAD else
+                  f"useful TFLOP/s + tokens/s, BigBird attn fwd L={w.L} H={w.H} d={w.d} {w.dtype}, 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "tokens_per_s": round(w.tokens / (ms_per_step * 1e-3), 1),

@@ -25,6 +25,7 @@ BB_LAUNCH_SPLIT = 1
 BB_PHASE_UNITS = 2
 BB_PHASE_MERGE = 4
 BB_QUERY_MASK = 8
+BB_ORDINARY_UNITS = 16
 STATUS_NAMES = {0: "BB_OK", 1: "BB_ERR_NULL", 2: "BB_ERR_SHAPE", 3: "BB_ERR_DTYPE",
                 4: "BB_ERR_RAND_IDX", 5: "BB_ERR_WORKSPACE", 6: "BB_ERR_HIP",
                 7: "BB_ERR_ALIAS", 8: "BB_ERR_ALIGN"}
@@ -284,6 +285,20 @@ def _check_qkv_out(B, H, L, d, q, rest):
         _expect(name, t, (B, H, L, d), (q.dtype,))
 
 
+def _forward_args(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, workspace, stream):
+    """Check the forward's arguments; the library call's argument tuple."""
+    _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out)))
+    table = _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("pad_mask", pad_mask),
+                    ("rand_idx", rand_idx), ("workspace", workspace)):
+        _check_device_tensor(name, t)
+    if table:
+        _check_rand_idx_contents(rand_idx, H, L, block, r)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx), B, H, L, d, block, r,
+            _ptr(out), _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(q, stream))
+
+
 def bb_attn_forward(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int,
                     r: int, out, workspace, stream=None, flags: int = BB_LAUNCH_FUSED,
                     events=None) -> None:
@@ -300,16 +315,7 @@ def bb_attn_forward(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int,
     the kernel launches themselves record (bb_attn_forward_timed); each must
     have been recorded once before, so that its HIP event exists.
     """
-    _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out)))
-    table = _check_pad_and_table(pad_mask, rand_idx, B, H, L, block, r)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("pad_mask", pad_mask),
-                    ("rand_idx", rand_idx), ("workspace", workspace)):
-        _check_device_tensor(name, t)
-    if table:
-        _check_rand_idx_contents(rand_idx, H, L, block, r)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx), B, H, L, d, block, r,
-            _ptr(out), _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(q, stream))
+    args = _forward_args(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, workspace, stream)
     if events is not None:
         e0, e1 = (int(e.cuda_event) for e in events)
         if not e0 or not e1:
@@ -321,6 +327,32 @@ def bb_attn_forward(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int,
         st = lib().bb_attn_forward_ex(*args, flags)
     if st != BB_OK:
         raise BBError(st, "bb_attn_forward")
+
+
+class PreparedForward:
+    """One bb_attn_forward call with its arguments checked once, at
+    construction; each call of the object enqueues it again with one ctypes
+    call and no Python-side checks.  For loops of small problems, where the
+    checks of bb_attn_forward take longer on the host than the kernels on the
+    device.  The object keeps its tensors alive; writing new values into them
+    between calls is the intended use (a rand_idx rewritten in place is not
+    checked again; the kernels clamp every table entry into the sequence)."""
+
+    def __init__(self, q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int, r: int,
+                 out, workspace, stream=None, flags: int = BB_LAUNCH_FUSED):
+        self._keep = (q, k, v, pad_mask, rand_idx, out, workspace)
+        self._args = _forward_args(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, workspace,
+                                   stream)
+        if flags == BB_LAUNCH_FUSED:
+            self._fn = lib().bb_attn_forward
+        else:
+            self._args = self._args + (flags,)
+            self._fn = lib().bb_attn_forward_ex
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != BB_OK:
+            raise BBError(st, "bb_attn_forward")
 
 
 def forward(q, k, v, rand_idx, pad_mask=None, block: int = 64, out=None, workspace=None,

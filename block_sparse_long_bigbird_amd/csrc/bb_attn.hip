@@ -111,6 +111,8 @@ struct Args {
   float* lse;      // [B*H][L] natural-log row log-sum-exp of the logits, or null (not written)
   int H, L, nb, r, n_s;
   int qmask;       // 1: pairs are masked when the query or the key is padding (pad != null)
+  int gc, mc;      // small-problem split (kind 3 units): key chunks per global / middle query
+                   // block; 0 when the call runs the ordinary units
 };
 
 // LDS ring: one object per (dtype, block, stage) holding that stage's K and V
@@ -478,11 +480,14 @@ struct TileList {
   int nwin;              // middle unit: band blocks inside 1..nb-2
   int nb;
   int global;            // 1: global unit, 0: middle unit
+  int skip;              // middle unit: position of its first tile in the block's list
+                         // (non-zero only for the key chunks of kind 3 units)
   const_i32_ptr rand;    // middle unit: its row of the random-block table
 };
 
 __device__ __forceinline__ int tile_at(const TileList& tl, int u) {
   if (tl.global) return tl.first + u;
+  u += tl.skip;
   if (u == 0) return 0;
   if (u <= tl.nwin) return tl.first + u - 1;
   if (u == tl.nwin + 1) return tl.nb - 1;
@@ -498,6 +503,12 @@ __device__ __forceinline__ int tile_at(const TileList& tl, int u) {
 // gsel < 0: a middle query block, finalised in place.  gsel in {0, 1}: global
 // query block 0 or nb-1 against one key chunk of the split-K, written as a
 // partial for the merge kernel.
+// kind 3 (problems with too few units to fill the chip): every query block is
+// split over its key tiles -- a->gc chunks per global block, a->mc per middle
+// block, each a contiguous run of the block's tile list -- and every unit
+// writes a partial (gsel 2 for the middle ones); the merge kernel then
+// combines the chunks of every query block.  Partial slots per (b, h):
+// [block 0 chunks | block nb-1 chunks | middle block 1 chunks | ...].
 struct Unit {
   size_t off;            // byte offset of (b, h) in q, k, v and out: bh * L * ROWB
   size_t pbase;          // global unit: partial row index of its first query row
@@ -519,6 +530,7 @@ __device__ __forceinline__ kargs_ptr kargs() {
 template <typename T, int BS, int kind>
 __device__ __forceinline__ int units_per_bh(kargs_ptr a) {
   constexpr int QS = Cfg<T, BS>::QSPLIT;
+  if constexpr (kind == 3) return (2 * a->gc + (a->nb - 2) * a->mc) * QS;
   return (kind == 2 ? 0 : 2 * a->n_s * QS) + (kind == 1 ? 0 : (a->nb - 2) * QS);
 }
 
@@ -563,11 +575,51 @@ __device__ __forceinline__ Unit decode_unit(kargs_ptr a, const Cursor& c) {
   constexpr int LQS = QS == 2 ? 1 : 0;
   static_assert(QS == 1 || QS == 2, "row slices per query block");
   const int nb = a->nb, n_s = a->n_s;
-  const int n_g = kind == 2 ? 0 : 2 * n_s * QS;
   Unit w;
   w.off = static_cast<size_t>(c.bh) * a->L * C::ROWB;
   w.b = c.b;
   w.tl.nb = nb;
+  w.tl.skip = 0;
+  if constexpr (kind == 3) {
+    const int gc = a->gc, mc = a->mc;
+    const size_t slots = static_cast<size_t>(2 * gc + (nb - 2) * mc);   // partial blocks per (b, h)
+    int slot, qb, qh;
+    if (c.u < 2 * gc * QS) {
+      const int half = gc * QS;
+      w.gsel = c.u >= half ? 1 : 0;
+      const int rem = c.u - (w.gsel ? half : 0);
+      const int chunk = rem >> LQS;
+      qh = rem & (QS - 1);
+      qb = w.gsel ? nb - 1 : 0;
+      slot = w.gsel * gc + chunk;
+      w.tl.global = 1;
+      w.tl.first = chunk * nb / gc;                // balanced chunks: none is empty (gc <= nb)
+      w.ntiles = (chunk + 1) * nb / gc - w.tl.first;
+      w.tl.nwin = 0;
+      w.tl.rand = nullptr;
+    } else {
+      const int v = (c.u - 2 * gc * QS) >> LQS;
+      qh = (c.u - 2 * gc * QS) & (QS - 1);
+      const int mi = v / mc, chunk = v - mi * mc;
+      qb = mi + 1;
+      w.gsel = 2;
+      slot = 2 * gc + mi * mc + chunk;
+      const int lo = qb - 1 < 1 ? 1 : qb - 1;
+      const int hi = qb + 1 > nb - 2 ? nb - 2 : qb + 1;
+      const int r = a->r;
+      w.tl.global = 0;
+      w.tl.first = lo;
+      w.tl.nwin = hi - lo + 1;
+      w.tl.rand = (const_i32_ptr)(a->rand_idx + (static_cast<size_t>(c.h) * (nb - 2) + (qb - 1)) * r);
+      const int nt = 2 + w.tl.nwin + r;            // mc <= the fewest tiles of any middle block
+      w.tl.skip = chunk * nt / mc;
+      w.ntiles = (chunk + 1) * nt / mc - w.tl.skip;
+    }
+    w.q0 = qb * BS + qh * C::QROWS;
+    w.pbase = (static_cast<size_t>(c.bh) * slots + slot) * BS + qh * C::QROWS;
+    return w;
+  }
+  const int n_g = kind == 2 ? 0 : 2 * n_s * QS;
   if (c.u < n_g) {
     const int half = n_s * QS;
     w.gsel = c.u >= half ? 1 : 0;
@@ -891,7 +943,10 @@ __device__ __forceinline__ void run(int n_units) {
       const Unit nu = decode_unit<T, BS, kind>(kargs(), nxt);
       nx.off = nu.off;
       nx.q0 = nu.q0;
-      nx.tile0 = nu.tl.global ? nu.tl.first : 0;
+      if constexpr (kind == 3)   // a chunk may start at a random block: read the table only
+        nx.tile0 = has_next ? tile_at(nu.tl, 0) : 0;   // for a unit that exists
+      else
+        nx.tile0 = nu.tl.global ? nu.tl.first : 0;
       nx.pf = has_next && (cu.ntiles & 1) == 0 ? 1 : 0;
       nx.unused = 0;
     }
@@ -979,7 +1034,10 @@ __device__ __forceinline__ void run(int n_units) {
 // order, so the result is deterministic.
 constexpr int kMergeSplit = 4;
 
-template <typename T, int BS>
+// ALL = false: the two global blocks of every (b, h), n_s chunks each.  ALL =
+// true (after kind 3 units): every query block, gc chunks for the global
+// blocks and mc for the middle ones (slot order of decode_unit).
+template <typename T, int BS, bool ALL>
 __global__ void __launch_bounds__(64 * kMergeSplit) bb_global_merge_kernel(Args a) {
   constexpr int ROWB = kD * sizeof(T);
   constexpr int UB = BS / 64;                                 // 64-row unit blocks per query block
@@ -989,18 +1047,31 @@ __global__ void __launch_bounds__(64 * kMergeSplit) bb_global_merge_kernel(Args 
   const int wq = (blockIdx.x >> 2) & 1;
   const int rest = blockIdx.x >> 3;
   const int qh = rest % UB, gblk = rest / UB;
-  const int bh = gblk >> 1, gsel = gblk & 1;
-  const int qb = gsel ? a.nb - 1 : 0;
+  int bh, qb, n_ch;
+  size_t base;
+  if constexpr (ALL) {
+    bh = gblk / a.nb;
+    qb = gblk - bh * a.nb;
+    const size_t slots = static_cast<size_t>(2 * a.gc + (a.nb - 2) * a.mc);
+    const int first = qb == 0 ? 0 : (qb == a.nb - 1 ? a.gc : 2 * a.gc + (qb - 1) * a.mc);
+    n_ch = qb == 0 || qb == a.nb - 1 ? a.gc : a.mc;
+    base = static_cast<size_t>(bh) * slots + first;
+  } else {
+    bh = gblk >> 1;
+    const int gsel = gblk & 1;
+    qb = gsel ? a.nb - 1 : 0;
+    n_ch = a.n_s;
+    base = (static_cast<size_t>(bh) * 2 + gsel) * a.n_s;
+  }
   const int cs = threadIdx.x >> 6, t = threadIdx.x & 63;
   const int q = t >> 4, g = (t >> 3) & 1, j = rb * 8 + (t & 7);
   const int lane = j + 32 * g;
   const int row = qh * 64 + wq * 32 + j;                      // row inside the query block
-  const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.n_s;
   float m = -__builtin_inff();
   float den = 0.0f;
   f32x4 num[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll 2
-  for (int s = cs; s < a.n_s; s += kMergeSplit) {
+  for (int s = cs; s < n_ch; s += kMergeSplit) {
     const size_t pi = (base + s) * BS + row;
     const float* blk = a.po + ((base + s) * BS + qh * 64) * kD;
     const float ms = a.pm[pi], ls = a.pl[pi];
@@ -1056,6 +1127,10 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
 template <typename T, int BS, bool HAS_PAD>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(4))) bb_middle_rows_kernel(Args, int n_units) {
   run<T, BS, 2, HAS_PAD>(n_units);
+}
+template <typename T, int BS, bool HAS_PAD>
+__global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(4))) bb_small_kernel(Args, int n_units) {
+  run<T, BS, 3, HAS_PAD>(n_units);
 }
 
 // ============================================ forward, bf16, block 128 ==
@@ -2486,14 +2561,56 @@ struct Layout {
   size_t pm, pl, po, total;
 };
 
+// Problems whose ordinary units (one per 64 query rows of a query block, the
+// global blocks split into kChunkTiles-tile chunks) number fewer than
+// kSmallUnits leave most of the chip idle and take one unit's latency.  They
+// run kind 3 units instead: every query block split over its key tiles into
+// the fewest chunks for which the units still number at most kSmallSlots /
+// (block / 64), one workgroup per compute unit (two workgroups sharing a
+// compute unit's matrix cores measured slower than one unit of twice the
+// tiles).  The choice depends on the sizes only, so the workspace size can
+// bound it.
+constexpr long long kSmallUnits = 512;
+constexpr long long kSmallSlots = 256;
+
+struct SmallSplit {
+  int gc, mc;   // chunks per global / middle query block; 0: ordinary units
+};
+
+SmallSplit small_split(int B, int H, int nb, int block, int r) {
+  const long long qs = block / 64, bh = static_cast<long long>(B) * H;
+  const int n_s = (nb + kChunkTiles - 1) / kChunkTiles;
+  const long long normal = bh * (2LL * n_s + nb - 2) * qs;
+  if (normal >= kSmallUnits || normal == 0) return {0, 0};
+  const int nt_min = 2 + (nb - 2 < 2 ? nb - 2 : 2) + r;   // tiles of blocks 1 and nb-2
+  const int nt_max = 2 + (nb - 2 < 3 ? nb - 2 : 3) + r;
+  for (int cs = 1; cs <= nb; ++cs) {
+    const int gc = (nb + cs - 1) / cs;
+    int mc = (nt_max + cs - 1) / cs;
+    if (mc > nt_min) mc = nt_min;                            // no chunk may be empty
+    const long long units = bh * (2LL * gc + static_cast<long long>(nb - 2) * mc) * qs;
+    if (units <= kSmallSlots / qs) return units > normal ? SmallSplit{gc, mc} : SmallSplit{0, 0};
+  }
+  return {0, 0};
+}
+
 Layout workspace_layout(int B, int H, int nb, int block) {
-  const size_t n_s = static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
-  const size_t units = static_cast<size_t>(B) * H * 2;
+  // partial blocks (block rows each): the global chunks of the ordinary
+  // units, or the chunks of every query block for the small-problem split
+  // (the largest over every r the sizes allow)
+  const size_t bh = static_cast<size_t>(B) * H;
+  size_t blocks = bh * 2 * static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
+  const int r_max = nb - 5 > 0 ? (nb - 5 < kMaxR ? nb - 5 : kMaxR) : 0;
+  for (int r = 0; r <= r_max; ++r) {
+    const SmallSplit sp = small_split(B, H, nb, block, r);
+    const size_t n = bh * (2 * static_cast<size_t>(sp.gc) + static_cast<size_t>(nb - 2) * sp.mc);
+    if (sp.gc > 0 && n > blocks) blocks = n;
+  }
   Layout w;
   w.pm = 0;
-  w.pl = w.pm + align256(units * n_s * block * sizeof(float));
-  w.po = w.pl + align256(units * n_s * block * sizeof(float));
-  w.total = w.po + units * n_s * block * kD * sizeof(float);
+  w.pl = w.pm + align256(blocks * block * sizeof(float));
+  w.po = w.pl + align256(blocks * block * sizeof(float));
+  w.total = w.po + blocks * block * kD * sizeof(float);
   return w;
 }
 
@@ -2527,8 +2644,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // Persistent grid for a kernel: as many workgroups as the current device
-// holds at once, at most one per unit, rounded down to a multiple of 8 (the
-// XCD count) so that every XCD runs the same number.
+// holds at once, at most one per unit.  When the device holds fewer than the
+// units, rounded down to a multiple of 8 (the XCD count) so that every XCD
+// runs the same number; otherwise one workgroup per unit.
 int persistent_grid(const void* kernel, int nt, long long n_units, unsigned* grid) {
   int dev = 0, ncu = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess) return BB_ERR_HIP;
@@ -2536,8 +2654,10 @@ int persistent_grid(const void* kernel, int nt, long long n_units, unsigned* gri
     return BB_ERR_HIP;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, nt, 0) != hipSuccess) return BB_ERR_HIP;
   long long g = static_cast<long long>(ncu > 0 ? ncu : 1) * (occ > 0 ? occ : 1);
-  if (g > n_units) g = n_units;
-  if (g >= 8) g -= g % 8;
+  if (g >= n_units)
+    g = n_units;
+  else if (g >= 8)
+    g -= g % 8;
   *grid = static_cast<unsigned>(g);
   return BB_OK;
 }
@@ -2571,7 +2691,22 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags, hipE
     k_middle = bb_middle_rows_kernel<T, BS, HAS_PAD>;
     nt = C::NT;
   }
-  if (units) {
+  // small problems (a.gc > 0, key-group kernels only): one launch of kind 3
+  // units, every query block merged after it
+  bool small = false;
+  if constexpr (!(sizeof(T) == 2 && BS == 128)) {
+    small = a.gc > 0;
+    if (units && small) {
+      hipEvent_t e1 = merge ? nullptr : ev1;
+      const long long n = bhs * (2LL * a.gc + static_cast<long long>(a.nb - 2) * a.mc) * C::QSPLIT;
+      st = persistent_grid(reinterpret_cast<const void*>(bb_small_kernel<T, BS, HAS_PAD>), nt, n, &grid);
+      if (st != BB_OK) return st;
+      hipExtLaunchKernelGGL(bb_small_kernel<T, BS, HAS_PAD>, dim3(grid), dim3(nt), 0, stream, ev0, e1, 0, a,
+                            static_cast<int>(n));
+      if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
+    }
+  }
+  if (units && !small) {
     hipEvent_t e1 = merge ? nullptr : ev1;
     if (flags & BB_LAUNCH_SPLIT) {
       st = persistent_grid(reinterpret_cast<const void*>(k_global), nt, bhs * per_g, &grid);
@@ -2592,8 +2727,17 @@ int launch(const Args& a, int B, int H, hipStream_t stream, unsigned flags, hipE
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   if (merge) {
-    hipExtLaunchKernelGGL(bb_global_merge_kernel<T, BS>, dim3(static_cast<unsigned>(bhs) * 2 * (BS / 64) * 2 * 4), dim3(64 * kMergeSplit),
-                          0, stream, units ? nullptr : ev0, ev1, 0, a);
+    // 8 workgroups per 64 query rows of every merged block
+    if constexpr (!(sizeof(T) == 2 && BS == 128)) {
+      if (small)
+        hipExtLaunchKernelGGL(bb_global_merge_kernel<T, BS, true>,
+                              dim3(static_cast<unsigned>(bhs * a.nb) * (BS / 64) * 2 * 4), dim3(64 * kMergeSplit), 0,
+                              stream, units ? nullptr : ev0, ev1, 0, a);
+    }
+    if (!small)
+      hipExtLaunchKernelGGL(bb_global_merge_kernel<T, BS, false>,
+                            dim3(static_cast<unsigned>(bhs) * 2 * (BS / 64) * 2 * 4), dim3(64 * kMergeSplit), 0,
+                            stream, units ? nullptr : ev0, ev1, 0, a);
     if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   }
   return BB_OK;
@@ -2633,7 +2777,8 @@ int forward_impl(const void* q, const void* k, const void* v, const uint8_t* pad
                  size_t workspace_bytes, void* stream, unsigned flags, void* start_event, void* stop_event,
                  float* lse) {
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
-  if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE | BB_QUERY_MASK)) return BB_ERR_SHAPE;
+  if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE | BB_QUERY_MASK | BB_ORDINARY_UNITS))
+    return BB_ERR_SHAPE;
   int nb = 0;
   const int st = check_shape(B, H, L, d, block, r, &nb);
   if (st != BB_OK) return st;
@@ -2668,6 +2813,12 @@ int forward_impl(const void* q, const void* k, const void* v, const uint8_t* pad
   a.r = r;
   a.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
   a.qmask = (flags & BB_QUERY_MASK) && pad_mask != nullptr ? 1 : 0;
+  a.gc = a.mc = 0;
+  if (!(dtype == BB_BF16 && block == 128) && !(flags & BB_ORDINARY_UNITS)) {   // the key-group kernels
+    const SmallSplit sp = small_split(B, H, nb, block, r);
+    a.gc = sp.gc;
+    a.mc = sp.mc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
   const bool p = pad_mask != nullptr;
@@ -2860,6 +3011,7 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   a.f.r = r;
   a.f.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
   a.f.qmask = 0;
+  a.f.gc = a.f.mc = 0;
   a.o = static_cast<const char*>(out);
   a.dout = static_cast<const char*>(dout);
   a.lse = lse;

@@ -64,6 +64,12 @@ typedef enum { BB_FP32 = 0, BB_BF16 = 1 } bb_dtype;
                               pair, which cancels in its softmax: it is the unmasked attention row.
                               No effect when pad_mask is NULL.  Forward output only (not
                               bb_attn_forward_lse or the backward). */
+#define BB_ORDINARY_UNITS 16u /* run the ordinary work units even for a small problem.  By default,
+                              when the ordinary units are too few to fill the device (fewer than
+                              512 of 64 query rows), the fp32 kernels and the bf16 kernels of block
+                              64 split every query block over its key tiles instead and merge the
+                              chunks afterwards (BB_LAUNCH_SPLIT then has no second launch); the
+                              result agrees to rounding.  For tests that want the ordinary units. */
 
 /* Version of this ABI (BB_ABI_VERSION of the built library). */
 int bb_abi_version(void);
@@ -183,8 +189,8 @@ int bb_attn_forward_noalloc(const void* q, const void* k, const void* v, const u
 /* bb_attn_forward with flags: a launch mode (BB_LAUNCH_FUSED or BB_LAUNCH_SPLIT,
  * which give the same result bit for bit), optionally one phase
  * (BB_PHASE_UNITS or BB_PHASE_MERGE) for callers that time the phases or
- * enqueue other work between them, and optionally BB_QUERY_MASK (the pair
- * masking variant).  Unknown flags: BB_ERR_SHAPE. */
+ * enqueue other work between them, optionally BB_QUERY_MASK (the pair
+ * masking variant) and BB_ORDINARY_UNITS.  Unknown flags: BB_ERR_SHAPE. */
 int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
                        const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
                        void* out, int dtype, void* workspace, size_t workspace_bytes,

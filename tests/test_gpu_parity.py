@@ -136,10 +136,16 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("units", ["default", "ordinary"])
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
-def test_small_shapes_full_parity(dev, w):
-    say(f"case {w.name}")
-    got, inputs, ri = run_gpu(w, dev)
+def test_small_shapes_full_parity(dev, w, units):
+    """Every output against the oracle.  These shapes have too few ordinary
+    work units to fill the device, so by default the key-group kernels split
+    every query block over its key tiles (one to a few tiles per unit) and
+    merge the chunks; BB_ORDINARY_UNITS runs the ordinary units instead."""
+    say(f"case {w.name} units={units}")
+    flags = bb.BB_ORDINARY_UNITS if units == "ordinary" else 0
+    got, inputs, ri = run_gpu(w, dev, flags)
     compare_full(w, got, inputs, ri)
 
 
@@ -148,8 +154,8 @@ def test_small_shapes_full_parity(dev, w):
 def test_split_launch_matches_fused_bitwise(dev, w):
     say(f"case split-vs-fused {w.name}")
     inputs = make_inputs(w)
-    a, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_FUSED, inputs=inputs)
-    b, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_SPLIT, inputs=inputs)
+    a, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_FUSED | bb.BB_ORDINARY_UNITS, inputs=inputs)
+    b, _, _ = run_gpu(w, dev, bb.BB_LAUNCH_SPLIT | bb.BB_ORDINARY_UNITS, inputs=inputs)
     assert np.array_equal(a, b)
 
 
@@ -388,3 +394,26 @@ def test_query_mask_flag_full_shape(dev):
     err = np.abs(got - exp).max()
     say(f"  max err {err:.3e}")
     assert err <= TOL[w.dtype]
+
+
+def test_prepared_forward_matches_and_follows_its_inputs(dev):
+    """PreparedForward (arguments checked once) gives bb_attn_forward's bits,
+    and a second call after new values are written into q picks them up."""
+    w = SMALL[6]
+    say(f"case prepared forward {w.name}")
+    inputs = make_inputs(w)
+    a, _, _ = run_gpu(w, dev, inputs=inputs)
+    q, k, v, pad = inputs
+    ri = torch.from_numpy(bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)).to(dev)
+    dq, dk, dv, dpad = q.to(dev), k.to(dev), v.to(dev), pad.to(dev)
+    out = torch.full_like(dq, float("nan"))
+    ws = poisoned_workspace(w, dev)
+    call = bb.PreparedForward(dq, dk, dv, dpad, ri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws)
+    call()
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), a)
+    dq.copy_(dk)                                      # new query values, same storage
+    call()
+    b, _, _ = run_gpu(w, dev, inputs=(k, k, v, pad))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), b)

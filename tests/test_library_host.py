@@ -167,7 +167,7 @@ def fwd(lib, q=FAKE, k=2 * FAKE, v=3 * FAKE, pad=None, rand=4 * FAKE, B=2, H=3, 
 def test_forward_validation_errors(lib):
     assert fwd(lib, dtype=7) == 3                       # BB_ERR_DTYPE
     assert fwd(lib, flags=32) == 2                      # unknown flags (8 is BB_QUERY_MASK)
-    assert fwd(lib, flags=16 | 1) == 2
+    assert fwd(lib, flags=64 | 1) == 2                  # (16 is BB_ORDINARY_UNITS)
     assert fwd(lib, d=128) == 2
     assert fwd(lib, block=32) == 2
     assert fwd(lib, L=1000) == 2                        # L % block
@@ -196,15 +196,38 @@ def test_forward_empty_is_noop(lib):
     assert lib.bb_attn_workspace_bytes(0, 12, 4096, 64, 64) == 0
 
 
+def small_split_blocks(B, H, nb, block, r):
+    """Partial blocks of the small-problem split (0 when the ordinary units
+    run): fewer than 512 ordinary 64-row units -> the fewest key chunks per
+    query block whose units fit 256 / (block / 64) slots, if that gives more
+    units than the ordinary ones; chunk counts never above a block's tiles."""
+    qs, bh, n_s = block // 64, B * H, -(-nb // 8)
+    normal = bh * (2 * n_s + nb - 2) * qs
+    if normal >= 512:
+        return 0
+    nt_min, nt_max = 2 + min(nb - 2, 2) + r, 2 + min(nb - 2, 3) + r
+    for cs in range(1, nb + 1):
+        gc, mc = -(-nb // cs), min(-(-nt_max // cs), nt_min)
+        units = bh * (2 * gc + (nb - 2) * mc) * qs
+        if units <= 256 // qs:
+            return bh * (2 * gc + (nb - 2) * mc) if units > normal else 0
+    return 0
+
+
 def test_workspace_size_formula(lib):
-    for B, H, L, block in [(4, 12, 4096, 64), (1, 12, 32768, 128), (1, 2, 192, 64)]:
+    for B, H, L, block in [(4, 12, 4096, 64), (1, 12, 32768, 128), (1, 2, 192, 64), (1, 2, 1024, 64),
+                           (2, 2, 7 * 128, 128), (1, 4, 40 * 64, 64)]:
         nb = L // block
         n_s = -(-nb // 8)
-        units = B * H * 2
+        blocks = max([B * H * 2 * n_s] + [small_split_blocks(B, H, nb, block, r)
+                                          for r in range(min(max(nb - 5, 0), 16) + 1)])
         def a256(x):
             return (x + 255) // 256 * 256
-        exp = 2 * a256(units * n_s * block * 4) + units * n_s * block * 64 * 4
-        assert lib.bb_attn_workspace_bytes(B, H, L, 64, block) == exp
+        exp = 2 * a256(blocks * block * 4) + blocks * block * 64 * 4
+        assert lib.bb_attn_workspace_bytes(B, H, L, 64, block) == exp, (B, H, L, block)
+    # the fp32 1 x 2 x 1024 shape: 8 two-tile chunks per global block and
+    # 4 per middle block (8 tiles each at r = 3)
+    assert small_split_blocks(1, 2, 16, 64, 3) == 2 * (2 * 8 + 14 * 4)
     assert lib.bb_attn_workspace_bytes(1, 1, 1000, 64, 64) == 0   # unsupported -> 0
 
 
@@ -444,6 +467,8 @@ def test_forward_wrapper_rejects_mismatched_tensors(lib, change, match):
     change(a)
     with pytest.raises(ValueError, match=match):
         bb.bb_attn_forward(**a)
+    with pytest.raises(ValueError, match=match):      # the same checks, once, at construction
+        bb.PreparedForward(**a)
 
 
 def test_lse_backward_layer_wrappers_reject_mismatched_tensors(lib):
