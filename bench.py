@@ -634,10 +634,17 @@ def main():
     flops = useful_flops(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
     alg_bytes = algorithmic_bytes(w)
-    kernel = MAIN_KERNEL if args.launch == "fused" else "bb_global_rows_kernel+bb_middle_rows_kernel"
+    _, small = bb.bb_attn_forward_plan(w.B, w.H, w.L, w.d, w.block, w.r, w.dtype, launch)
+    pre = "bb_sub32_" if w.dtype == "bf16" and w.block == 128 else "bb_"
+    if small:
+        kernel = "bb_small_kernel"
+    elif args.launch == "fused":
+        kernel = pre + "fused_kernel"
+    else:
+        kernel = f"{pre}global_rows_kernel+{pre}middle_rows_kernel"
     achieved = flops / (units_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = committed_traffic(w.name) if args.launch == "fused" else None
+    traffic = committed_traffic(w.name) if kernel == MAIN_KERNEL else None
 
     out = {
         "metric": METRIC if w.name == DEFAULT_WORKLOAD else

@@ -37,7 +37,7 @@ EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_
            "bb_attn_forward_timed", "bb_attn_forward_lse", "bb_rand_idx_invert",
            "bb_attn_backward_workspace_bytes", "bb_attn_backward", "bb_layer_workspace_bytes",
            "bb_layer_forward", "bb_attn_forward_noalloc", "bb_layer_stack_workspace_bytes",
-           "bb_layer_stack_forward")
+           "bb_layer_stack_forward", "bb_attn_forward_plan")
 
 _lib = None
 
@@ -76,6 +76,9 @@ def lib():
     L.bb_rand_idx_check.argtypes = [vp, c_int, c_int, c_int, c_int]
     L.bb_attn_workspace_bytes.restype = c_size
     L.bb_attn_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    L.bb_attn_forward_plan.restype = c_int
+    L.bb_attn_forward_plan.argtypes = [c_int] * 7 + [ctypes.c_uint, ctypes.POINTER(ctypes.c_longlong),
+                                                    ctypes.POINTER(c_int)]
     fwd = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, c_int, vp, c_size, vp]
     L.bb_attn_forward.restype = c_int
     L.bb_attn_forward.argtypes = fwd
@@ -153,6 +156,18 @@ def bb_rand_idx_check(rand_idx, H: int, L: int, block: int, r: int) -> int:
 
 def bb_attn_workspace_bytes(B: int, H: int, L: int, d: int, block: int) -> int:
     return int(lib().bb_attn_workspace_bytes(B, H, L, d, block))
+
+
+def bb_attn_forward_plan(B: int, H: int, L: int, d: int, block: int, r: int, dtype: str,
+                         flags: int = BB_LAUNCH_FUSED):
+    """(work units, small-problem split used) of a forward call of these sizes;
+    dtype "bf16" or "fp32"."""
+    n, small = ctypes.c_longlong(0), ctypes.c_int(0)
+    st = lib().bb_attn_forward_plan(B, H, L, d, block, r, BB_BF16 if dtype == "bf16" else BB_FP32, flags,
+                                    ctypes.byref(n), ctypes.byref(small))
+    if st != BB_OK:
+        raise BBError(st, "bb_attn_forward_plan")
+    return int(n.value), bool(small.value)
 
 
 def _ptr(t):

@@ -2763,6 +2763,25 @@ extern "C" const char* bb_status_str(int status) {
   }
 }
 
+extern "C" int bb_attn_forward_plan(int B, int H, int L, int d, int block, int r, int dtype, unsigned flags,
+                                    long long* n_units, int* small) {
+  if (!n_units || !small) return BB_ERR_NULL;
+  if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
+  if (flags & ~(BB_LAUNCH_SPLIT | BB_PHASE_UNITS | BB_PHASE_MERGE | BB_QUERY_MASK | BB_ORDINARY_UNITS))
+    return BB_ERR_SHAPE;
+  int nb = 0;
+  const int st = check_shape(B, H, L, d, block, r, &nb);
+  if (st != BB_OK) return st;
+  const long long bh = static_cast<long long>(B) * H, qs = block / 64;
+  SmallSplit sp{0, 0};
+  if (!(dtype == BB_BF16 && block == 128) && !(flags & BB_ORDINARY_UNITS)) sp = small_split(B, H, nb, block, r);
+  const int n_s = (nb + kChunkTiles - 1) / kChunkTiles;
+  *n_units = sp.gc > 0 ? bh * (2LL * sp.gc + static_cast<long long>(nb - 2) * sp.mc) * qs
+                       : bh * (2LL * n_s + nb - 2) * qs;
+  *small = sp.gc > 0 ? 1 : 0;
+  return BB_OK;
+}
+
 extern "C" size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block) {
   int nb = 0;
   if (check_shape(B, H, L, d, block, 0, &nb) != BB_OK) return 0;

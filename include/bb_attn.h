@@ -123,10 +123,24 @@ int bb_rand_idx_check(const int32_t* rand_idx, int H, int L, int block, int r);
 /*
  * Bytes of device workspace bb_attn_forward needs for these sizes: the
  * split-K partial results (row max, row sum, unnormalised output, fp32) of
- * the two global query blocks of every (b, h).  0 for empty inputs.  Returns
+ * the two global query blocks of every (b, h), or, for problems small enough
+ * to be split over their key tiles (BB_ORDINARY_UNITS), of every query block's
+ * key chunks, for the largest r the sizes allow.  0 for empty inputs.  Returns
  * 0 also for unsupported sizes (bb_attn_forward then reports BB_ERR_SHAPE).
  */
 size_t bb_attn_workspace_bytes(int B, int H, int L, int d, int block);
+
+/*
+ * How bb_attn_forward_ex with `flags` runs these sizes, without launching
+ * anything: *n_units = work units of its unit launch(es) (64 query rows
+ * against a list of key tiles each), *small = 1 when the problem is split
+ * over the key tiles of every query block (see BB_ORDINARY_UNITS), else 0.
+ * Same size, dtype and flag checks as the forward (no pointer checks);
+ * outputs untouched on an error.  For tools and benchmarks that name the
+ * kernels a call runs.
+ */
+int bb_attn_forward_plan(int B, int H, int L, int d, int block, int r, int dtype, unsigned flags,
+                         long long* n_units, int* small);
 
 /*
  * BigBird block-sparse self-attention forward.

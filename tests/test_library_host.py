@@ -231,6 +231,24 @@ def test_workspace_size_formula(lib):
     assert lib.bb_attn_workspace_bytes(1, 1, 1000, 64, 64) == 0   # unsupported -> 0
 
 
+def test_forward_plan(lib):
+    plan = bb.bb_attn_forward_plan
+    assert plan(1, 2, 1024, 64, 64, 3, "fp32") == (2 * (2 * 8 + 14 * 4), True)
+    assert plan(1, 2, 1024, 64, 64, 3, "fp32", bb.BB_ORDINARY_UNITS) == (2 * (2 * 2 + 14), False)
+    assert plan(4, 12, 4096, 64, 64, 3, "bf16") == (48 * (2 * 8 + 62), False)
+    assert plan(1, 2, 1024, 64, 128, 3, "bf16") == (2 * (2 * 1 + 6) * 2, False)   # 32-key-step kernels
+    for B, H, nb, block in [(1, 2, 16, 64), (2, 2, 7, 128), (1, 4, 40, 64), (3, 1, 9, 64)]:
+        for r in range(min(max(nb - 5, 0), 16) + 1):
+            n, small = plan(B, H, nb * block, 64, block, r, "fp32")
+            assert small == (small_split_blocks(B, H, nb, block, r) > 0)
+            if small:
+                assert n == small_split_blocks(B, H, nb, block, r) * (block // 64)
+    with pytest.raises(bb.BBError, match="BB_ERR_SHAPE"):
+        plan(1, 2, 1000, 64, 64, 3, "fp32")
+    with pytest.raises(bb.BBError, match="BB_ERR_SHAPE"):
+        plan(1, 2, 1024, 64, 64, 3, "fp32", 64)
+
+
 # ------------------------------------------------------ backward (host side) ---
 
 def numpy_invert(ri, nb):
