@@ -236,9 +236,11 @@ __device__ __forceinline__ void issue_tile(gchar_ptr kbh, gchar_ptr vbh, int til
 // Per-wave online-softmax state for 32 query rows (one per lane pair).
 struct WaveState {
   f32x16 o[2];   // O^T, dims [0,32) and [32,64)
-  float m;       // running row max in q.k units (may lag the true max by < tau/scale)
+  float m;       // fp32: running row max in q.k units (may lag the true max by < tau/scale);
+                 // bf16: the unit's fixed reference (see softmax_pv)
   float l;       // this lane's part of the row sum
   float qs;      // key offsets apply to this row: 1, or 0 for a padded query row under pair masking
+  float big;     // bf16: largest per-subtile probability sum of this lane (the bound check)
 };
 
 // V^T operands of one subtile for the PV MFMAs: [dim half][16-key half].
@@ -406,6 +408,40 @@ __device__ __forceinline__ float subtile_max(const f32x16& acc, float m0) {
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
+constexpr int kTile64 = 64 * kD * 2;               // one 64-key bf16 tile of K (or V): 8 KiB
+constexpr float kProbBound = 4294967296.0f;        // 2^32: the largest probability the fast path keeps
+
+// Probabilities of one 32-key subtile against the reference m (q.k units)
+// and uniform offset `bias`: P = 2^((s + bias - m) c), rounded to the bf16
+// PV operands; returns this lane's sum of the rounded values.
+__device__ __forceinline__ float probs_w(const f32x16& s, float m, float bias, bf16x8 (&pb)[2]) {
+  const float mc = (m - bias) * kScaleLog2;
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float lsum = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      f32x2 pr = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], kScaleLog2, -mc)),
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e + 1], kScaleLog2, -mc))};
+      const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, lsum, false);
+      pb[h][e] = c2[0];
+      pb[h][e + 1] = c2[1];
+    }
+  return lsum;
+}
+
+// O^T += V^T P^T for one subtile (4 MFMAs: 2 dim halves x 2 16-key halves).
+template <typename WS>
+__device__ __forceinline__ void pv_w(WS& ws, const VOp<__bf16>& vo, const bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+      ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[dh][mm], pb[mm], ws.o[dh], 0, 0, 0);
+}
+
 // Online softmax of one score subtile (lane = query row, 16 of its 32 keys)
 // and O^T += V^T . P^T.  Registers only.  `first`: the unit's first tile
 // (wave-uniform), whose max starts the running max.  `bias` (wave-uniform, 0
@@ -414,52 +450,46 @@ __device__ __forceinline__ float subtile_max(const f32x16& acc, float m0) {
 template <typename T>
 __device__ __forceinline__ void softmax_pv(WaveState& ws, const f32x16& acc, const VOp<T>& vo, bool first,
                                            float bias) {
-  // P = 2^((s + bias - m) c) against the running max m first; the tile's own
-  // max is reduced meanwhile, and only if it exceeds m by more than tau/c
-  // (rare) are O and l rescaled and P recomputed.  Keeps the exps off the
-  // critical path of the max reduction.
-  if (first) ws.m = subtile_max(acc, acc[15]) + bias;
-  float p[16];
-  float mc = (ws.m - bias) * kScaleLog2;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-  // Each lane tests its own 16 scores; only a rescale needs the row max over
-  // both lane halves.
-  const float lm = lane_max(acc, acc[15]) + bias;
-  if (__any(lm - ws.m > kRescaleTau / kScaleLog2)) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
-    const float mloc = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), ws.m);
-    const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      ws.o[0][v] *= alpha;
-      ws.o[1][v] *= alpha;
-    }
-    ws.l *= alpha;
-    ws.m = mloc;
-    mc = (ws.m - bias) * kScaleLog2;
+  if constexpr (sizeof(T) == 2) {
+    // bf16: every probability of the unit is taken against one fixed
+    // reference, the row max of this wave's keys of the unit's first tile
+    // (the reading of the block-128 kernel: P <= 2^32 is checked per subtile
+    // through the lane's probability sum, and a unit that exceeds it is
+    // recomputed exactly at its end); no max and no rescale in the step.
+    if (first) ws.m = subtile_max(acc, acc[15]) + bias;
+    bf16x8 pb[2];
+    const float lsum = probs_w(acc, ws.m, bias, pb);
+    ws.l += lsum;
+    ws.big = fmaxf(ws.big, lsum);
+    pv_w(ws, vo, pb);
+  } else {
+    // P = 2^((s + bias - m) c) against the running max m first; the tile's own
+    // max is reduced meanwhile, and only if it exceeds m by more than tau/c
+    // (rare) are O and l rescaled and P recomputed.  Keeps the exps off the
+    // critical path of the max reduction.
+    if (first) ws.m = subtile_max(acc, acc[15]) + bias;
+    float p[16];
+    float mc = (ws.m - bias) * kScaleLog2;
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
-  }
-  if constexpr (sizeof(T) == 2) {
-    bf16x8 pb[2];
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    // Each lane tests its own 16 scores; only a rescale needs the row max over
+    // both lane halves.
+    const float lm = lane_max(acc, acc[15]) + bias;
+    if (__any(lm - ws.m > kRescaleTau / kScaleLog2)) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+      const float mloc = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), ws.m);
+      const float alpha = __builtin_amdgcn_exp2f((ws.m - mloc) * kScaleLog2);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        f32x2 pr = {p[8 * h + e], p[8 * h + e + 1]};
-        const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
-        ws.l = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, ws.l, false);   // row sum of bf16(P)
-        pb[h][e] = c2[0];
-        pb[h][e + 1] = c2[1];
+      for (int v = 0; v < 16; ++v) {
+        ws.o[0][v] *= alpha;
+        ws.o[1][v] *= alpha;
       }
+      ws.l *= alpha;
+      ws.m = mloc;
+      mc = (ws.m - bias) * kScaleLog2;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-      for (int dh = 0; dh < 2; ++dh)
-        ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[dh][mm], pb[mm], ws.o[dh], 0, 0, 0);
-  } else {
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], kScaleLog2, -mc));
+    }
     float lsum = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) lsum += p[v];
@@ -889,6 +919,140 @@ __device__ __forceinline__ void finalize(WaveState& ws, const Unit& w, int wq, i
     lds_barrier();   // key groups 2 and 3 (block 128) are merged already: the round's second barrier
 }
 
+
+// A wave's softmax state per query row (fixed-reference softmax).
+struct WaveStateW {
+  f32x16 o[2];     // O^T, dims [0,32) and [32,64)
+  float m;         // the unit's reference max (q.k units)
+  float l;         // this lane's part of the row sum
+  float big;       // largest per-subtile probability sum of this lane (the bound check)
+  float qs;        // key offsets apply to this row: 1, or 0 for a padded query row under pair masking
+};
+
+// Pad offsets of one 32-key subtile, classified on the scalar unit before the
+// score products (the classes of apply_pad()): the uniform offset `bias` (0,
+// or -10000 on the logit when all 32 keys are padding) and, for a subtile
+// with both kinds of keys, `mixed` = the per-key mask (bit k: key k padded),
+// added after the products by add_pad_bias(); 0 otherwise.
+struct PadClass {
+  float bias;
+  uint32_t mixed;
+};
+__device__ __forceinline__ PadClass classify_pad(const PadWords& w) {
+  PadClass c;
+  c.bias = 0.0f;
+  c.mixed = 0u;
+  if ((zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0)
+    return c;
+  if ((w.p[0] | w.p[1] | w.p[2] | w.p[3]) == 0) {
+    c.bias = kMaskRaw;
+    return c;
+  }
+  c.mixed = zero_byte_mask(w.p[0]) | (zero_byte_mask(w.p[1]) << 8) | (zero_byte_mask(w.p[2]) << 16) |
+            (zero_byte_mask(w.p[3]) << 24);
+  return c;
+}
+
+// The per-key offsets of a mixed subtile, added to the score accumulator by
+// one fp32 32x32x2 MFMA (as in apply_pad(), with its per-query factor qs).
+__device__ __forceinline__ void add_pad_bias(f32x16& acc, uint32_t mixed, int lane, float qs) {
+  const int j = lane & 31;
+  const bool lo = lane < 32;
+  const bool padded = (mixed >> perm_row(j)) & 1u;
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? qs : 0.0f, acc, 0, 0, 0);
+}
+
+// 64-key tile id of entry i of a unit's tile list (block-level list, TPB
+// 64-key tiles per key block).
+template <int TPB>
+__device__ __forceinline__ int tile64_at(const TileList& tl, int i) {
+  if constexpr (TPB == 1) return tile_at(tl, i);
+  return TPB * tile_at(tl, i / TPB) + i % TPB;
+}
+
+// Scores of one 32-key subtile read straight from global memory (the slow
+// path): S^T = K Q^T with K rows perm_row-ordered as in scores(), the
+// subtile's pad offsets added per key in fp32 (times the row's factor qs).
+__device__ __forceinline__ f32x16 scores_global(const char* kt, const uint8_t* pt, const u32x4 (&qop)[4], int kbase,
+                                                int lane, float qs) {
+  const int j = lane & 31, g = lane >> 5;
+  const char* krow = kt + (kbase + perm_row(j)) * (kD * 2);
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    acc = mfma_qk(*reinterpret_cast<const u32x4*>(krow + (2 * x + g) * 16), qop[x], acc, static_cast<__bf16*>(nullptr));
+  if (pt != nullptr) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)   // element v holds key kbase + 16 (v / 8) + 8 g + v % 8
+      if (pt[kbase + 16 * (v >> 3) + 8 * g + (v & 7)] == 0) acc[v] += kMaskRaw * qs;
+  }
+  return acc;
+}
+
+// Slow path of a unit in which some lane of this wave saw a probability sum
+// above the bound: this wave's state over its keys of the unit is recomputed
+// exactly, in two passes over the unit's tiles read straight from global
+// memory -- the row max over every allowed key first, then the
+// probabilities against it (all at most 1) and O, l.  Registers and global
+// loads only (no LDS, no barrier), so the other waves of the workgroup do not
+// take part.  The wave's keys: NKB 32-key halves of every 64-key tile from
+// key kb0 (NKB 2: complete rows; NKB 1: the key group of kb0).
+template <int TPB, bool HAS_PAD, int NKB, typename WS>
+__device__ __forceinline__ void redo_unit_w(WS& ws, const Unit& cu, int ntiles, int wq, int lane, int kb0) {
+  const kargs_ptr a = kargs();
+  const char* kbh = a->k + cu.off;
+  const char* vbh = a->v + cu.off;
+  const uint8_t* pad_b = HAS_PAD ? a->pad + static_cast<size_t>(cu.b) * a->L : nullptr;
+  u32x4 q[4];
+  load_q<__bf16, 64>(a->q + cu.off + static_cast<size_t>(cu.q0) * (kD * 2), wq, lane, q);
+  float lm = -__builtin_inff();
+#pragma unroll 1
+  for (int i = 0; i < NKB * ntiles; ++i) {
+    const int t = tile64_at<TPB>(cu.tl, i / NKB), kb = kb0 + 32 * (i % NKB);
+    const char* kt = kbh + static_cast<size_t>(t) * kTile64;
+    const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
+    lm = lane_max(scores_global(kt, pt, q, kb, lane, ws.qs), lm);
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+  ws.m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  ws.l = 0.0f;
+  ws.big = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    ws.o[0][v] = 0.0f;
+    ws.o[1][v] = 0.0f;
+  }
+  const int j = lane & 31, g = lane >> 5;
+#pragma unroll 1
+  for (int i = 0; i < NKB * ntiles; ++i) {
+    const int t = tile64_at<TPB>(cu.tl, i / NKB), kb = kb0 + 32 * (i % NKB);
+    const char* kt = kbh + static_cast<size_t>(t) * kTile64;
+    const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
+    const f32x16 s = scores_global(kt, pt, q, kb, lane, ws.qs);
+    bf16x8 pb[2];
+    ws.l += probs_w(s, ws.m, 0.0f, pb);
+    // V^T operand: dim dh*32 + perm_row(j), keys kb + 16 mm + 8 g + e (e = 0..7),
+    // gathered two keys at a time
+    const uint16_t* vcol = reinterpret_cast<const uint16_t*>(vbh + static_cast<size_t>(t) * kTile64) +
+                           (kb + 8 * g) * kD + perm_row(j);
+    VOp<__bf16> vo;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const uint16_t* c = vcol + 16 * mm * kD + 32 * dh;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = static_cast<uint32_t>(c[(2 * e) * kD]) | (static_cast<uint32_t>(c[(2 * e + 1) * kD]) << 16);
+        vo.a[dh][mm] = __builtin_bit_cast(bf16x8, w);
+      }
+    pv_w(ws, vo, pb);
+  }
+}
+
 // A persistent workgroup: it runs a fixed sequence of work units back to back,
 // streaming their key tiles through the 2-stage LDS ring.  The sequence: the
 // hardware deals workgroup ids round robin to the 8 XCDs, so workgroup x runs
@@ -969,6 +1133,7 @@ __device__ __forceinline__ void run(int n_units) {
     ws.m = -__builtin_inff();
     ws.l = 0.0f;
     ws.qs = 1.0f;
+    ws.big = 0.0f;
     if constexpr (HAS_PAD) {
       if (kargs()->qmask) ws.qs = pad_b[cu.q0 + wq * 32 + (lane_u & 31)] != 0 ? 1.0f : 0.0f;
     }
@@ -1003,6 +1168,11 @@ __device__ __forceinline__ void run(int n_units) {
 #undef BB_TILE
     }
 
+    if constexpr (sizeof(T) == 2) {
+      // a probability above the fixed reference's bound: this wave's keys of
+      // the unit again, exactly (rare; see softmax_pv)
+      if (__any(ws.big > kProbBound)) redo_unit_w<1, HAS_PAD, 1>(ws, cu, ntiles, wq, lane_u, kbase);
+    }
     if ((ntiles - 1) & 1)
       finalize<T, BS, 1>(ws, cu, wq, wk, lane_u);
     else
@@ -1159,170 +1329,6 @@ __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_
 // an all-padding first subtile against valid later ones), that wave
 // recomputes its rows of the unit at the end, exactly, in two passes from
 // global memory (redo_unit_w).
-
-constexpr int kTile64 = 64 * kD * 2;               // one 64-key bf16 tile of K (or V): 8 KiB
-constexpr float kProbBound = 4294967296.0f;        // 2^32: the largest probability the fast path keeps
-
-// A wave's softmax state per query row (fixed-reference softmax).
-struct WaveStateW {
-  f32x16 o[2];     // O^T, dims [0,32) and [32,64)
-  float m;         // the unit's reference max (q.k units)
-  float l;         // this lane's part of the row sum
-  float big;       // largest per-subtile probability sum of this lane (the bound check)
-  float qs;        // key offsets apply to this row: 1, or 0 for a padded query row under pair masking
-};
-
-// Probabilities of one 32-key subtile against the reference m (q.k units)
-// and uniform offset `bias`: P = 2^((s + bias - m) c), rounded to the bf16
-// PV operands; returns this lane's sum of the rounded values.
-__device__ __forceinline__ float probs_w(const f32x16& s, float m, float bias, bf16x8 (&pb)[2]) {
-  const float mc = (m - bias) * kScaleLog2;
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  float lsum = 0.0f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      f32x2 pr = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], kScaleLog2, -mc)),
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e + 1], kScaleLog2, -mc))};
-      const bf16x2 c2 = __builtin_convertvector(pr, bf16x2);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(c2, ones, lsum, false);
-      pb[h][e] = c2[0];
-      pb[h][e + 1] = c2[1];
-    }
-  return lsum;
-}
-
-// O^T += V^T P^T for one subtile (4 MFMAs: 2 dim halves x 2 16-key halves).
-__device__ __forceinline__ void pv_w(WaveStateW& ws, const VOp<__bf16>& vo, const bf16x8 (&pb)[2]) {
-#pragma unroll
-  for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-      ws.o[dh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[dh][mm], pb[mm], ws.o[dh], 0, 0, 0);
-}
-
-// Pad offsets of one 32-key subtile, classified on the scalar unit before the
-// score products (the classes of apply_pad()): the uniform offset `bias` (0,
-// or -10000 on the logit when all 32 keys are padding) and, for a subtile
-// with both kinds of keys, `mixed` = the per-key mask (bit k: key k padded),
-// added after the products by add_pad_bias(); 0 otherwise.
-struct PadClass {
-  float bias;
-  uint32_t mixed;
-};
-__device__ __forceinline__ PadClass classify_pad(const PadWords& w) {
-  PadClass c;
-  c.bias = 0.0f;
-  c.mixed = 0u;
-  if ((zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0)
-    return c;
-  if ((w.p[0] | w.p[1] | w.p[2] | w.p[3]) == 0) {
-    c.bias = kMaskRaw;
-    return c;
-  }
-  c.mixed = zero_byte_mask(w.p[0]) | (zero_byte_mask(w.p[1]) << 8) | (zero_byte_mask(w.p[2]) << 16) |
-            (zero_byte_mask(w.p[3]) << 24);
-  return c;
-}
-
-// The per-key offsets of a mixed subtile, added to the score accumulator by
-// one fp32 32x32x2 MFMA (as in apply_pad(), with its per-query factor qs).
-__device__ __forceinline__ void add_pad_bias(f32x16& acc, uint32_t mixed, int lane, float qs) {
-  const int j = lane & 31;
-  const bool lo = lane < 32;
-  const bool padded = (mixed >> perm_row(j)) & 1u;
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lo && padded ? kMaskRaw : 0.0f, lo ? qs : 0.0f, acc, 0, 0, 0);
-}
-
-// 64-key tile id of entry i of a unit's tile list (block-level list, TPB
-// 64-key tiles per key block).
-template <int TPB>
-__device__ __forceinline__ int tile64_at(const TileList& tl, int i) {
-  if constexpr (TPB == 1) return tile_at(tl, i);
-  return TPB * tile_at(tl, i / TPB) + i % TPB;
-}
-
-// Scores of one 32-key subtile read straight from global memory (the slow
-// path): S^T = K Q^T with K rows perm_row-ordered as in scores(), the
-// subtile's pad offsets added per key in fp32 (times the row's factor qs).
-__device__ __forceinline__ f32x16 scores_global(const char* kt, const uint8_t* pt, const u32x4 (&qop)[4], int kbase,
-                                                int lane, float qs) {
-  const int j = lane & 31, g = lane >> 5;
-  const char* krow = kt + (kbase + perm_row(j)) * (kD * 2);
-  f32x16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-    acc = mfma_qk(*reinterpret_cast<const u32x4*>(krow + (2 * x + g) * 16), qop[x], acc, static_cast<__bf16*>(nullptr));
-  if (pt != nullptr) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v)   // element v holds key kbase + 16 (v / 8) + 8 g + v % 8
-      if (pt[kbase + 16 * (v >> 3) + 8 * g + (v & 7)] == 0) acc[v] += kMaskRaw * qs;
-  }
-  return acc;
-}
-
-// Slow path of a unit in which some lane of this wave saw a probability sum
-// above the bound: this wave's 32 rows of the unit are recomputed exactly,
-// in two passes over the unit's tiles read straight from global memory --
-// the row max over every allowed key first, then the probabilities against
-// it (all at most 1) and O, l.  Registers and global loads only (no LDS, no
-// barrier), so the other wave of the workgroup does not take part.
-template <int TPB, bool HAS_PAD>
-__device__ __forceinline__ void redo_unit_w(WaveStateW& ws, const Unit& cu, int ntiles, int wq, int lane) {
-  const kargs_ptr a = kargs();
-  const char* kbh = a->k + cu.off;
-  const char* vbh = a->v + cu.off;
-  const uint8_t* pad_b = HAS_PAD ? a->pad + static_cast<size_t>(cu.b) * a->L : nullptr;
-  u32x4 q[4];
-  load_q<__bf16, 64>(a->q + cu.off + static_cast<size_t>(cu.q0) * (kD * 2), wq, lane, q);
-  float lm = -__builtin_inff();
-#pragma unroll 1
-  for (int i = 0; i < 2 * ntiles; ++i) {
-    const int t = tile64_at<TPB>(cu.tl, i >> 1), kb = 32 * (i & 1);
-    const char* kt = kbh + static_cast<size_t>(t) * kTile64;
-    const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
-    lm = lane_max(scores_global(kt, pt, q, kb, lane, ws.qs), lm);
-  }
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
-  ws.m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  ws.l = 0.0f;
-  ws.big = 0.0f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    ws.o[0][v] = 0.0f;
-    ws.o[1][v] = 0.0f;
-  }
-  const int j = lane & 31, g = lane >> 5;
-#pragma unroll 1
-  for (int i = 0; i < 2 * ntiles; ++i) {
-    const int t = tile64_at<TPB>(cu.tl, i >> 1), kb = 32 * (i & 1);
-    const char* kt = kbh + static_cast<size_t>(t) * kTile64;
-    const uint8_t* pt = HAS_PAD ? pad_b + static_cast<size_t>(t) * 64 : nullptr;
-    const f32x16 s = scores_global(kt, pt, q, kb, lane, ws.qs);
-    bf16x8 pb[2];
-    ws.l += probs_w(s, ws.m, 0.0f, pb);
-    // V^T operand: dim dh*32 + perm_row(j), keys kb + 16 mm + 8 g + e (e = 0..7),
-    // gathered two keys at a time
-    const uint16_t* vcol = reinterpret_cast<const uint16_t*>(vbh + static_cast<size_t>(t) * kTile64) +
-                           (kb + 8 * g) * kD + perm_row(j);
-    VOp<__bf16> vo;
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const uint16_t* c = vcol + 16 * mm * kD + 32 * dh;
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = static_cast<uint32_t>(c[(2 * e) * kD]) | (static_cast<uint32_t>(c[(2 * e + 1) * kD]) << 16);
-        vo.a[dh][mm] = __builtin_bit_cast(bf16x8, w);
-      }
-    pv_w(ws, vo, pb);
-  }
-}
 
 // End of a unit: each wave holds complete rows.  Middle unit: out = O / l in
 // bf16 (and the row log-sum-exp when asked for); global unit: the
@@ -1598,7 +1604,7 @@ __device__ __forceinline__ void run_n(int n_units) {
 #undef BB_STEPN
 #undef BB_SUB
     }
-    if (__any(ws.big > kProbBound)) redo_unit_w<TPB, HAS_PAD>(ws, cu, ntiles, wave, lane_u);
+    if (__any(ws.big > kProbBound)) redo_unit_w<TPB, HAS_PAD, 2>(ws, cu, ntiles, wave, lane_u, 0);
     finalize_w(ws, cu, wave, lane_u);
     if (!has_next) break;
     cur = nxt;
