@@ -209,7 +209,7 @@ def test_timed_entry_matches_and_times(dev, w):
                 assert e0.elapsed_time(e1) > 0.0
 
 
-def test_north_star_symbol_through_ctypes(dev):
+def test_bb_attn_forward_symbol_through_ctypes(dev):
     """bb_attn_forward itself, called through ctypes with raw device pointers
     (no binding wrapper), against the oracle on a padded multi-chunk case."""
     import ctypes
