@@ -12,6 +12,10 @@ useful FLOPs add 2*M*N*K per projection (M = B*L) to the attention's.
 BigBird-base's depth), layer l with its own weights and the random table
 seeded with l; the layers feed each other, so the call is timed warm.
 
+`--query-mask` runs the forward (or, with `--pass backward`, the forward
+with the log-sum-exp and the backward) with BB_QUERY_MASK (the query-side
+padding variant: a pair is masked when its query or its key is padding).
+
 `--pass backward` times bb_attn_backward instead (the default is the forward,
 the headline): one step = one backward call over the whole batch (the dQ
 pass, which also forms D and LSE2, the dK/dV pass, the split-K reduce), its inputs (q, k, v,
@@ -311,25 +315,27 @@ def pmc_mfma_summary(csv_path: str, workload: str, command: str) -> None:
     print("\n".join(lines))
 
 
-def cpu_baseline(w, inputs, ri, budget_s: float):
+def cpu_baseline(w, inputs, ri, budget_s: float, query_mask: bool = False):
     """Time the fp64 oracle on (b, h) units until `budget_s` is spent."""
     from oracle.parallel import forward_units
     q, k, v, pad = inputs
     qd, kd, vd = (t.float().numpy() for t in (q, k, v))
     pd = None if pad is None else pad.numpy()
     done, el, n = _oracle_waves(
-        w, lambda units, n: forward_units(qd, kd, vd, pd, ri, w.block, units=units, workers=n), budget_s)
+        w, lambda units, n: forward_units(qd, kd, vd, pd, ri, w.block, units=units, workers=n,
+                                          query_mask=query_mask), budget_s)
     return _baseline_fields(w, done, el, n, useful_flops(w), "forward")
 
 
-def cpu_baseline_backward(w, inputs, dout, ri, budget_s: float):
+def cpu_baseline_backward(w, inputs, dout, ri, budget_s: float, query_mask: bool = False):
     """Time the fp64 oracle's backward on (b, h) units until `budget_s` is spent."""
     from oracle.parallel import backward_units
     q, k, v, pad = inputs
     qd, kd, vd, gd = (t.float().numpy() for t in (q, k, v, dout))
     pd = None if pad is None else pad.numpy()
     done, el, n = _oracle_waves(
-        w, lambda units, n: backward_units(qd, kd, vd, pd, ri, w.block, gd, units=units, workers=n),
+        w, lambda units, n: backward_units(qd, kd, vd, pd, ri, w.block, gd, units=units, workers=n,
+                                           query_mask=query_mask),
         budget_s)
     return _baseline_fields(w, done, el, n, 2.5 * useful_flops(w), "backward")
 
@@ -437,7 +443,9 @@ def bench_backward(args, w, dev):
     dq0, dk0, dv0, dg0 = q.to(dev), k.to(dev), v.to(dev), dout.to(dev)
     out0 = torch.empty_like(dq0)
     lse0 = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
-    bb.bb_attn_forward_lse(dq0, dk0, dv0, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, out0, fws, lse0)
+    qflag = bb.BB_QUERY_MASK if args.query_mask else 0
+    bb.bb_attn_forward_lse(dq0, dk0, dv0, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, out0, fws, lse0,
+                           flags=qflag)
     # cold mode: rotate among copies of the inputs (q, k, v, out, dout: 5 x 25 MB on the
     # headline shape) and outputs so that each call reads HBM
     footprint = 8 * dq0.numel() * dq0.element_size()
@@ -454,7 +462,7 @@ def bench_backward(args, w, dev):
     def call(i):
         a, b_, c, o, g, l, gq, gk, gv = sets[i % n_sets]
         bb.bb_attn_backward(a, b_, c, dpad, dri, doff, drows, w.B, w.H, w.L, w.d, w.block, w.r,
-                            o, g, l, gq, gk, gv, ws, stream=stream.cuda_stream)
+                            o, g, l, gq, gk, gv, ws, stream=stream.cuda_stream, flags=qflag)
 
     for i in range(args.warmup):
         call(i)
@@ -469,7 +477,8 @@ def bench_backward(args, w, dev):
     flops = 2.5 * useful_flops(w)
     value = flops / (ms * 1e-3) / 1e12
     out = {
-        "metric": f"useful TFLOP/s, BigBird attn bwd L={w.L} H={w.H} d={w.d} {w.dtype}, 1 GPU",
+        "metric": f"useful TFLOP/s, BigBird attn bwd{' (pair-masked)' if args.query_mask else ''} "
+                  f"L={w.L} H={w.H} d={w.d} {w.dtype}, 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -483,6 +492,7 @@ def bench_backward(args, w, dev):
         "data": "synthetic (seeded N(0,1) draws shaped like the BigBird-base attention layer)",
         "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "L": w.L, "d": w.d,
                    "block": w.block, "r": w.r, "pad": w.pad, "mode": args.mode, "input_sets": n_sets,
+                   "query_mask": bool(args.query_mask),
                    "useful_gflop_per_step": round(flops / 1e9, 4),
                    "executed_gflop_per_step": round(3.5 * useful_flops(w) / 1e9, 4)},
         "roofline": {"bound": "mfma", "kernel": "whole backward call (dq, dkdv, reduce)",
@@ -491,7 +501,8 @@ def bench_backward(args, w, dev):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_backward(w, inputs, dout, ri, args.cpu_budget_s)
+        out["cpu_baseline"] = cpu_baseline_backward(w, inputs, dout, ri, args.cpu_budget_s,
+                                                    query_mask=args.query_mask)
     print(json.dumps(out), flush=True)
 
 
@@ -506,6 +517,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--launch", choices=["fused", "split"], default="fused")
+    ap.add_argument("--query-mask", action="store_true",
+                    help="forward with BB_QUERY_MASK (a pair is masked when its query or its key "
+                         "is padding)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -553,6 +567,8 @@ def main():
         bench_layer(args, w, dev, stack=args.which == "stack")
         return
     launch = bb.BB_LAUNCH_SPLIT if args.launch == "split" else bb.BB_LAUNCH_FUSED
+    if args.query_mask:
+        launch |= bb.BB_QUERY_MASK
 
     t0 = time.perf_counter()
     ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
@@ -644,11 +660,12 @@ def main():
         kernel = f"{pre}global_rows_kernel+{pre}middle_rows_kernel"
     achieved = flops / (units_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = committed_traffic(w.name) if kernel == MAIN_KERNEL else None
+    traffic = committed_traffic(w.name) if kernel == MAIN_KERNEL and not args.query_mask else None
 
     out = {
-        "metric": METRIC if w.name == DEFAULT_WORKLOAD else
-                  f"useful TFLOP/s + tokens/s, BigBird attn fwd L={w.L} H={w.H} d={w.d} {w.dtype}, 1 GPU",
+        "metric": METRIC if w.name == DEFAULT_WORKLOAD and not args.query_mask else
+                  f"useful TFLOP/s + tokens/s, BigBird attn fwd{' (pair-masked)' if args.query_mask else ''} "
+                  f"L={w.L} H={w.H} d={w.d} {w.dtype}, 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "tokens_per_s": round(w.tokens / (ms_per_step * 1e-3), 1),
@@ -664,6 +681,7 @@ def main():
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "block": w.block, "r": w.r,
             "pad": w.pad, "mode": args.mode, "input_sets": n_sets, "launch": args.launch,
+            "query_mask": bool(args.query_mask),
             "useful_gflop_per_step": round(flops / 1e9, 4),
             "algorithmic_mb_per_step": round(alg_bytes / 1e6, 3),
             "rand_idx_build_ms_host_untimed": round(t_adj * 1e3, 3),
@@ -686,7 +704,7 @@ def main():
     if traffic is not None:
         out["roofline"]["traffic_GBps"] = round(traffic / (units_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inputs, ri, args.cpu_budget_s)
+        out["cpu_baseline"] = cpu_baseline(w, inputs, ri, args.cpu_budget_s, query_mask=args.query_mask)
     print(json.dumps(out), flush=True)
 
 

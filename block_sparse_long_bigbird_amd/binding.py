@@ -37,7 +37,8 @@ EXPORTS = ("bb_abi_version", "bb_status_str", "bb_rand_idx_build", "bb_rand_idx_
            "bb_attn_forward_timed", "bb_attn_forward_lse", "bb_rand_idx_invert",
            "bb_attn_backward_workspace_bytes", "bb_attn_backward", "bb_layer_workspace_bytes",
            "bb_layer_forward", "bb_attn_forward_noalloc", "bb_layer_stack_workspace_bytes",
-           "bb_layer_stack_forward", "bb_attn_forward_plan")
+           "bb_layer_stack_forward", "bb_attn_forward_plan", "bb_attn_forward_lse_ex",
+           "bb_attn_backward_ex")
 
 _lib = None
 
@@ -88,6 +89,8 @@ def lib():
     L.bb_attn_forward_timed.argtypes = fwd + [ctypes.c_uint, vp, vp]
     L.bb_attn_forward_lse.restype = c_int
     L.bb_attn_forward_lse.argtypes = fwd + [vp]
+    L.bb_attn_forward_lse_ex.restype = c_int
+    L.bb_attn_forward_lse_ex.argtypes = fwd + [vp, ctypes.c_uint]
     L.bb_attn_forward_noalloc.restype = c_int
     L.bb_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, c_int, vp]
     L.bb_rand_idx_invert.restype = c_int
@@ -97,6 +100,8 @@ def lib():
     L.bb_attn_backward.restype = c_int
     L.bb_attn_backward.argtypes = ([vp, vp, vp, vp, vp, vp, vp] + [c_int] * 6 +
                                    [vp, vp, vp, vp, vp, vp, c_int, vp, c_size, vp])
+    L.bb_attn_backward_ex.restype = c_int
+    L.bb_attn_backward_ex.argtypes = L.bb_attn_backward.argtypes + [ctypes.c_uint]
     L.bb_layer_workspace_bytes.restype = c_size
     L.bb_layer_workspace_bytes.argtypes = [c_int] * 5
     L.bb_layer_forward.restype = c_int
@@ -416,9 +421,10 @@ def bb_attn_forward_noalloc(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int,
 
 
 def bb_attn_forward_lse(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: int, block: int,
-                        r: int, out, workspace, lse, stream=None) -> None:
+                        r: int, out, workspace, lse, stream=None, flags: int = 0) -> None:
     """The forward that also writes the row log-sum-exp: lse is a float32
-    device tensor [B, H, L] (natural log)."""
+    device tensor [B, H, L] (natural log).  flags (BB_QUERY_MASK,
+    BB_ORDINARY_UNITS) go through bb_attn_forward_lse_ex."""
     import torch
     _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out)))
     _expect("lse", lse, (B, H, L), (torch.float32,))
@@ -429,9 +435,12 @@ def bb_attn_forward_lse(q, k, v, pad_mask, rand_idx, B: int, H: int, L: int, d: 
     if table:
         _check_rand_idx_contents(rand_idx, H, L, block, r)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().bb_attn_forward_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
-                                   B, H, L, d, block, r, _ptr(out), _dtype_code(q),
-                                   _ptr(workspace), ws_bytes, _stream_handle(q, stream), _ptr(lse))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx), B, H, L, d, block, r, _ptr(out),
+            _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(q, stream), _ptr(lse))
+    if flags:
+        st = lib().bb_attn_forward_lse_ex(*args, flags)
+    else:
+        st = lib().bb_attn_forward_lse(*args)
     if st != BB_OK:
         raise BBError(st, "bb_attn_forward_lse")
 
@@ -457,10 +466,11 @@ def bb_attn_backward_workspace_bytes(B: int, H: int, L: int, d: int, block: int)
 
 def bb_attn_backward(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B: int, H: int, L: int,
                      d: int, block: int, r: int, out, dout, lse, dq, dk, dv, workspace,
-                     stream=None) -> None:
+                     stream=None, flags: int = 0) -> None:
     """Enqueue the backward on `stream` (default: torch's current stream).
     inv_off / inv_rows: int32 device tensors from bb_rand_idx_invert of the same
-    table (checked against it once per table, as rand_idx itself)."""
+    table (checked against it once per table, as rand_idx itself).  flags
+    (BB_QUERY_MASK, as given to the forward) go through bb_attn_backward_ex."""
     import torch
     _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
                                    ("dk", dk), ("dv", dv)))
@@ -474,11 +484,13 @@ def bb_attn_backward(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B: int, H: 
     host = _check_rand_idx_contents(rand_idx, H, L, block, r) if table else None
     _check_inverse(rand_idx, host, inv_off, inv_rows, H, L, block, r)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().bb_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx),
-                                _ptr(inv_off), _ptr(inv_rows), B, H, L, d, block, r, _ptr(out),
-                                _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                                _dtype_code(q), _ptr(workspace), ws_bytes,
-                                _stream_handle(q, stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(pad_mask), _ptr(rand_idx), _ptr(inv_off), _ptr(inv_rows),
+            B, H, L, d, block, r, _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(q, stream))
+    if flags:
+        st = lib().bb_attn_backward_ex(*args, flags)
+    else:
+        st = lib().bb_attn_backward(*args)
     if st != BB_OK:
         raise BBError(st, "bb_attn_backward")
 

@@ -1775,7 +1775,7 @@ __device__ __forceinline__ void tprod(f32x16 (&acc)[2], const VOp<float>& a, con
 // Stage layout: V in the K slot (its rows feed dP^T = V dO^T), K in the V
 // slot (its transposed operand feeds dQ^T += K^T dS^T; its rows, read
 // through the V swizzle, feed S^T = K Q^T).
-template <typename T, int BS, int S, bool HAS_PAD>
+template <typename T, int BS, int S, bool HAS_PAD, bool QM>
 __device__ __forceinline__ void step_dq(WaveState& ws, const u32x4 (&qop)[Cfg<T, BS>::QC],
                                         const u32x4 (&dop)[Cfg<T, BS>::QC], float lse2, float dsum, bool last,
                                         int tile_u, int tile_fill, gchar_ptr vbh, gchar_ptr kbh,
@@ -1792,7 +1792,10 @@ __device__ __forceinline__ void step_dq(WaveState& ws, const u32x4 (&qop)[Cfg<T,
   const VOp<T> kt = cols_op<T, BS, S, 1>(kbase, lane);       // K^T
   if (!last) issue_tile<T, BS, S ^ 1>(vbh, kbh, tile_fill, wave, lane);
   float pbias = 0.0f;
-  if constexpr (HAS_PAD) pbias = apply_pad(s, pw, lane);
+  if constexpr (QM)
+    pbias = apply_pad(s, pw, lane, ws.qs) * ws.qs;
+  else if constexpr (HAS_PAD)
+    pbias = apply_pad(s, pw, lane);
   const float off = lse2 - pbias * kScaleLog2;
   float ds[16];
 #pragma unroll
@@ -1880,7 +1883,7 @@ __device__ __forceinline__ void finalize_dq(WaveState& ws, const Unit& w, int wq
     lds_barrier();   // key groups 2 and 3: the last round's barrier
 }
 
-template <typename T, int BS, bool HAS_PAD>
+template <typename T, int BS, bool HAS_PAD, bool QM>
 __device__ __forceinline__ void run_dq(int n_units) {
   using C = Cfg<T, BS>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1945,6 +1948,10 @@ __device__ __forceinline__ void run_dq(int n_units) {
     }
     ws.m = 0.0f;
     ws.l = 0.0f;
+    // pair masking: a padded query row takes no key offsets (its uniform
+    // offset cancels; the forward's log-sum-exp of such a row leaves it out)
+    ws.qs = 1.0f;
+    if constexpr (QM) ws.qs = pad_b[cu.q0 + wq * 32 + (lane & 31)] != 0 ? 1.0f : 0.0f;
     const int ntiles = cu.ntiles;
     constexpr int TRIP = 12;
     for (int u = 0; u < ntiles; u += TRIP) {
@@ -1960,7 +1967,7 @@ __device__ __forceinline__ void run_dq(int n_units) {
 #define BB_TILE(k) static_cast<int>((tp[(k) >> 1] >> (16 * ((k) & 1))) & 0xffffu)
 #define BB_STEP(k)                                                                                    \
   if ((k) < rem)                                                                                      \
-    step_dq<T, BS, (k) % 2, HAS_PAD>(ws, qop, dop, lse2, dsum, (k) + 1 == rem, BB_TILE(k),            \
+    step_dq<T, BS, (k) % 2, HAS_PAD, QM>(ws, qop, dop, lse2, dsum, (k) + 1 == rem, BB_TILE(k),        \
                                      BB_TILE((k) + 1), vbh, kbh, pad_b, wave, lane, kbase);
       BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
       BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
@@ -2090,12 +2097,21 @@ __device__ __forceinline__ void issue_rowstats(gchar_ptr rs_bh, int tile, int wa
 }
 
 // One query tile: this wave's 32 keys x its 32 queries of the tile.
-template <typename T, int BS, int S>
+template <typename T, int BS, int S, bool QM>
 __device__ __forceinline__ void step_kv(KvState& st, const u32x4 (&kop)[Cfg<T, BS>::QC],
                                         const u32x4 (&vop)[Cfg<T, BS>::QC], float kbias_c, bool last,
                                         int tile_u, int tile_fill, gchar_ptr qbh, gchar_ptr gbh,
-                                        gchar_ptr rs_bh, int wave, int lane, int wq) {
+                                        gchar_ptr rs_bh, int wave, int lane, int wq, const uint8_t* qpad_b) {
   const int qb = wq * 32, g = lane >> 5;
+  // Pair masking with padded keys in this unit: the pad bytes of this wave's
+  // 32 query rows of the tile (null otherwise), loaded before the wait.
+  PadWords qw;
+  if constexpr (QM) {
+    if (qpad_b != nullptr) {
+      qw = load_pad(qpad_b + static_cast<size_t>(tile_u) * BS, qb);
+      asm volatile("" ::: "memory");
+    }
+  }
   __builtin_amdgcn_s_waitcnt(7 << 4);
   ring_barrier();
   // (LSE2, D) of this lane's 16 accumulator rows (two runs of 8 queries), from LDS
@@ -2114,12 +2130,32 @@ __device__ __forceinline__ void step_kv(KvState& st, const u32x4 (&kop)[Cfg<T, B
   const f32x16 dp = rows_times<T, BS, S, 1>(vop, qb, lane);   // dP = dO V^T
   const VOp<T> got = cols_op<T, BS, S, 1>(qb, lane);         // dO^T
   const VOp<T> qt = cols_op<T, BS, S, 0>(qb, lane);          // Q^T
+  // Pair masking: bit i of rpad set when query qb + i of the tile is padding;
+  // such a row takes no key offsets (its uniform offset cancels).
+  uint32_t rpad = 0;
+  if constexpr (QM) {
+    if (qpad_b != nullptr)
+      rpad = zero_byte_mask(qw.p[0]) | (zero_byte_mask(qw.p[1]) << 8) | (zero_byte_mask(qw.p[2]) << 16) |
+             (zero_byte_mask(qw.p[3]) << 24);
+  }
   float p[16], ds[16];
+  if (rpad == 0) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float l2 = l4[v >> 2][v & 3], dd = d4[v >> 2][v & 3];
-    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], kScaleLog2, kbias_c - l2));
-    ds[v] = p[v] * (dp[v] - dd);
+    for (int v = 0; v < 16; ++v) {
+      const float l2 = l4[v >> 2][v & 3], dd = d4[v >> 2][v & 3];
+      p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], kScaleLog2, kbias_c - l2));
+      ds[v] = p[v] * (dp[v] - dd);
+    }
+  } else {
+    // element v of this lane is query qb + 16 (v / 8) + 8 g + 4 ((v / 4) % 2) + v % 4
+    const uint32_t rg = rpad >> (8 * g);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float l2 = l4[v >> 2][v & 3], dd = d4[v >> 2][v & 3];
+      const float kb = (rg >> (16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3))) & 1u ? 0.0f : kbias_c;
+      p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], kScaleLog2, kb - l2));
+      ds[v] = p[v] * (dp[v] - dd);
+    }
   }
   if constexpr (sizeof(T) == 2) {
     bf16x8 pb[2], db[2];
@@ -2237,7 +2273,7 @@ __device__ __forceinline__ void finalize_kv(KvState& st, const KvUnit& w, int wq
     lds_barrier();   // query groups 2 and 3: the last round's barrier
 }
 
-template <typename T, int BS, bool HAS_PAD>
+template <typename T, int BS, bool HAS_PAD, bool QM>
 __device__ __forceinline__ void run_dkdv(int n_units) {
   using C = Cfg<T, BS>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -2268,9 +2304,13 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
     load_q<T, BS>(b->f.k + cu.off + static_cast<size_t>(cu.k0) * C::ROWB, wk, lane, kop);
     load_q<T, BS>(b->f.v + cu.off + static_cast<size_t>(cu.k0) * C::ROWB, wk, lane, vop);
     float kbias_c = 0.0f;
+    const uint8_t* qpad_b = nullptr;   // query pad bytes, when pair masking has key offsets to take back
     if constexpr (HAS_PAD) {
       const uint8_t pv = b->f.pad[static_cast<size_t>(cu.b) * b->f.L + cu.k0 + wk * 32 + (lane & 31)];
       kbias_c = pv == 0 ? kMaskRaw * kScaleLog2 : 0.0f;
+      if constexpr (QM) {
+        if (__any(pv == 0)) qpad_b = b->f.pad + static_cast<size_t>(cu.b) * b->f.L;
+      }
     }
     const gchar_ptr qbh = (gchar_ptr)(b->f.q) + cu.off, gbh = (gchar_ptr)(b->dout) + cu.off;
     const gchar_ptr rs_bh = (gchar_ptr)(b->rowstat + static_cast<size_t>(cu.bh) * b->f.L);
@@ -2299,8 +2339,8 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
 #define BB_TILE(k) static_cast<int>((tp[(k) >> 1] >> (16 * ((k) & 1))) & 0xffffu)
 #define BB_STEP(k)                                                                                    \
   if ((k) < rem)                                                                                      \
-    step_kv<T, BS, (k) % 2>(st, kop, vop, kbias_c, (k) + 1 == rem, BB_TILE(k), BB_TILE((k) + 1), qbh,   \
-                            gbh, rs_bh, wave, lane, wq);
+    step_kv<T, BS, (k) % 2, QM>(st, kop, vop, kbias_c, (k) + 1 == rem, BB_TILE(k), BB_TILE((k) + 1), qbh, \
+                            gbh, rs_bh, wave, lane, wq, qpad_b);
       BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
       BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
 #undef BB_STEP
@@ -2356,13 +2396,15 @@ __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
 // SIMD -- a budget of 3 made the compiler fit 168 with 4 spills at the unit
 // boundaries, 1.6% slower.  Block 128 keeps the budget of 3: with 2 its padded
 // form grows to 221 registers, 2 waves per SIMD.)
-template <typename T, int BS, bool HAS_PAD>
+// QM: pair masking (BB_QUERY_MASK), its own instantiation so that the usual
+// kernels keep their registers.
+template <typename T, int BS, bool HAS_PAD, bool QM>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 64 ? 2 : 3) : (BS == 64 ? 1 : 2)))) bb_bwd_dq_kernel(BwdArgs, int n_units) {
-  run_dq<T, BS, HAS_PAD>(n_units);
+  run_dq<T, BS, HAS_PAD, QM>(n_units);
 }
-template <typename T, int BS, bool HAS_PAD>
+template <typename T, int BS, bool HAS_PAD, bool QM>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : (BS == 64 ? 1 : 2)))) bb_bwd_dkdv_kernel(BwdArgs, int n_units) {
-  run_dkdv<T, BS, HAS_PAD>(n_units);
+  run_dkdv<T, BS, HAS_PAD, QM>(n_units);
 }
 
 
@@ -2867,14 +2909,23 @@ extern "C" int bb_attn_forward_timed(const void* q, const void* k, const void* v
                       stream, flags, start_event, stop_event, nullptr);
 }
 
+extern "C" int bb_attn_forward_lse_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                      const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                                      void* out, int dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream, float* lse, unsigned flags) {
+  if (flags & ~(BB_QUERY_MASK | BB_ORDINARY_UNITS)) return BB_ERR_SHAPE;
+  if (B > 0 && H > 0 && lse == nullptr) return BB_ERR_NULL;
+  if (lse != nullptr && !aligned(lse, 4)) return BB_ERR_ALIGN;
+  return forward_impl(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace, workspace_bytes,
+                      stream, BB_LAUNCH_FUSED | flags, nullptr, nullptr, lse);
+}
+
 extern "C" int bb_attn_forward_lse(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
                                    const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
                                    void* out, int dtype, void* workspace, size_t workspace_bytes,
                                    void* stream, float* lse) {
-  if (B > 0 && H > 0 && lse == nullptr) return BB_ERR_NULL;
-  if (lse != nullptr && !aligned(lse, 4)) return BB_ERR_ALIGN;
-  return forward_impl(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace, workspace_bytes,
-                      stream, BB_LAUNCH_FUSED, nullptr, nullptr, lse);
+  return bb_attn_forward_lse_ex(q, k, v, pad_mask, rand_idx, B, H, L, d, block, r, out, dtype, workspace,
+                                workspace_bytes, stream, lse, 0u);
 }
 
 extern "C" int bb_attn_forward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
@@ -2962,7 +3013,7 @@ BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
   return w;
 }
 
-template <typename T, int BS, bool HAS_PAD>
+template <typename T, int BS, bool HAS_PAD, bool QM>
 int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
   using C = Cfg<T, BS>;
   const long long bhs = static_cast<long long>(B) * H;
@@ -2971,14 +3022,14 @@ int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
   const long long n_units = bhs * (2LL * a.f.n_s + a.f.nb - 2) * (BS / 64);
   (void)rows;
   unsigned grid = 0;
-  int st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dq_kernel<T, BS, HAS_PAD>), C::NT, n_units, &grid);
+  int st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dq_kernel<T, BS, HAS_PAD, QM>), C::NT, n_units, &grid);
   if (st != BB_OK) return st;
-  hipLaunchKernelGGL((bb_bwd_dq_kernel<T, BS, HAS_PAD>), dim3(grid), dim3(C::NT), 0, stream, a,
+  hipLaunchKernelGGL((bb_bwd_dq_kernel<T, BS, HAS_PAD, QM>), dim3(grid), dim3(C::NT), 0, stream, a,
                      static_cast<int>(n_units));
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-  st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dkdv_kernel<T, BS, HAS_PAD>), C::NT, n_units, &grid);
+  st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dkdv_kernel<T, BS, HAS_PAD, QM>), C::NT, n_units, &grid);
   if (st != BB_OK) return st;
-  hipLaunchKernelGGL((bb_bwd_dkdv_kernel<T, BS, HAS_PAD>), dim3(grid), dim3(C::NT), 0, stream, a,
+  hipLaunchKernelGGL((bb_bwd_dkdv_kernel<T, BS, HAS_PAD, QM>), dim3(grid), dim3(C::NT), 0, stream, a,
                      static_cast<int>(n_units));
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   hipLaunchKernelGGL((bb_bwd_reduce_kernel<T, BS>), dim3(static_cast<unsigned>(bhs) * 2 * 3 * (BS / 64) * 8), dim3(64), 0,
@@ -2996,11 +3047,12 @@ extern "C" size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, i
   return bwd_layout(B, H, L, nb, block).total;
 }
 
-extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
-                                const int32_t* rand_idx, const int32_t* inv_off, const int32_t* inv_rows,
-                                int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
-                                const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+extern "C" int bb_attn_backward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                   const int32_t* rand_idx, const int32_t* inv_off, const int32_t* inv_rows,
+                                   int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream, unsigned flags) {
+  if (flags & ~BB_QUERY_MASK) return BB_ERR_SHAPE;
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
   int nb = 0;
   const int st = check_shape(B, H, L, d, block, r, &nb);
@@ -3035,7 +3087,7 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   a.f.nb = nb;
   a.f.r = r;
   a.f.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
-  a.f.qmask = 0;
+  a.f.qmask = (flags & BB_QUERY_MASK) && pad_mask != nullptr ? 1 : 0;
   a.f.gc = a.f.mc = 0;
   a.o = static_cast<const char*>(out);
   a.dout = static_cast<const char*>(dout);
@@ -3051,14 +3103,28 @@ extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, con
   a.dk = static_cast<char*>(dk);
   a.dv = static_cast<char*>(dv);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.f.qmask) {   // pair masking (pad_mask given)
+    if (dtype == BB_BF16)
+      return block == 64 ? launch_bwd<__bf16, 64, true, true>(a, B, H, s) : launch_bwd<__bf16, 128, true, true>(a, B, H, s);
+    return block == 64 ? launch_bwd<float, 64, true, true>(a, B, H, s) : launch_bwd<float, 128, true, true>(a, B, H, s);
+  }
   if (dtype == BB_BF16) {
     if (block == 64)
-      return pad_mask ? launch_bwd<__bf16, 64, true>(a, B, H, s) : launch_bwd<__bf16, 64, false>(a, B, H, s);
-    return pad_mask ? launch_bwd<__bf16, 128, true>(a, B, H, s) : launch_bwd<__bf16, 128, false>(a, B, H, s);
+      return pad_mask ? launch_bwd<__bf16, 64, true, false>(a, B, H, s) : launch_bwd<__bf16, 64, false, false>(a, B, H, s);
+    return pad_mask ? launch_bwd<__bf16, 128, true, false>(a, B, H, s) : launch_bwd<__bf16, 128, false, false>(a, B, H, s);
   }
   if (block == 64)
-    return pad_mask ? launch_bwd<float, 64, true>(a, B, H, s) : launch_bwd<float, 64, false>(a, B, H, s);
-  return pad_mask ? launch_bwd<float, 128, true>(a, B, H, s) : launch_bwd<float, 128, false>(a, B, H, s);
+    return pad_mask ? launch_bwd<float, 64, true, false>(a, B, H, s) : launch_bwd<float, 64, false, false>(a, B, H, s);
+  return pad_mask ? launch_bwd<float, 128, true, false>(a, B, H, s) : launch_bwd<float, 128, false, false>(a, B, H, s);
+}
+
+extern "C" int bb_attn_backward(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                                const int32_t* rand_idx, const int32_t* inv_off, const int32_t* inv_rows,
+                                int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return bb_attn_backward_ex(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B, H, L, d, block, r, out, dout, lse,
+                             dq, dk, dv, dtype, workspace, workspace_bytes, stream, 0u);
 }
 
 // --------------------------------------------------------------- layer host --

@@ -62,8 +62,9 @@ typedef enum { BB_FP32 = 0, BB_BF16 = 1 } bb_dtype;
                               built from it by an einsum of the query and key sides.  Rows of valid
                               queries are unchanged; a padded query row has the same offset on every
                               pair, which cancels in its softmax: it is the unmasked attention row.
-                              No effect when pad_mask is NULL.  Forward output only (not
-                              bb_attn_forward_lse or the backward). */
+                              No effect when pad_mask is NULL.  Also taken by
+                              bb_attn_forward_lse_ex and bb_attn_backward_ex (give both the flag,
+                              or neither). */
 #define BB_ORDINARY_UNITS 16u /* run the ordinary work units even for a small problem.  By default,
                               when the ordinary units are too few to fill the device (fewer than
                               512 of 64 query rows), the fp32 kernels and the bf16 kernels of block
@@ -240,6 +241,16 @@ int bb_attn_forward_lse(const void* q, const void* k, const void* v, const uint8
                         void* out, int dtype, void* workspace, size_t workspace_bytes,
                         void* stream, float* lse);
 
+/* bb_attn_forward_lse with flags: BB_QUERY_MASK (pair masking; then the
+ * log-sum-exp of a padded query row leaves out the row's uniform -10000
+ * offset -- it cancels in that row's softmax and in the backward's rebuilt P,
+ * and kept, an fp32 value near -10000 would hold the row's log-sum-exp to
+ * about 1e-3) and BB_ORDINARY_UNITS.  Other flags: BB_ERR_SHAPE. */
+int bb_attn_forward_lse_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                           const int32_t* rand_idx, int B, int H, int L, int d, int block, int r,
+                           void* out, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream, float* lse, unsigned flags);
+
 /*
  * Invert a HOST random-block table for the backward pass: for every head h
  * and key block j, the middle query blocks i (ascending) whose row
@@ -288,6 +299,15 @@ int bb_attn_backward(const void* q, const void* k, const void* v, const uint8_t*
                      int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* bb_attn_backward with flags: BB_QUERY_MASK, the gradients of the
+ * pair-masked forward (out and lse from bb_attn_forward_lse_ex with the same
+ * flag).  Other flags: BB_ERR_SHAPE. */
+int bb_attn_backward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
+                        const int32_t* rand_idx, const int32_t* inv_off, const int32_t* inv_rows,
+                        int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream, unsigned flags);
 
 /*
  * The attention layer around the op: input projections of the hidden states

@@ -249,13 +249,16 @@ def attention_lse(q, k, pad_mask, rand_idx, block: int, units=None, query_mask: 
 
 
 def attention_backward(q, k, v, pad_mask, rand_idx, block: int, dout, units=None,
-                       row_group: int = 4096):
+                       row_group: int = 4096, query_mask: bool = False):
     """Gradients (dq, dk, dv) of sum(out * dout) for the forward above, fp64.
 
     q, k, v, dout: [B, H, L, d]; pad_mask [B, L] or None; rand_idx [H, nb-2, r].
     Follows the formulas in the module docstring, one (b, h) at a time; rows
     may be taken in groups (dK and dV are sums over rows, added group by group).
     units: optional (b, h) pairs to evaluate; other units are NaN.
+    query_mask: the gradients of the pair-masked forward (pair_masked: the
+    offset on pairs whose query or key is padding; page [P2], section
+    "随机块掩码是如何生成的", the query-side and key-side masks).
     Returns three fp64 [B, H, L, d] arrays.
     """
     B, H, L, d = np.shape(q)
@@ -272,11 +275,12 @@ def attention_backward(q, k, v, pad_mask, rand_idx, block: int, dout, units=None
         adj = block_adjacency(rand_idx[h], nb)
         pad_b = None if pad_mask is None else np.asarray(pad_mask)[b]
         dq[b, h], dk[b, h], dv[b, h] = attention_backward_unit(q[b, h], k[b, h], v[b, h], dout[b, h],
-                                                               pad_b, adj, block, row_group)
+                                                               pad_b, adj, block, row_group, query_mask)
     return dq, dk, dv
 
 
-def attention_backward_unit(q_bh, k_bh, v_bh, dout_bh, pad_b, adj, block: int, row_group: int = 4096):
+def attention_backward_unit(q_bh, k_bh, v_bh, dout_bh, pad_b, adj, block: int, row_group: int = 4096,
+                            query_mask: bool = False):
     """attention_backward for one (batch, head): q_bh, k_bh, v_bh, dout_bh [L, d];
     pad_b [L] or None; adj the head's block adjacency.  Returns (dq, dk, dv), fp64 [L, d]."""
     qb = np.asarray(q_bh, np.float64)
@@ -290,7 +294,7 @@ def attention_backward_unit(q_bh, k_bh, v_bh, dout_bh, pad_b, adj, block: int, r
     dv = np.zeros((L, d))
     for r0 in range(0, L, row_group):
         rows = np.arange(r0, min(L, r0 + row_group))
-        s = _logits_rows(qb, kb, pad_b, adj, block, rows)
+        s = _logits_rows(qb, kb, pad_b, adj, block, rows, query_mask)
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p = p / p.sum(axis=1, keepdims=True)          # P, rows of the softmax

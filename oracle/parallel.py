@@ -64,7 +64,8 @@ def forward_units(q, k, v, pad, rand_idx, block: int, units=None, workers: int =
     return out
 
 
-def backward_units(q, k, v, pad, rand_idx, block: int, dout, units=None, workers: int = 0):
+def backward_units(q, k, v, pad, rand_idx, block: int, dout, units=None, workers: int = 0,
+                   query_mask: bool = False):
     """Oracle gradients (dq, dk, dv) of `units` ((b, h) pairs; default all), each
     float64 [B, H, L, d] with NaN outside the units; the oracle's own
     attention_backward_unit per unit, units spread over host threads."""
@@ -83,7 +84,8 @@ def backward_units(q, k, v, pad, rand_idx, block: int, dout, units=None, workers
     def one(bh):
         b, h = bh
         res = attention_backward_unit(q[b, h], k[b, h], v[b, h], dout[b, h],
-                                      None if pad is None else np.asarray(pad[b]), adj[h], block, group)
+                                      None if pad is None else np.asarray(pad[b]), adj[h], block, group,
+                                      query_mask)
         for g, x in zip(grads, res):
             g[b, h] = x
         return bh

@@ -49,7 +49,7 @@ def f64(t):
     return t.to(torch.float64).numpy()
 
 
-def forward_lse(w, dev, inputs, ri):
+def forward_lse(w, dev, inputs, ri, flags=0):
     q, k, v, pad = inputs
     dq_, dk_, dv_ = q.to(dev), k.to(dev), v.to(dev)
     dpad = None if pad is None else pad.to(dev)
@@ -58,8 +58,9 @@ def forward_lse(w, dev, inputs, ri):
     lse = torch.full((w.B, w.H, w.L), float("nan"), dtype=torch.float32, device=dev)
     n = bb.bb_attn_workspace_bytes(w.B, w.H, w.L, w.d, w.block)
     ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
-    say(f"  forward_lse {w.name} B={w.B} H={w.H} L={w.L} block={w.block} r={w.r} {w.dtype}")
-    bb.bb_attn_forward_lse(dq_, dk_, dv_, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws, lse)
+    say(f"  forward_lse {w.name} B={w.B} H={w.H} L={w.L} block={w.block} r={w.r} {w.dtype} flags={flags}")
+    bb.bb_attn_forward_lse(dq_, dk_, dv_, dpad, dri, w.B, w.H, w.L, w.d, w.block, w.r, out, ws, lse,
+                           flags=flags)
     torch.cuda.synchronize()
     return (dq_, dk_, dv_, dpad, dri), out, lse
 
@@ -133,8 +134,8 @@ BWD_CASES = [
 ]
 
 
-def run_backward(w, dev, inputs, ri, dout):
-    (dq_, dk_, dv_, dpad, dri), out, lse = forward_lse(w, dev, inputs, ri)
+def run_backward(w, dev, inputs, ri, dout, flags=0):
+    (dq_, dk_, dv_, dpad, dri), out, lse = forward_lse(w, dev, inputs, ri, flags)
     off, rows = bb.bb_rand_idx_invert(ri, w.H, w.L, w.block, w.r)
     doff = torch.from_numpy(off).to(dev)
     drows = torch.from_numpy(rows).to(dev) if rows.size else None
@@ -144,7 +145,7 @@ def run_backward(w, dev, inputs, ri, dout):
     ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=dev)
     say(f"  backward {w.name}")
     bb.bb_attn_backward(dq_, dk_, dv_, dpad, dri, doff, drows, w.B, w.H, w.L, w.d, w.block, w.r,
-                        out, g, lse, gq, gk, gv, ws)
+                        out, g, lse, gq, gk, gv, ws, flags=flags)
     torch.cuda.synchronize()
     return [t.float().cpu().numpy() for t in (gq, gk, gv)]
 
@@ -271,3 +272,49 @@ def test_backward_tensors_over_4gib_sampled_units(dev):
         exp = attention_backward(sub(q), sub(k), sub(v), None, ri[h:h + 1], w.block, sub(g))
         got = [t[b:b + 1, h:h + 1].float().cpu().numpy() for t in (gq, gk, gv)]
         check_grads(got, exp, dtype=w.dtype)
+
+
+# ------------------------------------------------ pair masking (BB_QUERY_MASK) ---
+
+QMASK_BWD_CASES = [c for c in BWD_CASES if c.pad != "none"]
+
+
+@pytest.mark.parametrize("w", QMASK_BWD_CASES, ids=[w.name for w in QMASK_BWD_CASES])
+def test_pair_masked_lse_and_backward_match_oracle(dev, w):
+    """bb_attn_forward_lse_ex and bb_attn_backward_ex with BB_QUERY_MASK against
+    the oracle's pair-masked forward, log-sum-exp and gradients.  The kernel's
+    log-sum-exp of a padded query row leaves out the row's uniform -10000 (the
+    header's reading), so the oracle's gets +10000 on those rows."""
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    q, k, v, pad = inputs
+    pn = pad.numpy()
+    _, out, lse = forward_lse(w, dev, inputs, ri, bb.BB_QUERY_MASK)
+    exp_out = attention_forward(f64(q), f64(k), f64(v), pn, ri, w.block, query_mask=True)
+    exp_lse = attention_lse(f64(q), f64(k), pn, ri, w.block, query_mask=True) + 10000.0 * (pn == 0)[:, None, :]
+    got_out, got_lse = out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64)
+    assert not np.isnan(got_lse).any() and not np.isnan(got_out).any()
+    e_out, e_lse = np.abs(got_out - exp_out).max(), np.abs(got_lse - exp_lse).max()
+    say(f"  out err {e_out:.3e}  lse err {e_lse:.3e}")
+    assert e_out <= {"fp32": 1e-5, "bf16": 2e-2}[w.dtype]
+    assert e_lse <= LSE_TOL[w.dtype]
+    got = run_backward(w, dev, inputs, ri, dout, bb.BB_QUERY_MASK)
+    exp = attention_backward(f64(q), f64(k), f64(v), pn, ri, w.block, f64(dout), query_mask=True)
+    check_grads(got, exp, dtype=w.dtype)
+
+
+def test_pair_masked_backward_full_size_every_output(dev):
+    """The benchmark shape (4 x 12 x 4096, per-sequence padding) with pair
+    masking: every gradient of every (batch, head) unit against the oracle."""
+    w = WORKLOADS["base_B4_H12_L4096_pad"]
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    got = run_backward(w, dev, inputs, ri, dout, bb.BB_QUERY_MASK)
+    q, k, v, pad = inputs
+    t0 = time.perf_counter()
+    exp = backward_units(q.float().numpy(), k.float().numpy(), v.float().numpy(), pad.numpy(), ri, w.block,
+                         dout.float().numpy(), query_mask=True)
+    say(f"  oracle on {w.B * w.H} units in {time.perf_counter() - t0:.1f} s")
+    check_grads(got, exp)

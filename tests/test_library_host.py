@@ -189,6 +189,25 @@ def test_forward_validation_errors(lib):
     assert fwd(lib, ws_bytes=need - 1) == 5             # BB_ERR_WORKSPACE
 
 
+def test_lse_and_backward_ex_flags(lib):
+    """The _ex entry points take BB_QUERY_MASK (and the LSE forward
+    BB_ORDINARY_UNITS); any other flag is BB_ERR_SHAPE before a launch."""
+    P = ctypes.c_void_p
+    def lse_ex(flags):
+        return lib.bb_attn_forward_lse_ex(P(FAKE), P(2 * FAKE), P(3 * FAKE), None, P(4 * FAKE), 2, 3, 1024, 64,
+                                          64, 3, P(5 * FAKE), 1, P(6 * FAKE), 1 << 30, None, P(7 * FAKE), flags)
+    def bwd_ex(flags):
+        return lib.bb_attn_backward_ex(P(FAKE), P(2 * FAKE), P(3 * FAKE), None, P(4 * FAKE), P(8 * FAKE),
+                                       P(9 * FAKE), 2, 3, 1024, 64, 64, 3, P(5 * FAKE), P(10 * FAKE),
+                                       P(7 * FAKE), P(11 * FAKE), P(12 * FAKE), P(13 * FAKE), 1, P(6 * FAKE),
+                                       1 << 30, None, flags)
+    for f in (bb.BB_LAUNCH_SPLIT, bb.BB_PHASE_UNITS, bb.BB_PHASE_MERGE, 32):
+        assert lse_ex(f) == 2, f
+    for f in (bb.BB_LAUNCH_SPLIT, bb.BB_ORDINARY_UNITS, 32):
+        assert bwd_ex(f) == 2, f
+    assert lse_ex(bb.BB_QUERY_MASK | 64) == 2
+
+
 def test_forward_empty_is_noop(lib):
     """B == 0 or H == 0: nothing to do, BB_OK without touching any pointer."""
     assert fwd(lib, B=0, q=0, k=0, v=0, out=0, ws=0, rand=0) == 0

@@ -9,7 +9,11 @@ Each pin comes from outside the oracle's backward formulas:
     key-gradient sum vanishes and the value-gradient sum equals the
     output-gradient sum; a zero upstream gradient gives zero gradients;
   - the log-sum-exp against torch.logsumexp on the same independent logits,
-    and the forward rebuilt from it.
+    and the forward rebuilt from it;
+  - pair masking (the offset when the query or the key is padding): autograd
+    through the dense logits with the per-pair offset written here, and the
+    closed forms that follow from the softmax -- a valid query row's dQ is the
+    key-only masking's, a padded query row's dQ is the unmasked attention's.
 """
 
 import math
@@ -45,8 +49,9 @@ def dense_mask_torch(L, block, rand_idx_h):
     return m
 
 
-def torch_reference(q, k, v, pad, rand_idx, block, dout):
-    """float64 autograd through dense masked softmax attention."""
+def torch_reference(q, k, v, pad, rand_idx, block, dout, query_mask=False):
+    """float64 autograd through dense masked softmax attention (query_mask: the
+    -10000 on a pair whose query or key is padding, else whose key is)."""
     B, H, L, d = q.shape
     qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
     outs, lses = [], []
@@ -55,7 +60,9 @@ def torch_reference(q, k, v, pad, rand_idx, block, dout):
         for h in range(H):
             s = qt[b, h] @ kt[b, h].T / math.sqrt(d)
             if pad is not None:
-                s = s + torch.tensor(np.where(pad[b] == 0, -10000.0, 0.0))[None, :]
+                kp = pad[b] == 0
+                off = (kp[None, :] | kp[:, None]) if query_mask else np.broadcast_to(kp[None, :], (L, L))
+                s = s + torch.tensor(np.where(off, -10000.0, 0.0))
             s = s.masked_fill(~dense_mask_torch(L, block, rand_idx[h]), float("-inf"))
             ob.append(torch.softmax(s, dim=1) @ vt[b, h])
             lb.append(torch.logsumexp(s, dim=1))
@@ -146,3 +153,30 @@ def test_lse_rebuilds_the_forward():
         assert np.abs(p.sum(axis=1) - 1.0).max() <= 1e-12
         assert np.abs(p @ v[0, h] - out[0, h]).max() <= 1e-12
     check_rand_idx(ri, 2, 24, 4, 1)
+
+
+@pytest.mark.parametrize("nb,block,r", [(8, 4, 3), (10, 2, 5)])
+def test_pair_masked_backward_matches_torch_autograd(nb, block, r):
+    q, k, v, g, ri, pad = make_case(300 + nb, 2, 2, nb, block, 4, r, True)
+    q = q * 2.0
+    tq, tk, tv, tlse, tout = torch_reference(q, k, v, pad, ri, block, g, query_mask=True)
+    dq, dk, dv = attention_backward(q, k, v, pad, ri, block, g, query_mask=True)
+    for a, b in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.abs(a - b).max() <= 1e-10 * max(1.0, np.abs(b).max())
+    assert np.abs(attention_lse(q, k, pad, ri, block, query_mask=True) - tlse).max() <= 1e-9
+
+
+def test_pair_masked_backward_closed_forms():
+    """dQ of a valid query row is the key-only masking's; dQ of a padded query
+    row is the unmasked attention's (its offset is uniform and cancels); the
+    softmax invariants still hold."""
+    q, k, v, g, ri, pad = make_case(41, 2, 2, 9, 4, 4, 2, True)
+    dq, dk, dv = attention_backward(q, k, v, pad, ri, 4, g, query_mask=True)
+    dq_key, _, _ = attention_backward(q, k, v, pad, ri, 4, g)
+    dq_none, _, _ = attention_backward(q, k, v, None, ri, 4, g)
+    valid = (pad != 0)[:, None, :, None]
+    assert np.abs(np.where(valid, dq - dq_key, 0.0)).max() <= 1e-12
+    assert np.abs(np.where(valid, 0.0, dq - dq_none)).max() <= 1e-12
+    assert (~valid).any() and np.abs(np.where(valid, 0.0, dq_key - dq_none)).max() > 1e-3
+    assert np.abs(dk.sum(axis=2)).max() <= 1e-11
+    assert np.abs(dv.sum(axis=2) - g.sum(axis=2)).max() <= 1e-11
