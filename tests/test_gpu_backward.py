@@ -193,6 +193,24 @@ def test_backward_full_size_every_output(dev):
     check_grads(got, exp)
 
 
+@pytest.mark.parametrize("name", ["fp32_B1_H2_L1024", "large_B8_H16_L4096", "long_B1_H12_L32768_bs128"])
+def test_backward_other_benchmark_shapes_every_output(dev, name):
+    """The other benchmark shapes (fp32 1 x 2 x 1024; 8 x 16 x 4096; 1 x 12 x
+    32768 at block 128): every gradient of every (batch, head) unit against
+    the oracle (units spread over host threads)."""
+    w = WORKLOADS[name]
+    inputs = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    got = run_backward(w, dev, inputs, ri, dout)
+    q, k, v, pad = inputs
+    t0 = time.perf_counter()
+    exp = backward_units(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                         None if pad is None else pad.numpy(), ri, w.block, dout.float().numpy())
+    say(f"  oracle on {w.B * w.H} units in {time.perf_counter() - t0:.1f} s")
+    check_grads(got, exp, dtype=w.dtype)
+
+
 def test_capped_random_range_forward_and_backward(dev):
     """A table whose random blocks all sit in the first 8 blocks (cap at token
     512): the inverted table then gives those key blocks long query lists
