@@ -39,6 +39,14 @@
 // through LDS at the end.
 //
 // fp32 inputs run the same code with fp32 MFMA (32x32x2) and fp32 P.
+//
+// Two more forms of the unit kernel share the work units, tile lists,
+// partials and merge: bf16 at block 128 runs the 32-key-step kernel (two
+// waves of complete rows per workgroup, no merge between waves; its section
+// below), and problems with too few units to fill the device run "kind 3"
+// units, every query block split over its key tiles (small_split()).  The bf16
+// softmax takes a unit's probabilities against one fixed reference per row
+// with an exact slow path (softmax_pv(), redo_unit_w()).
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
