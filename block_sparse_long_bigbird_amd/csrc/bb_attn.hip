@@ -2455,6 +2455,63 @@ __device__ __forceinline__ void dma16x2(gchar_ptr base, uint32_t o0, uint32_t o1
       : "memory", "m0");
 }
 
+// Tile order of the projections.  Consecutive workgroups go round-robin to
+// the 8 XCDs, each with its own L2: when the row panels split evenly, XCD x
+// takes panels [x pm, (x+1) pm) and walks them in groups of GM panels, column
+// tile by column tile, so the A panels and W tiles its resident workgroups
+// share stay in its L2 (one read of the layer's A per XCD instead of per tile
+// column).
+__device__ __forceinline__ void proj_tile(int tiles_m, int tiles_n, int& tm, int& tn) {
+  if ((tiles_m & 7) == 0) {
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int pm = tiles_m >> 3;
+    const int GM = pm % 8 == 0 ? 8 : (pm % 4 == 0 ? 4 : 1);
+    const int grp = idx / (GM * tiles_n), rr = idx - grp * (GM * tiles_n);
+    tm = xcd * pm + grp * GM + rr % GM;
+    tn = rr / GM;
+  } else {
+    tm = blockIdx.x / tiles_n;
+    tn = blockIdx.x - tm * tiles_n;
+  }
+}
+
+// Epilogue of a wave's SN x SMW subtiles of C^T: lane (j, gh) holds C[m][n]
+// for m = mw + 32 ms + j and n = nw + 32 ns + 16 h + 8 gh + (0..7); the bias
+// is added and each run of 8 columns is one 16-byte store.
+template <int MODE, int SMW, int SN>
+__device__ __forceinline__ void proj_epilogue(const ProjArgs& g, const f32x16 (&acc)[SN][SMW], int mw, int nw,
+                                              int j, int gh) {
+#pragma unroll
+  for (int ns = 0; ns < SN; ++ns)
+#pragma unroll
+    for (int ms = 0; ms < SMW; ++ms) {
+      const int m = mw + ms * 32 + j;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = nw + ns * 32 + 16 * h + 8 * gh;
+        const f32x4 b0v = *reinterpret_cast<const f32x4*>(g.bias + n);
+        const f32x4 b1v = *reinterpret_cast<const f32x4*>(g.bias + n + 4);
+        float x8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x8[e] = acc[ns][ms][8 * h + e] + b0v[e];
+          x8[4 + e] = acc[ns][ms][8 * h + 4 + e] + b1v[e];
+        }
+        char* dst;
+        if (MODE == 0) {
+          const int which = n / g.hidden, nn = n - which * g.hidden;
+          const int hh = nn >> 6, dd = nn & 63;
+          const int bb = m / g.L, l = m - bb * g.L;
+          dst = g.out + static_cast<size_t>(which) * g.M * g.hidden * 2 +
+                ((static_cast<size_t>(bb) * g.H + hh) * g.L + l) * 128 + dd * 2;
+        } else {
+          dst = g.out + (static_cast<size_t>(m) * g.N + n) * 2;
+        }
+        store_row8(dst, x8, static_cast<__bf16*>(nullptr));
+      }
+    }
+}
+
 template <int MODE, int WMW, int SMW, int SN>
 __global__ void __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(SMW > 2 ? 1 : 2)))
 bb_proj_kernel(ProjArgs g) {
@@ -2470,24 +2527,8 @@ bb_proj_kernel(ProjArgs g) {
   const int j = lane & 31, gh = lane >> 5;
   const int tiles_n = g.N / TN;
   const int tiles_m = g.M / TM;
-  // Tile order.  Consecutive workgroups go round-robin to the 8 XCDs, each
-  // with its own L2: when the row panels split evenly, XCD x takes panels
-  // [x pm, (x+1) pm) and walks them in groups of GM panels, column tile by
-  // column tile, so the A panels and W tiles its resident workgroups share
-  // stay in its L2 (one read of the layer's A per XCD instead of per tile
-  // column).
   int tm, tn;
-  if ((tiles_m & 7) == 0) {
-    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-    const int pm = tiles_m >> 3;
-    const int GM = pm % 8 == 0 ? 8 : (pm % 4 == 0 ? 4 : 1);
-    const int grp = idx / (GM * tiles_n), rr = idx - grp * (GM * tiles_n);
-    tm = xcd * pm + grp * GM + rr % GM;
-    tn = rr / GM;
-  } else {
-    tm = blockIdx.x / tiles_n;
-    tn = blockIdx.x - tm * tiles_n;
-  }
+  proj_tile(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * TM, n0 = tn * TN;
   const int nk = g.K / 64;
   // A rows of this tile: MODE 1 reads head ks of batch b, rows l0 .. l0+TM-1
@@ -2565,36 +2606,7 @@ bb_proj_kernel(ProjArgs g) {
           acc[ns][ms] = mfma_qk(aop[ns], bop[ms], acc[ns][ms], static_cast<__bf16*>(nullptr));
     }
   }
-  // epilogue: lane (j, gh) holds C[m][n] for m = its row, n in two runs of 8
-#pragma unroll
-  for (int ns = 0; ns < SN; ++ns)
-#pragma unroll
-    for (int ms = 0; ms < SMW; ++ms) {
-      const int m = m0 + wm * (32 * SMW) + ms * 32 + j;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int n = n0 + wn * (32 * SN) + ns * 32 + 16 * h + 8 * gh;
-        const f32x4 b0v = *reinterpret_cast<const f32x4*>(g.bias + n);
-        const f32x4 b1v = *reinterpret_cast<const f32x4*>(g.bias + n + 4);
-        float x8[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x8[e] = acc[ns][ms][8 * h + e] + b0v[e];
-          x8[4 + e] = acc[ns][ms][8 * h + 4 + e] + b1v[e];
-        }
-        char* dst;
-        if (MODE == 0) {
-          const int which = n / g.hidden, nn = n - which * g.hidden;
-          const int hh = nn >> 6, dd = nn & 63;
-          const int bb = m / g.L, l = m - bb * g.L;
-          dst = g.out + static_cast<size_t>(which) * g.M * g.hidden * 2 +
-                ((static_cast<size_t>(bb) * g.H + hh) * g.L + l) * 128 + dd * 2;
-        } else {
-          dst = g.out + (static_cast<size_t>(m) * g.N + n) * 2;
-        }
-        store_row8(dst, x8, static_cast<__bf16*>(nullptr));
-      }
-    }
+  proj_epilogue<MODE, SMW, SN>(g, acc, m0 + wm * (32 * SMW), n0 + wn * (32 * SN), j, gh);
 }
 
 // Launch C = A W^T + bias for one projection: tiles of 128 rows of A by 192

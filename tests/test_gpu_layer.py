@@ -72,6 +72,10 @@ LAYER_CASES = [
           valid_len=8 * 64 - 77, data_seed=72),
     small("layer_h128_bs128_nb6_r1", B=1, H=2, L=6 * 128, block=128, r=1, data_seed=73),
     small("layer_h768_nb10_r3", B=1, H=12, L=10 * 64 + 128, block=64, r=3, data_seed=74),
+    # B*L a multiple of 256 but L not: the QKV projection's 256-row tiles
+    # straddle the two sequences; the output projection takes 128-row tiles
+    small("layer_h768_B2_L384_pad", B=2, H=12, L=6 * 64, block=64, r=1, pad="fixed",
+          valid_len=6 * 64 - 50, data_seed=75),
 ]
 
 
