@@ -470,7 +470,8 @@ def bb_attn_backward(q, k, v, pad_mask, rand_idx, inv_off, inv_rows, B: int, H: 
     """Enqueue the backward on `stream` (default: torch's current stream).
     inv_off / inv_rows: int32 device tensors from bb_rand_idx_invert of the same
     table (checked against it once per table, as rand_idx itself).  flags
-    (BB_QUERY_MASK, as given to the forward) go through bb_attn_backward_ex."""
+    (BB_QUERY_MASK, as given to the forward; BB_ORDINARY_UNITS) go through
+    bb_attn_backward_ex."""
     import torch
     _check_qkv_out(B, H, L, d, q, (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
                                    ("dk", dk), ("dv", dv)))

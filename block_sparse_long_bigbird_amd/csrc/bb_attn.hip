@@ -1891,7 +1891,10 @@ __device__ __forceinline__ void finalize_dq(WaveState& ws, const Unit& w, int wq
     lds_barrier();   // key groups 2 and 3: the last round's barrier
 }
 
-template <typename T, int BS, bool HAS_PAD, bool QM>
+// KIND 0: the forward's ordinary units (middle query blocks finalised in
+// place, global ones as split-K partials); KIND 3: the forward's small-problem
+// units, every one a partial.
+template <typename T, int BS, bool HAS_PAD, bool QM, int KIND>
 __device__ __forceinline__ void run_dq(int n_units) {
   using C = Cfg<T, BS>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1913,9 +1916,9 @@ __device__ __forceinline__ void run_dq(int n_units) {
     }
   }
   if (first >= end) return;
-  Cursor cur = cursor_at<T, BS, 0>(kargs(), first);
+  Cursor cur = cursor_at<T, BS, KIND>(kargs(), first);
   for (;;) {
-    const Unit cu = decode_unit<T, BS, 0>(kargs(), cur);
+    const Unit cu = decode_unit<T, BS, KIND>(kargs(), cur);
     const bargs_ptr b = bargs();
     const size_t row = cu.off / C::ROWB + cu.q0 + wq * 32 + (lane & 31);
     u32x4 qop[C::QC], dop[C::QC], oop[C::QC];
@@ -1987,7 +1990,7 @@ __device__ __forceinline__ void run_dq(int n_units) {
     else
       finalize_dq<T, BS, 0>(ws, cu, wq, wk, lane);
     lds_barrier();   // the exchange area is read before the next unit's first tile lands there
-    cur = cursor_advance<T, BS, 0>(kargs(), cur, stride);
+    cur = cursor_advance<T, BS, KIND>(kargs(), cur, stride);
     if (cur.unit >= end) break;
   }
 }
@@ -2002,11 +2005,15 @@ struct KvTiles {
   int nwin;              // middle: band rows inside 1..nb-2
   int nb;
   int global;
+  int skip;              // middle unit: position of its first tile in the block's list
+                         // (non-zero only for the query chunks of kind 3 units)
+  int unused;            // (keeps the struct free of padding)
   const_i32_ptr inv;     // middle: its inverted-table rows
 };
 
 __device__ __forceinline__ int kv_tile_at(const KvTiles& tl, int u) {
   if (tl.global) return tl.first + u;
+  u += tl.skip;
   if (u == 0) return 0;
   if (u == 1) return tl.nb - 1;
   if (u < 2 + tl.nwin) return tl.first + u - 2;
@@ -2022,17 +2029,76 @@ struct KvUnit {
   KvTiles tl;
 };
 
-template <typename T, int BS>
+// Query tiles [i0, i1) of inv_rows seeing key block j of head h: the
+// inverted table's range, clamped into the table, so that a corrupted offset
+// cannot read outside it.
+__device__ __forceinline__ void inv_range(bargs_ptr a, int h, int j, int& i0, int& i1) {
+  const int nb = a->f.nb;
+  const int32_t* offs = a->inv_off + static_cast<size_t>(h) * (nb + 1);
+  const int total = a->f.H * (nb - 2) * a->f.r;
+  const int o0 = offs[j], o1 = offs[j + 1];
+  i0 = o0 < 0 ? 0 : (o0 > total ? total : o0);
+  i1 = o1 < i0 ? i0 : (o1 > total ? total : o1);
+}
+
+// KIND 0: the ordinary units above.  KIND 3 (problems with too few units to
+// fill the chip): every key block's query list split into chunks -- a->f.gc
+// per global key block, a->f.mc per middle one, each a contiguous run of the
+// list -- every unit writing partials, slots per (b, h) as for the dQ pass:
+// [key block 0 chunks | key block nb-1 chunks | middle key block 1 chunks | ...].
+template <typename T, int BS, int KIND>
 __device__ __forceinline__ KvUnit decode_kv_unit(bargs_ptr a, const Cursor& c) {
   constexpr int KS = BS / 64;           // 64-key units per key block
   constexpr int LKS = KS == 2 ? 1 : 0;
   const int nb = a->f.nb, n_s = a->f.n_s;
-  const int n_g = 2 * n_s * KS;
   KvUnit w;
   w.bh = static_cast<size_t>(c.bh);
   w.off = static_cast<size_t>(c.bh) * a->f.L * Cfg<T, BS>::ROWB;
   w.b = c.b;
   w.tl.nb = nb;
+  w.tl.skip = 0;
+  w.tl.unused = 0;
+  if constexpr (KIND == 3) {
+    const int gc = a->f.gc, mc = a->f.mc;
+    const size_t slots = static_cast<size_t>(2 * gc + (nb - 2) * mc);
+    int slot, kb, kh;
+    if (c.u < 2 * gc * KS) {
+      const int half = gc * KS;
+      w.gsel = c.u >= half ? 1 : 0;
+      const int rem = c.u - (w.gsel ? half : 0);
+      const int chunk = rem >> LKS;
+      kh = rem & (KS - 1);
+      kb = w.gsel ? nb - 1 : 0;
+      slot = w.gsel * gc + chunk;
+      w.tl.global = 1;
+      w.tl.first = chunk * nb / gc;             // balanced chunks: none is empty (gc <= nb)
+      w.ntiles = (chunk + 1) * nb / gc - w.tl.first;
+      w.tl.nwin = 0;
+      w.tl.inv = nullptr;
+    } else {
+      const int v = (c.u - 2 * gc * KS) >> LKS;
+      kh = (c.u - 2 * gc * KS) & (KS - 1);
+      const int mi = v / mc, chunk = v - mi * mc;
+      kb = mi + 1;
+      w.gsel = 2;
+      slot = 2 * gc + mi * mc + chunk;
+      const int lo = kb - 1 < 1 ? 1 : kb - 1;
+      const int hi = kb + 1 > nb - 2 ? nb - 2 : kb + 1;
+      int i0, i1;
+      inv_range(a, c.h, kb, i0, i1);
+      w.tl.global = 0;
+      w.tl.first = lo;
+      w.tl.nwin = hi - lo + 1;
+      w.tl.inv = (const_i32_ptr)(a->inv_rows + i0);
+      const int nt = 2 + w.tl.nwin + (i1 - i0);   // mc <= 2 + the fewest band rows: no chunk is empty
+      w.tl.skip = chunk * nt / mc;
+      w.ntiles = (chunk + 1) * nt / mc - w.tl.skip;
+    }
+    w.k0 = kb * BS + kh * 64;
+    w.pbase = (static_cast<size_t>(c.bh) * slots + slot) * BS + kh * 64;
+    return w;
+  }
+  const int n_g = 2 * n_s * KS;
   if (c.u < n_g) {
     w.gsel = c.u >= n_s * KS ? 1 : 0;
     const int rem = c.u - (w.gsel ? n_s * KS : 0);
@@ -2055,12 +2121,8 @@ __device__ __forceinline__ KvUnit decode_kv_unit(bargs_ptr a, const Cursor& c) {
     w.tl.global = 0;
     w.tl.first = lo;
     w.tl.nwin = hi - lo + 1;
-    const int32_t* offs = a->inv_off + static_cast<size_t>(c.h) * (nb + 1);
-    // offsets clamped into the table, so a corrupted one cannot read outside it
-    const int total = a->f.H * (nb - 2) * a->f.r;
-    const int o0 = offs[j], o1 = offs[j + 1];
-    const int i0 = o0 < 0 ? 0 : (o0 > total ? total : o0);
-    const int i1 = o1 < i0 ? i0 : (o1 > total ? total : o1);
+    int i0, i1;
+    inv_range(a, c.h, j, i0, i1);
     w.tl.inv = (const_i32_ptr)(a->inv_rows + i0);
     w.ntiles = 2 + w.tl.nwin + (i1 - i0);
   }
@@ -2281,7 +2343,7 @@ __device__ __forceinline__ void finalize_kv(KvState& st, const KvUnit& w, int wq
     lds_barrier();   // query groups 2 and 3: the last round's barrier
 }
 
-template <typename T, int BS, bool HAS_PAD, bool QM>
+template <typename T, int BS, bool HAS_PAD, bool QM, int KIND>
 __device__ __forceinline__ void run_dkdv(int n_units) {
   using C = Cfg<T, BS>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -2303,10 +2365,10 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
     }
   }
   if (first >= end) return;
-  Cursor cur = cursor_at<T, BS, 0>(kargs(), first);
+  Cursor cur = cursor_at<T, BS, KIND>(kargs(), first);
   for (;;) {
     const bargs_ptr b = bargs();
-    const KvUnit cu = decode_kv_unit<T, BS>(b, cur);
+    const KvUnit cu = decode_kv_unit<T, BS, KIND>(b, cur);
     // K^T and V^T of this wave's 32 keys as B operands (lane j: key k0 + 32 wk + j)
     u32x4 kop[C::QC], vop[C::QC];
     load_q<T, BS>(b->f.k + cu.off + static_cast<size_t>(cu.k0) * C::ROWB, wk, lane, kop);
@@ -2356,16 +2418,17 @@ __device__ __forceinline__ void run_dkdv(int n_units) {
     }
     finalize_kv<T, BS>(st, cu, wq, wk, lane);
     lds_barrier();
-    cur = cursor_advance<T, BS, 0>(kargs(), cur, stride);
+    cur = cursor_advance<T, BS, KIND>(kargs(), cur, stride);
     if (cur.unit >= end) break;
   }
 }
 
-// Sums of the split-K partials: dQ rows of query blocks 0 and nb-1, dK and dV
-// rows of key blocks 0 and nb-1.  Workgroup: 8 rows x 64 dims of one 32-row
-// group of one block of one matrix; thread (q, g, jj) as in the forward's
-// merge; chunks summed in order.
-template <typename T, int BS>
+// Sums of the split-K partials: KIND 0, dQ rows of query blocks 0 and nb-1,
+// dK and dV rows of key blocks 0 and nb-1; KIND 3, the rows of every block of
+// the three.  Workgroup: 8 rows x 64 dims of one 32-row group of one block of
+// one matrix; thread (q, g, jj) as in the forward's merge; chunks summed in
+// order.
+template <typename T, int BS, int KIND>
 __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
   constexpr int ROWB = kD * sizeof(T);
   constexpr int UB = BS / 64;                                 // 64-row blocks per block
@@ -2375,17 +2438,30 @@ __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
   const int ub = rest % UB;
   rest /= UB;
   const int mat = rest % 3, gblk = rest / 3;
-  const int bh = gblk >> 1, gsel = gblk & 1;
-  const int blkid = gsel ? a.f.nb - 1 : 0;
+  int bh, blkid, nsum;
+  size_t base;
+  if constexpr (KIND == 3) {
+    const int nb = a.f.nb, gc = a.f.gc, mc = a.f.mc;
+    bh = gblk / nb;
+    blkid = gblk - bh * nb;
+    const int slot0 = blkid == 0 ? 0 : (blkid == nb - 1 ? gc : 2 * gc + (blkid - 1) * mc);
+    nsum = blkid == 0 || blkid == nb - 1 ? gc : mc;
+    base = static_cast<size_t>(bh) * (2 * gc + (nb - 2) * mc) + slot0;
+  } else {
+    bh = gblk >> 1;
+    const int gsel = gblk & 1;
+    blkid = gsel ? a.f.nb - 1 : 0;
+    nsum = a.f.n_s;
+    base = (static_cast<size_t>(bh) * 2 + gsel) * a.f.n_s;
+  }
   const int t = threadIdx.x;
   const int q = t >> 4, g = (t >> 3) & 1, j = rb * 8 + (t & 7);
   const int lane = j + 32 * g;
   const int row = ub * 64 + grp * 32 + j;
   const float* part = mat == 0 ? a.dq_part : (mat == 1 ? a.dk_part : a.dv_part);
   char* dst = mat == 0 ? a.dq : (mat == 1 ? a.dk : a.dv);
-  const size_t base = (static_cast<size_t>(bh) * 2 + gsel) * a.f.n_s;
   f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  for (int s = 0; s < a.f.n_s; ++s) {
+  for (int s = 0; s < nsum; ++s) {
     const float* blk = part + ((base + s) * BS + ub * 64) * kD;
     acc[0] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 0, q, lane));
     acc[1] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 1, q, lane));
@@ -2406,13 +2482,14 @@ __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
 // form grows to 221 registers, 2 waves per SIMD.)
 // QM: pair masking (BB_QUERY_MASK), its own instantiation so that the usual
 // kernels keep their registers.
-template <typename T, int BS, bool HAS_PAD, bool QM>
+// KIND: 0 ordinary units, 3 the small-problem split.
+template <typename T, int BS, bool HAS_PAD, bool QM, int KIND>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 64 ? 2 : 3) : (BS == 64 ? 1 : 2)))) bb_bwd_dq_kernel(BwdArgs, int n_units) {
-  run_dq<T, BS, HAS_PAD, QM>(n_units);
+  run_dq<T, BS, HAS_PAD, QM, KIND>(n_units);
 }
-template <typename T, int BS, bool HAS_PAD, bool QM>
+template <typename T, int BS, bool HAS_PAD, bool QM, int KIND>
 __global__ void __launch_bounds__((Cfg<T, BS>::NT)) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : (BS == 64 ? 1 : 2)))) bb_bwd_dkdv_kernel(BwdArgs, int n_units) {
-  run_dkdv<T, BS, HAS_PAD, QM>(n_units);
+  run_dkdv<T, BS, HAS_PAD, QM, KIND>(n_units);
 }
 
 
@@ -3020,10 +3097,39 @@ struct BwdLayout {
   size_t rowstat, dq, dk, dv, total;
 };
 
+// The backward's small-problem split (kind 3 units in both passes): with too
+// few ordinary units to fill the chip, every query block (dQ) and every key
+// block (dK/dV) is split over its tile list into the fewest chunks for which
+// the units still number at most kSmallSlots / (block / 64) -- gc chunks per
+// global block, mc per middle block, chunks of about the same number of tiles
+// (lists of about 8).  mc stays within the shortest middle list of the dK/dV
+// pass (its two global rows and band rows), so no chunk is empty; the choice
+// does not depend on r, and neither does the workspace.
+SmallSplit bwd_split(int B, int H, int nb, int block) {
+  const long long qs = block / 64, bh = static_cast<long long>(B) * H;
+  const int n_s = (nb + kChunkTiles - 1) / kChunkTiles;
+  const long long normal = bh * (2LL * n_s + nb - 2) * qs;
+  if (normal >= kSmallUnits || normal == 0) return {0, 0};
+  const int mc_max = 2 + (nb - 2 < 2 ? nb - 2 : 2);
+  for (int cs = 1; cs <= nb; ++cs) {
+    const int gc = (nb + cs - 1) / cs;
+    int mc = (8 + cs - 1) / cs;
+    if (mc > mc_max) mc = mc_max;
+    const long long units = bh * (2LL * gc + static_cast<long long>(nb - 2) * mc) * qs;
+    if (units <= kSmallSlots / qs) return units > normal ? SmallSplit{gc, mc} : SmallSplit{0, 0};
+  }
+  return {0, 0};
+}
+
 BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
   const size_t rows = static_cast<size_t>(B) * H * L;
   const size_t n_s = static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
-  const size_t part = static_cast<size_t>(B) * H * 2 * n_s * block * kD * sizeof(float);
+  // partial blocks per (b, h): the global blocks' split-K chunks, or the
+  // chunks of every block for the small-problem split
+  const SmallSplit sp = bwd_split(B, H, nb, block);
+  const size_t per_bh = sp.gc > 0 ? 2 * static_cast<size_t>(sp.gc) + static_cast<size_t>(nb - 2) * sp.mc : 0;
+  const size_t blocks = per_bh > 2 * n_s ? per_bh : 2 * n_s;
+  const size_t part = static_cast<size_t>(B) * H * blocks * block * kD * sizeof(float);
   BwdLayout w;
   w.rowstat = 0;
   w.dq = w.rowstat + align256(rows * 2 * sizeof(float));
@@ -3033,29 +3139,37 @@ BwdLayout bwd_layout(int B, int H, int L, int nb, int block) {
   return w;
 }
 
-template <typename T, int BS, bool HAS_PAD, bool QM>
-int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
+template <typename T, int BS, bool HAS_PAD, bool QM, int KIND>
+int launch_bwd_kind(const BwdArgs& a, long long n_units, long long reduce_blocks, hipStream_t stream) {
   using C = Cfg<T, BS>;
-  const long long bhs = static_cast<long long>(B) * H;
-  const long long rows = bhs * a.f.L;
-  // 64-row query units (dQ) and 64-key units (dK/dV): the same count
-  const long long n_units = bhs * (2LL * a.f.n_s + a.f.nb - 2) * (BS / 64);
-  (void)rows;
   unsigned grid = 0;
-  int st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dq_kernel<T, BS, HAS_PAD, QM>), C::NT, n_units, &grid);
+  int st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dq_kernel<T, BS, HAS_PAD, QM, KIND>), C::NT, n_units,
+                           &grid);
   if (st != BB_OK) return st;
-  hipLaunchKernelGGL((bb_bwd_dq_kernel<T, BS, HAS_PAD, QM>), dim3(grid), dim3(C::NT), 0, stream, a,
+  hipLaunchKernelGGL((bb_bwd_dq_kernel<T, BS, HAS_PAD, QM, KIND>), dim3(grid), dim3(C::NT), 0, stream, a,
                      static_cast<int>(n_units));
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-  st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dkdv_kernel<T, BS, HAS_PAD, QM>), C::NT, n_units, &grid);
+  st = persistent_grid(reinterpret_cast<const void*>(&bb_bwd_dkdv_kernel<T, BS, HAS_PAD, QM, KIND>), C::NT, n_units,
+                       &grid);
   if (st != BB_OK) return st;
-  hipLaunchKernelGGL((bb_bwd_dkdv_kernel<T, BS, HAS_PAD, QM>), dim3(grid), dim3(C::NT), 0, stream, a,
+  hipLaunchKernelGGL((bb_bwd_dkdv_kernel<T, BS, HAS_PAD, QM, KIND>), dim3(grid), dim3(C::NT), 0, stream, a,
                      static_cast<int>(n_units));
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
-  hipLaunchKernelGGL((bb_bwd_reduce_kernel<T, BS>), dim3(static_cast<unsigned>(bhs) * 2 * 3 * (BS / 64) * 8), dim3(64), 0,
-                     stream, a);
+  // reduce: 8 workgroups per 64 rows of each summed block of each matrix
+  hipLaunchKernelGGL((bb_bwd_reduce_kernel<T, BS, KIND>), dim3(static_cast<unsigned>(reduce_blocks * 3 * (BS / 64) * 8)),
+                     dim3(64), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return BB_ERR_HIP;
   return BB_OK;
+}
+
+template <typename T, int BS, bool HAS_PAD, bool QM>
+int launch_bwd(const BwdArgs& a, int B, int H, hipStream_t stream) {
+  const long long bhs = static_cast<long long>(B) * H;
+  // 64-row query units (dQ) and 64-key units (dK/dV): the same count in either kind
+  if (a.f.gc > 0)
+    return launch_bwd_kind<T, BS, HAS_PAD, QM, 3>(a, bhs * (2LL * a.f.gc + (a.f.nb - 2LL) * a.f.mc) * (BS / 64),
+                                                  bhs * a.f.nb, stream);
+  return launch_bwd_kind<T, BS, HAS_PAD, QM, 0>(a, bhs * (2LL * a.f.n_s + a.f.nb - 2) * (BS / 64), bhs * 2, stream);
 }
 
 }  // namespace
@@ -3072,7 +3186,7 @@ extern "C" int bb_attn_backward_ex(const void* q, const void* k, const void* v, 
                                    int B, int H, int L, int d, int block, int r, const void* out, const void* dout,
                                    const float* lse, void* dq, void* dk, void* dv, int dtype, void* workspace,
                                    size_t workspace_bytes, void* stream, unsigned flags) {
-  if (flags & ~BB_QUERY_MASK) return BB_ERR_SHAPE;
+  if (flags & ~(BB_QUERY_MASK | BB_ORDINARY_UNITS)) return BB_ERR_SHAPE;
   if (dtype != BB_FP32 && dtype != BB_BF16) return BB_ERR_DTYPE;
   int nb = 0;
   const int st = check_shape(B, H, L, d, block, r, &nb);
@@ -3109,6 +3223,11 @@ extern "C" int bb_attn_backward_ex(const void* q, const void* k, const void* v, 
   a.f.n_s = (nb + kChunkTiles - 1) / kChunkTiles;
   a.f.qmask = (flags & BB_QUERY_MASK) && pad_mask != nullptr ? 1 : 0;
   a.f.gc = a.f.mc = 0;
+  if (!(flags & BB_ORDINARY_UNITS)) {
+    const SmallSplit sp = bwd_split(B, H, nb, block);
+    a.f.gc = sp.gc;
+    a.f.mc = sp.mc;
+  }
   a.o = static_cast<const char*>(out);
   a.dout = static_cast<const char*>(dout);
   a.lse = lse;

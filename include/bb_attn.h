@@ -70,7 +70,10 @@ typedef enum { BB_FP32 = 0, BB_BF16 = 1 } bb_dtype;
                               512 of 64 query rows), the fp32 kernels and the bf16 kernels of block
                               64 split every query block over its key tiles instead and merge the
                               chunks afterwards (BB_LAUNCH_SPLIT then has no second launch); the
-                              result agrees to rounding.  For tests that want the ordinary units. */
+                              result agrees to rounding.  The backward (bb_attn_backward_ex, any
+                              dtype and block) splits the same way: every query block over its
+                              key tiles for dQ, every key block over its query tiles for dK and
+                              dV, summed afterwards.  For tests that want the ordinary units. */
 
 /* Version of this ABI (BB_ABI_VERSION of the built library). */
 int bb_abi_version(void);
@@ -265,7 +268,9 @@ int bb_rand_idx_invert(const int32_t* rand_idx, int H, int L, int block, int r, 
                        int32_t* inv_rows);
 
 /* Bytes of device workspace bb_attn_backward needs (0 for empty or
- * unsupported sizes). */
+ * unsupported sizes): the rows' (LSE, D) pairs and fp32 partials of dQ, dK
+ * and dV -- of the global blocks' chunks, or for small problems (see
+ * BB_ORDINARY_UNITS) of every block's chunks. */
 size_t bb_attn_backward_workspace_bytes(int B, int H, int L, int d, int block);
 
 /*
@@ -302,7 +307,8 @@ int bb_attn_backward(const void* q, const void* k, const void* v, const uint8_t*
 
 /* bb_attn_backward with flags: BB_QUERY_MASK, the gradients of the
  * pair-masked forward (out and lse from bb_attn_forward_lse_ex with the same
- * flag).  Other flags: BB_ERR_SHAPE. */
+ * flag), and BB_ORDINARY_UNITS (no small-problem split).  Other flags:
+ * BB_ERR_SHAPE. */
 int bb_attn_backward_ex(const void* q, const void* k, const void* v, const uint8_t* pad_mask,
                         const int32_t* rand_idx, const int32_t* inv_off, const int32_t* inv_rows,
                         int B, int H, int L, int d, int block, int r, const void* out, const void* dout,

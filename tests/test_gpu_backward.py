@@ -165,12 +165,17 @@ def check_grads(got, exp, units=None, dtype="bf16"):
     return worst
 
 
+@pytest.mark.parametrize("units", ["default", "ordinary"])
 @pytest.mark.parametrize("w", BWD_CASES, ids=[w.name for w in BWD_CASES])
-def test_backward_matches_oracle(dev, w):
+def test_backward_matches_oracle(dev, w, units):
+    """Every gradient of the small cases, with the small-problem split (every
+    one of these shapes has fewer ordinary units than the split's threshold)
+    and with the ordinary units (BB_ORDINARY_UNITS: the in-place middle blocks,
+    the global blocks' split-K, tile lists longer than one trip)."""
     inputs = make_inputs(w)
     dout = make_dout(w)
     ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
-    got = run_backward(w, dev, inputs, ri, dout)
+    got = run_backward(w, dev, inputs, ri, dout, flags=bb.BB_ORDINARY_UNITS if units == "ordinary" else 0)
     q, k, v, pad = inputs
     exp = attention_backward(f64(q), f64(k), f64(v), None if pad is None else pad.numpy(), ri,
                              w.block, f64(dout))

@@ -190,8 +190,8 @@ def test_forward_validation_errors(lib):
 
 
 def test_lse_and_backward_ex_flags(lib):
-    """The _ex entry points take BB_QUERY_MASK (and the LSE forward
-    BB_ORDINARY_UNITS); any other flag is BB_ERR_SHAPE before a launch."""
+    """The _ex entry points take BB_QUERY_MASK and BB_ORDINARY_UNITS; any
+    other flag is BB_ERR_SHAPE before a launch."""
     P = ctypes.c_void_p
     def lse_ex(flags):
         return lib.bb_attn_forward_lse_ex(P(FAKE), P(2 * FAKE), P(3 * FAKE), None, P(4 * FAKE), 2, 3, 1024, 64,
@@ -203,7 +203,7 @@ def test_lse_and_backward_ex_flags(lib):
                                        1 << 30, None, flags)
     for f in (bb.BB_LAUNCH_SPLIT, bb.BB_PHASE_UNITS, bb.BB_PHASE_MERGE, 32):
         assert lse_ex(f) == 2, f
-    for f in (bb.BB_LAUNCH_SPLIT, bb.BB_ORDINARY_UNITS, 32):
+    for f in (bb.BB_LAUNCH_SPLIT, bb.BB_PHASE_UNITS, 32, bb.BB_ORDINARY_UNITS | 64):
         assert bwd_ex(f) == 2, f
     assert lse_ex(bb.BB_QUERY_MASK | 64) == 2
 
@@ -333,14 +333,45 @@ def test_backward_validation_errors(lib):
     assert bwd(lib, B=1, H=1, block=128, L=2048, ws_bytes=need128 - 1) == 5
 
 
+def bwd_split_blocks(B, H, nb, block):
+    """Partial blocks of the backward's small-problem split (0 when the
+    ordinary units run): fewer than 512 ordinary units -> the fewest chunks per
+    block (about 8 tiles per list; middle blocks at most 2 + min(nb - 2, 2),
+    the shortest dK/dV list) whose units fit 256 / (block / 64) slots, if that
+    gives more units than the ordinary ones."""
+    qs, bh, n_s = block // 64, B * H, -(-nb // 8)
+    normal = bh * (2 * n_s + nb - 2) * qs
+    if normal >= 512:
+        return 0
+    mc_max = 2 + min(nb - 2, 2)
+    for cs in range(1, nb + 1):
+        gc, mc = -(-nb // cs), min(-(-8 // cs), mc_max)
+        units = bh * (2 * gc + (nb - 2) * mc) * qs
+        if units <= 256 // qs:
+            return bh * (2 * gc + (nb - 2) * mc) if units > normal else 0
+    return 0
+
+
+def test_backward_small_split_choice():
+    """Hand-worked cases of the backward's split: 1 x 2 x 1024 at block 64 (36
+    ordinary units) takes one global tile per chunk and 4 chunks per middle
+    block, 2 (32 + 14 * 4) = 176 units; the headline shape keeps its
+    ordinary units."""
+    assert bwd_split_blocks(1, 2, 16, 64) == 2 * (2 * 16 + 14 * 4)
+    assert bwd_split_blocks(4, 12, 64, 64) == 0
+    # nb = 3: the one middle block's dK/dV list holds 3 tiles at least
+    assert bwd_split_blocks(1, 2, 3, 64) == 2 * (2 * 3 + 1 * 3)
+
+
 def test_backward_workspace_size_formula(lib):
-    for B, H, L, block in [(4, 12, 4096, 64), (1, 8, 16384, 64), (1, 2, 192, 64), (1, 12, 32768, 128)]:
+    for B, H, L, block in [(4, 12, 4096, 64), (1, 8, 16384, 64), (1, 2, 192, 64), (1, 12, 32768, 128),
+                           (1, 2, 1024, 64), (2, 2, 7 * 128, 128), (1, 1, 640, 128)]:
         nb = L // block
         n_s = -(-nb // 8)
         def a256(x):
             return (x + 255) // 256 * 256
         rows = B * H * L
-        part = B * H * 2 * n_s * block * 64 * 4
+        part = max(B * H * 2 * n_s, bwd_split_blocks(B, H, nb, block)) * block * 64 * 4
         exp = 2 * a256(rows * 4) + 2 * a256(part) + part
         assert lib.bb_attn_backward_workspace_bytes(B, H, L, 64, block) == exp
 
