@@ -2461,10 +2461,28 @@ __global__ void __launch_bounds__(64) bb_bwd_reduce_kernel(BwdArgs a) {
   const float* part = mat == 0 ? a.dq_part : (mat == 1 ? a.dk_part : a.dv_part);
   char* dst = mat == 0 ? a.dq : (mat == 1 ? a.dk : a.dv);
   f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  for (int s = 0; s < nsum; ++s) {
-    const float* blk = part + ((base + s) * BS + ub * 64) * kD;
-    acc[0] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 0, q, lane));
-    acc[1] += *reinterpret_cast<const f32x4*>(blk + partial_slot(grp, 1, q, lane));
+  // four chunks' loads in flight before their adds (the adds stay in chunk
+  // order); one at a time, each chunk waited out the previous one's latency
+  const float* p0 = part + (base * BS + ub * 64) * kD;
+  constexpr size_t CH = static_cast<size_t>(BS) * kD;        // floats per chunk
+  const int o0 = partial_slot(grp, 0, q, lane), o1 = partial_slot(grp, 1, q, lane);
+  int s = 0;
+  for (; s + 4 <= nsum; s += 4) {
+    f32x4 x[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i][0] = *reinterpret_cast<const f32x4*>(p0 + (s + i) * CH + o0);
+      x[i][1] = *reinterpret_cast<const f32x4*>(p0 + (s + i) * CH + o1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[0] += x[i][0];
+      acc[1] += x[i][1];
+    }
+  }
+  for (; s < nsum; ++s) {
+    acc[0] += *reinterpret_cast<const f32x4*>(p0 + s * CH + o0);
+    acc[1] += *reinterpret_cast<const f32x4*>(p0 + s * CH + o1);
   }
   const float sc = mat == 2 ? 1.0f : 0.125f;   // dQ and dK carry 1/sqrt(64)
   char* orow = dst + (static_cast<size_t>(bh) * a.f.L + static_cast<size_t>(blkid) * BS + row) * ROWB;
