@@ -40,7 +40,8 @@ last-level cache, so each call reads HBM.
 every useful FLOP): a second pass runs the same K steps through the two-phase
 form of the call, each kernel timestamped at its start and end by its own
 launch (hipExtLaunchKernel events on the launch stream), so the kernel's
-execution time is measured without enqueue gaps.  `traffic` is the HBM bytes per launch from
+execution time is measured without enqueue gaps (mean, and p10 / median /
+p90 over the K launches).  `traffic` is the HBM bytes per launch from
 the committed rocprofv3 counter summary, used only if that summary was taken
 on the current kernel source.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of (batch, head) units of the same workload on this host.
@@ -626,7 +627,8 @@ def main():
         call(i, launch | bb.BB_PHASE_UNITS, events=(e[i][0], e[i][1]))
         call(i, launch | bb.BB_PHASE_MERGE, events=(e[i][2], e[i][3]))
     torch.cuda.synchronize()
-    units_ms = float(np.mean([x[0].elapsed_time(x[1]) for x in e]))
+    units_each = np.array([x[0].elapsed_time(x[1]) for x in e])
+    units_ms = float(np.mean(units_each))
     merge_ms = float(np.mean([x[2].elapsed_time(x[3]) for x in e]))
 
     if args.copy_calibration:
@@ -695,7 +697,9 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "launch_us_mean": round(units_ms * 1e3, 3),
+            "launch_us_p10_median_p90": [round(float(np.percentile(units_each, p)) * 1e3, 3) for p in (10, 50, 90)],
             "merge_us_mean": round(merge_ms * 1e3, 3),
+
             "hbm_algorithmic_GBps": round(alg_bytes / (units_ms * 1e-3) / 1e9, 1),
             "hbm_algorithmic_frac": round(alg_bytes / (units_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
