@@ -20,8 +20,8 @@ import numpy as np
 from .bigbird_oracle import (attention_backward_unit, attention_rows, block_adjacency, check_rand_idx,
                              num_blocks)
 
-# A GPU machine grants one GPU's share of its host: 16 cores, whatever the
-# machine-wide count says.
+# At most 16 worker threads: a host shared between GPUs gives each GPU's
+# process about that many cores, whatever the machine-wide count says.
 MAX_WORKERS = 16
 
 
