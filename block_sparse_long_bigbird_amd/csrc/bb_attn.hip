@@ -34,7 +34,8 @@
 // registers turn into the PV operand without any data movement: the K rows
 // fed to the score MFMA are permuted (perm_row) so that each lane's 16 score
 // registers are 2 runs of 8 consecutive keys, exactly the operand layout the
-// PV MFMA wants.  V is staged transposed in LDS (V^T, dims x keys).
+// PV MFMA wants.  V stays row-major in LDS; a transposing LDS read
+// (ds_read_b64_tr_b16) hands it to the PV MFMA as V^T.
 // The two key-half waves of a query group merge their (max, sum, O) states
 // through LDS at the end.
 //
@@ -1653,6 +1654,10 @@ __global__ void __launch_bounds__(kSub32NT) __attribute__((amdgpu_waves_per_eu(4
 //                        dV^T += dO^T P, dK^T += Q^T dS; the two global key
 //                        blocks (seen by every query block) as split-K chunks;
 //   bb_bwd_reduce_kernel sums the split-K partials of those four blocks.
+// Problems with too few units to fill the device run kind 3 units in both
+// passes instead (bwd_split()): every query block's key tiles and every key
+// block's query tiles cut into chunks, every chunk a partial, and the reduce
+// sums the chunks of every block.
 // Every pass stages its streamed tiles through the same two-stage LDS ring
 // as the forward; a tile that is read both as rows and transposed is read
 // one of the two ways through the other matrix's swizzle (correct, with
