@@ -1,7 +1,8 @@
 """GPU parity on seeded random small shapes: the forward with the row
 log-sum-exp and the backward, through the C ABI, against the fp64 oracle,
-each with the small-problem split (the default for all of these shapes) and
-with the ordinary units (BB_ORDINARY_UNITS).
+each with the small-problem split (the default for most of these shapes)
+and with the ordinary units (BB_ORDINARY_UNITS); the padded ones also with
+pair masking (BB_QUERY_MASK).
 
 The shapes are drawn once from a fixed seed (PCG64(2024)): block 64 or 128,
 nb from 3 up, r from 0 to its largest legal value (at most 16), B and H from
@@ -73,15 +74,17 @@ def f64(t):
     return t.to(torch.float64).numpy()
 
 
-@pytest.mark.parametrize("units", ["default", "ordinary"])
-@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
-def test_random_shape_forward_and_backward(dev, w, units):
-    flags = bb.BB_ORDINARY_UNITS if units == "ordinary" else 0
+def run_case(dev, w, units, pair):
+    """Forward with LSE and backward of case w through the C ABI against the
+    oracle; pair: BB_QUERY_MASK (the oracle's pair-masked functions; the
+    kernel's log-sum-exp of a padded query row leaves out the row's uniform
+    -10000, so the oracle's gets +10000 on those rows)."""
+    flags = (bb.BB_ORDINARY_UNITS if units == "ordinary" else 0) | (bb.BB_QUERY_MASK if pair else 0)
     q, k, v, pad = make_inputs(w)
     dout = make_dout(w)
     ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
     off, rows = bb.bb_rand_idx_invert(ri, w.H, w.L, w.block, w.r)
-    say(f"  {w.name} units={units}")
+    say(f"  {w.name} units={units} pair_masked={pair}")
 
     dq_, dk_, dv_ = q.to(dev), k.to(dev), v.to(dev)
     dpad = None if pad is None else pad.to(dev)
@@ -105,16 +108,36 @@ def test_random_shape_forward_and_backward(dev, w, units):
     got_out = out.float().cpu().numpy()
     got_lse = lse.cpu().numpy().astype(np.float64)
     assert not np.isnan(got_out).any() and not np.isnan(got_lse).any(), "unwritten forward outputs"
-    e_out = np.abs(got_out - attention_forward(f64(q), f64(k), f64(v), pn, ri, w.block)).max()
-    e_lse = np.abs(got_lse - attention_lse(f64(q), f64(k), pn, ri, w.block)).max()
+    exp_out = attention_forward(f64(q), f64(k), f64(v), pn, ri, w.block, query_mask=pair)
+    exp_lse = attention_lse(f64(q), f64(k), pn, ri, w.block, query_mask=pair)
+    if pair:
+        exp_lse = exp_lse + 10000.0 * (pn == 0)[:, None, :]
+    e_out, e_lse = np.abs(got_out - exp_out).max(), np.abs(got_lse - exp_lse).max()
     say(f"    out err {e_out:.3e}  lse err {e_lse:.3e}")
     assert e_out <= OUT_TOL[w.dtype]
     assert e_lse <= LSE_TOL[w.dtype]
 
-    exp = attention_backward(f64(q), f64(k), f64(v), pn, ri, w.block, f64(dout))
+    exp = attention_backward(f64(q), f64(k), f64(v), pn, ri, w.block, f64(dout), query_mask=pair)
     for name, g, e in zip(("dq", "dk", "dv"), grads, exp):
         a = g.float().cpu().numpy()
         assert not np.isnan(a).any(), f"unwritten (NaN) {name}"
         err, scale = np.abs(a - e).max(), np.abs(e).max()
         say(f"    {name}: max err {err:.3e}  max |ref| {scale:.3e}")
         assert err <= GRAD_REL[w.dtype] * scale, name
+
+
+@pytest.mark.parametrize("units", ["default", "ordinary"])
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_random_shape_forward_and_backward(dev, w, units):
+    run_case(dev, w, units, pair=False)
+
+
+PADDED = [w for w in CASES if w.pad != "none"]
+
+
+@pytest.mark.parametrize("units", ["default", "ordinary"])
+@pytest.mark.parametrize("w", PADDED, ids=[w.name for w in PADDED])
+def test_random_shape_pair_masked(dev, w, units):
+    """The padded cases again with BB_QUERY_MASK (a pair is masked when its
+    query or its key is padding)."""
+    run_case(dev, w, units, pair=True)
