@@ -1147,10 +1147,13 @@ __device__ __forceinline__ void run(int n_units) {
       if (kargs()->qmask) ws.qs = pad_b[cu.q0 + wq * 32 + (lane_u & 31)] != 0 ? 1.0f : 0.0f;
     }
 
-    // ---- tile loop: trips of 12 straight-line steps ---------------------------
-    // Units of the usual shapes have at most 12 tiles, so one trip covers them.
-    // Tile ids are computed once per trip.
-    constexpr int TRIP = 12;
+    // ---- tile loop: trips of 8 straight-line steps ----------------------------
+    // Middle units at r <= 3 and the global chunks have at most 8 tiles, so
+    // one trip covers them; longer lists take more.  Tile ids are computed
+    // once per trip: the trip's and the one after it (its last step
+    // prefetches that tile), two per scalar register.
+    // (Trips of 12, with their 14 guarded ids, were 1% slower at r = 3.)
+    constexpr int TRIP = 8;
     static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
     for (int u = 0; u < ntiles; u += TRIP) {
       // Tiles left from u.  Opaque, so that the step guards and the last-step
@@ -1172,7 +1175,7 @@ __device__ __forceinline__ void run(int n_units) {
     step<T, BS, (k) % 2, HAS_PAD>(ws, qop, u + (k) == 0, (k) + 1 == rem, BB_TILE(k), BB_TILE((k) + 1),  \
                                   kbh, vbh, pad_b, wave, lane_u, kbase, nx, wq);
       BB_STEP(0) BB_STEP(1) BB_STEP(2) BB_STEP(3) BB_STEP(4) BB_STEP(5)
-      BB_STEP(6) BB_STEP(7) BB_STEP(8) BB_STEP(9) BB_STEP(10) BB_STEP(11)
+      BB_STEP(6) BB_STEP(7)
 #undef BB_STEP
 #undef BB_TILE
     }
