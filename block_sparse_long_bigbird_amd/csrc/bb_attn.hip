@@ -63,7 +63,6 @@ namespace {
 
 constexpr int kD = 64;                   // supported head dimension
 constexpr int kChunkTiles = 8;           // key tiles per global-row work unit
-constexpr int kMaxR = 16;                // random blocks per row, upper bound
 constexpr float kScaleLog2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
 constexpr float kMaskRaw = -10000.0f * 8.0f;  // -10000 on the logit, in q.k units
 constexpr float kRescaleTau = 8.0f;      // lazy rescale threshold (log2 units)
@@ -2770,8 +2769,11 @@ Layout workspace_layout(int B, int H, int nb, int block) {
   // units, or the chunks of every query block for the small-problem split
   // (the largest over every r the sizes allow)
   const size_t bh = static_cast<size_t>(B) * H;
-  size_t blocks = bh * 2 * static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
-  const int r_max = nb - 5 > 0 ? (nb - 5 < kMaxR ? nb - 5 : kMaxR) : 0;
+  const size_t n_s = static_cast<size_t>((nb + kChunkTiles - 1) / kChunkTiles);
+  size_t blocks = bh * 2 * n_s;
+  // (the split needs fewer than kSmallUnits ordinary units, whatever r is)
+  const bool can_split = bh * (2 * n_s + nb - 2) * static_cast<size_t>(block / 64) < static_cast<size_t>(kSmallUnits);
+  const int r_max = can_split && nb - 5 > 0 ? nb - 5 : 0;
   for (int r = 0; r <= r_max; ++r) {
     const SmallSplit sp = small_split(B, H, nb, block, r);
     const size_t n = bh * (2 * static_cast<size_t>(sp.gc) + static_cast<size_t>(nb - 2) * sp.mc);
@@ -2793,7 +2795,7 @@ int check_shape(int B, int H, int L, int d, int block, int r, int* nb_out) {
   const int nb = L / block;
   if (nb < 3 || L / 64 > 65535) return BB_ERR_SHAPE;   // 64-key tile ids fit in 16 bits
   const int r_max = nb - 5 > 0 ? nb - 5 : 0;
-  if (r > r_max || r > kMaxR) return BB_ERR_SHAPE;
+  if (r > r_max) return BB_ERR_SHAPE;
   const int n_s = (nb + kChunkTiles - 1) / kChunkTiles;
   const long long units = static_cast<long long>(B) * H * (2LL * n_s + nb - 2) * (block / 64);
   if (units > 0x7fffffffLL) return BB_ERR_SHAPE;

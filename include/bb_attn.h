@@ -162,7 +162,8 @@ int bb_attn_forward_plan(int B, int H, int L, int d, int block, int r, int dtype
  *   d          head dimension; must be 64.
  *   block      block size; 64 or 128; L % block == 0; nb = L/block >= 3;
  *              L <= 64 * 65535 (64-key tile ids are 16-bit).
- *   r          random blocks per middle row, 0 <= r <= min(16, max(0, nb-5)).
+ *   r          random blocks per middle row, 0 <= r <= max(0, nb-5) (at nb-5 every
+ *              middle row attends every block).
  *   out        DEVICE [B][H][L][d] in `dtype`, 16-byte aligned, fully
  *              overwritten; must not overlap q, k or v.
  *   dtype      BB_BF16 (fp32 accumulation, bf16 output rounded to nearest

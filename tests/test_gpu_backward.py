@@ -118,6 +118,12 @@ BWD_CASES = [
     small("bwd_bs128_nb11_r4_pad", B=1, H=2, L=11 * 128, block=128, r=4, pad="fixed",
           valid_len=11 * 128 - 200, data_seed=63),
     small("bwd_bs128_nb22_r16_two_trips", B=1, H=1, L=22 * 128, block=128, r=16, data_seed=64),
+    # r = nb - 5: every middle row attends every block; the dK/dV lists of the
+    # middle key blocks hold every query block
+    small("bwd_nb30_r25_dense_rows_pad", B=1, H=2, L=30 * 64, block=64, r=25, pad="per_seq_blocks",
+          pad_lo_blocks=12, pad_hi_blocks=30, data_seed=74),
+    small("bwd_fp32_nb26_r21", B=1, H=2, L=26 * 64, block=64, r=21, dtype="fp32", data_seed=75),
+    small("bwd_bs128_nb24_r19", B=1, H=2, L=24 * 128, block=128, r=19, data_seed=76),
     small("bwd_fp32_nb3", B=1, H=2, L=3 * 64, block=64, r=0, dtype="fp32", data_seed=66),
     small("bwd_fp32_nb9_r3_pad", B=2, H=2, L=9 * 64, block=64, r=3, dtype="fp32", pad="fixed",
           valid_len=9 * 64 - 70, data_seed=67),

@@ -113,11 +113,18 @@ SMALL = [
     small("fp32_bs128_nb7_r2", B=1, H=2, L=7 * 128, block=128, r=2, dtype="fp32", data_seed=25),
     small("outliers_unscaled", B=1, H=2, L=16 * 64, block=64, r=3, outlier_frac=0.02,
           outlier_mult=8.0, data_seed=26),
-    # r at its maximum (16): middle units of 21 tiles run the tile loop in two
-    # trips (12 + 9 steps), with padding; and the same in fp32 with block 128
+    # r = 16: middle units of 21 tiles run the tile loop in three trips
+    # (8 + 8 + 5 steps), with padding; and the same in fp32 with block 128
     small("nb24_r16_pad_two_trips", B=2, H=2, L=24 * 64, block=64, r=16, pad="per_seq_blocks",
           pad_lo_blocks=10, pad_hi_blocks=24, data_seed=27),
     small("fp32_bs128_nb22_r16", B=1, H=1, L=22 * 128, block=128, r=16, dtype="fp32", data_seed=28),
+    # r = nb - 5, its largest value: every middle row attends every block
+    # (lists of nb tiles), against the oracle's dense rows; bf16 with padding,
+    # fp32, and bf16 at block 128
+    small("nb30_r25_dense_rows_pad", B=1, H=2, L=30 * 64, block=64, r=25, pad="per_seq_blocks",
+          pad_lo_blocks=12, pad_hi_blocks=30, data_seed=37),
+    small("fp32_nb26_r21", B=1, H=2, L=26 * 64, block=64, r=21, dtype="fp32", data_seed=38),
+    small("bs128_nb24_r19", B=1, H=2, L=24 * 128, block=128, r=19, data_seed=39),
     # pad masks with holes (mixed and fully padded subtiles between valid ones)
     small("nb10_r3_scattered_pad", B=2, H=2, L=10 * 64, block=64, r=3, pad="scattered", data_seed=29),
     small("bs128_nb7_r2_scattered_pad", B=1, H=2, L=7 * 128, block=128, r=2, pad="scattered",
@@ -134,6 +141,7 @@ SMALL = [
     small("huge_logit_gaps_bs128_pad", B=2, H=2, L=8 * 128, block=128, r=2, outlier_frac=0.05,
           outlier_mult=24.0, pad="fixed", valid_len=8 * 128 - 100, data_seed=36),
 ]
+CASE = {w.name: w for w in SMALL}
 
 
 @pytest.mark.parametrize("units", ["default", "ordinary"])
@@ -149,7 +157,8 @@ def test_small_shapes_full_parity(dev, w, units):
     compare_full(w, got, inputs, ri)
 
 
-@pytest.mark.parametrize("w", [SMALL[5], SMALL[6], SMALL[11], SMALL[14]],
+@pytest.mark.parametrize("w", [CASE["nb17_r3_ragged_chunk"], CASE["nb12_r3_pad"], CASE["bs128_nb11_r4_pad"],
+                               CASE["fp32_bs128_nb7_r2"]],
                          ids=lambda w: w.name)
 def test_split_launch_matches_fused_bitwise(dev, w):
     say(f"case split-vs-fused {w.name}")
@@ -159,7 +168,7 @@ def test_split_launch_matches_fused_bitwise(dev, w):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("w", [SMALL[6], SMALL[11]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [CASE["nb12_r3_pad"], CASE["bs128_nb11_r4_pad"]], ids=lambda w: w.name)
 def test_two_phase_call_matches_single_call(dev, w):
     """BB_PHASE_UNITS then BB_PHASE_MERGE on the same stream == one full call, bit for bit."""
     say(f"case two-phase {w.name}")
@@ -179,7 +188,7 @@ def test_two_phase_call_matches_single_call(dev, w):
         assert np.array_equal(out.float().cpu().numpy(), a)
 
 
-@pytest.mark.parametrize("w", [SMALL[6], SMALL[11]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [CASE["nb12_r3_pad"], CASE["bs128_nb11_r4_pad"]], ids=lambda w: w.name)
 def test_timed_entry_matches_and_times(dev, w):
     """bb_attn_forward_timed: the same bits as the untimed call, for the whole call and
     for each phase, and its launch-recorded events bracket a positive duration."""
@@ -213,7 +222,7 @@ def test_bb_attn_forward_symbol_through_ctypes(dev):
     """bb_attn_forward itself, called through ctypes with raw device pointers
     (no binding wrapper), against the oracle on a padded multi-chunk case."""
     import ctypes
-    w = SMALL[6]
+    w = CASE["nb12_r3_pad"]
     say(f"case ctypes bb_attn_forward {w.name}")
     q, k, v, pad = make_inputs(w)
     ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
@@ -331,7 +340,7 @@ def test_tensors_over_4gib_sampled(dev):
 # --------------------------------------------------------------- error paths ---
 
 def test_errors_raise_before_launch(dev):
-    w = SMALL[4]
+    w = CASE["nb9_r4_two_chunks"]
     q, k, v, _ = make_inputs(w)
     dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(dq)
@@ -359,7 +368,11 @@ def test_errors_raise_before_launch(dev):
 
 # --------------------------------------------------- pair masking (flag) ---
 
-QMASK_CASES = [SMALL[6], SMALL[7], SMALL[11], SMALL[13], SMALL[16], SMALL[18], SMALL[19], SMALL[20], SMALL[21]]
+QMASK_NAMES = ("nb12_r3_pad", "nb10_r2_pad_ragged", "bs128_nb11_r4_pad", "fp32_nb9_r3_pad",
+               "nb24_r16_pad_two_trips", "nb10_r3_scattered_pad", "bs128_nb7_r2_scattered_pad",
+               "fp32_nb8_r2_scattered_pad", "nb8_r2_all_padded", "nb30_r25_dense_rows_pad")
+QMASK_CASES = [w for w in SMALL if w.name in QMASK_NAMES]
+assert len(QMASK_CASES) == len(QMASK_NAMES)
 
 
 @pytest.mark.parametrize("w", QMASK_CASES, ids=[w.name for w in QMASK_CASES])
@@ -399,7 +412,7 @@ def test_query_mask_flag_full_shape(dev):
 def test_prepared_forward_matches_and_follows_its_inputs(dev):
     """PreparedForward (arguments checked once) gives bb_attn_forward's bits,
     and a second call after new values are written into q picks them up."""
-    w = SMALL[6]
+    w = CASE["nb12_r3_pad"]
     say(f"case prepared forward {w.name}")
     inputs = make_inputs(w)
     a, _, _ = run_gpu(w, dev, inputs=inputs)

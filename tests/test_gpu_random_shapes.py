@@ -5,7 +5,8 @@ and with the ordinary units (BB_ORDINARY_UNITS); the padded ones also with
 pair masking (BB_QUERY_MASK).
 
 The shapes are drawn once from a fixed seed (PCG64(2024)): block 64 or 128,
-nb from 3 up, r from 0 to its largest legal value (at most 16), B and H from
+nb from 3 up, r from 0 to min(nb - 5, 16) (larger r: the explicit cases of
+the parity and backward tests), B and H from
 1 to 3, bf16 or fp32, and every padding mode (none, a fixed valid length
 including zero, per-sequence block counts, scattered holes).  The case list
 is printed by pytest's ids, so a failure names its shape.

@@ -173,7 +173,8 @@ def test_forward_validation_errors(lib):
     assert fwd(lib, L=1000) == 2                        # L % block
     assert fwd(lib, L=128) == 2                         # nb < 3
     assert fwd(lib, r=12) == 2                          # r > nb-5 (nb = 16)
-    assert fwd(lib, L=64 * 40, r=17) == 2               # r above the kernel's limit
+    assert fwd(lib, L=64 * 40, r=36) == 2               # r > nb-5 (nb = 40)
+    assert fwd(lib, L=64 * 40, r=35, ws_bytes=1) == 5   # r = nb-5 is accepted (stops at the workspace)
     assert fwd(lib, B=-1) == 2
     assert fwd(lib, q=0) == 1                           # BB_ERR_NULL
     assert fwd(lib, out=0) == 1
@@ -239,7 +240,7 @@ def test_workspace_size_formula(lib):
         nb = L // block
         n_s = -(-nb // 8)
         blocks = max([B * H * 2 * n_s] + [small_split_blocks(B, H, nb, block, r)
-                                          for r in range(min(max(nb - 5, 0), 16) + 1)])
+                                          for r in range(max(nb - 5, 0) + 1)])
         def a256(x):
             return (x + 255) // 256 * 256
         exp = 2 * a256(blocks * block * 4) + blocks * block * 64 * 4
