@@ -115,7 +115,7 @@ SMALL = [
           outlier_mult=8.0, data_seed=26),
     # r = 16: middle units of 21 tiles run the tile loop in three trips
     # (8 + 8 + 5 steps), with padding; and the same in fp32 with block 128
-    small("nb24_r16_pad_two_trips", B=2, H=2, L=24 * 64, block=64, r=16, pad="per_seq_blocks",
+    small("nb24_r16_pad_multi_trip", B=2, H=2, L=24 * 64, block=64, r=16, pad="per_seq_blocks",
           pad_lo_blocks=10, pad_hi_blocks=24, data_seed=27),
     small("fp32_bs128_nb22_r16", B=1, H=1, L=22 * 128, block=128, r=16, dtype="fp32", data_seed=28),
     # r = nb - 5, its largest value: every middle row attends every block
@@ -369,7 +369,7 @@ def test_errors_raise_before_launch(dev):
 # --------------------------------------------------- pair masking (flag) ---
 
 QMASK_NAMES = ("nb12_r3_pad", "nb10_r2_pad_ragged", "bs128_nb11_r4_pad", "fp32_nb9_r3_pad",
-               "nb24_r16_pad_two_trips", "nb10_r3_scattered_pad", "bs128_nb7_r2_scattered_pad",
+               "nb24_r16_pad_multi_trip", "nb10_r3_scattered_pad", "bs128_nb7_r2_scattered_pad",
                "fp32_nb8_r2_scattered_pad", "nb8_r2_all_padded", "nb30_r25_dense_rows_pad")
 QMASK_CASES = [w for w in SMALL if w.name in QMASK_NAMES]
 assert len(QMASK_CASES) == len(QMASK_NAMES)
