@@ -29,6 +29,10 @@ their merge -- every per-call step of the hot path.  The random-block table is
 built once on the host beforehand, as the reference builds it once at layer
 construction; its build time is reported separately.
 
+Before the W warm-up calls, a W below CLOCK_SETTLE's count gets untimed
+calls up to that count (about 30 ms of kernels), so that the timed region
+starts at full engine clock; their number is config.clock_settle_calls.
+
 Prints ONE JSON line.  `value` is useful TFLOP/s: 4*d FLOPs per attended
 (query, key) pair, pairs counted from the block pattern (padding included),
 over the wall time of K timed steps (hipEvents on the launch stream, device
@@ -71,6 +75,17 @@ KERNEL_SRC = os.path.join(ROOT, "block_sparse_long_bigbird_amd", "csrc", "bb_att
 BUILD_SCRIPT = os.path.join(ROOT, "block_sparse_long_bigbird_amd", "build.py")
 PROFILES = os.path.join(ROOT, "profiles")
 MAIN_KERNEL = "bb_fused_kernel"
+# Untimed calls made before the W warm-up calls when W is smaller (about 30 ms
+# of kernels per pass): the engine clock ramps up over the first milliseconds
+# of load, and a timed region that starts below full clock reads low (10
+# warm-up calls: 431 useful TFLOP/s on the headline shape; 500: 521).  The
+# count is reported as config.clock_settle_calls; the timed region is always
+# exactly K calls.
+CLOCK_SETTLE = {"forward": 500, "backward": 200, "layer": 200, "stack": 20}
+
+
+def settle_calls(args, which: str) -> int:
+    return max(0, CLOCK_SETTLE[which] - args.warmup)
 
 
 def pairs_per_unit(L: int, block: int, r: int):
@@ -379,7 +394,8 @@ def bench_layer(args, w, dev, stack=False):
             bb.bb_layer_forward(xi, *weights, dpad, dri, w.B, w.L, hid, w.H, w.block, w.r, yi, ws,
                                 stream=stream.cuda_stream)
 
-    for i in range(args.warmup):
+    settle = settle_calls(args, "stack" if stack else "layer")
+    for i in range(settle + args.warmup):
         call(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -412,7 +428,7 @@ def bench_layer(args, w, dev, stack=False):
         "config": {"workload": w.name, "pass": "stack" if stack else "layer", "layers": n_layers,
                    "B": w.B, "L": w.L, "hidden": hid, "H": w.H,
                    "block": w.block, "r": w.r, "pad": w.pad, "mode": "warm" if stack else args.mode,
-                   "input_sets": n_sets,
+                   "input_sets": n_sets, "clock_settle_calls": settle,
                    "useful_gflop_per_step": round(flops / 1e9, 4),
                    "projection_gflop_per_step": round(proj / 1e9, 4)},
         "roofline": {"bound": "mfma",
@@ -465,7 +481,8 @@ def bench_backward(args, w, dev):
         bb.bb_attn_backward(a, b_, c, dpad, dri, doff, drows, w.B, w.H, w.L, w.d, w.block, w.r,
                             o, g, l, gq, gk, gv, ws, stream=stream.cuda_stream, flags=qflag)
 
-    for i in range(args.warmup):
+    settle = settle_calls(args, "backward")
+    for i in range(settle + args.warmup):
         call(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -493,6 +510,7 @@ def bench_backward(args, w, dev):
         "data": "synthetic (seeded N(0,1) draws shaped like the BigBird-base attention layer)",
         "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "L": w.L, "d": w.d,
                    "block": w.block, "r": w.r, "pad": w.pad, "mode": args.mode, "input_sets": n_sets,
+                   "clock_settle_calls": settle,
                    "query_mask": bool(args.query_mask),
                    "useful_gflop_per_step": round(flops / 1e9, 4),
                    "executed_gflop_per_step": round(3.5 * useful_flops(w) / 1e9, 4)},
@@ -512,8 +530,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     # 500 calls (~30 ms of kernels): the engine clock ramps up over the first
-    # few milliseconds of load; with only 10 warm-up calls the timed region
-    # starts below full clock and reads ~15% low.
+    # few milliseconds of load (a smaller W gets untimed clock-settle calls
+    # first, CLOCK_SETTLE).
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
@@ -601,7 +619,8 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    for i in range(args.warmup):
+    settle = settle_calls(args, "forward")
+    for i in range(settle + args.warmup):
         prepared[i % n_sets]()
     torch.cuda.synchronize()
 
@@ -683,6 +702,7 @@ def main():
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "block": w.block, "r": w.r,
             "pad": w.pad, "mode": args.mode, "input_sets": n_sets, "launch": args.launch,
+            "clock_settle_calls": settle,
             "query_mask": bool(args.query_mask),
             "useful_gflop_per_step": round(flops / 1e9, 4),
             "algorithmic_mb_per_step": round(alg_bytes / 1e6, 3),
