@@ -342,9 +342,18 @@ __device__ __forceinline__ uint64_t zero_bytes_any(uint64_t x) {
   return (x - 0x0101010101010101ull) & ~x & 0x8080808080808080ull;
 }
 
+// No key of the subtile padded (no pad byte zero).  Tested first on the AND of
+// the four words: a byte of the AND is non-zero only if that byte is non-zero
+// in every word, so a zero-free AND settles the common all-valid case in half
+// the scalar instructions; otherwise (a zero byte somewhere, or non-0/1 bytes
+// whose AND vanishes) the exact per-word test decides.
+__device__ __forceinline__ bool no_key_padded(const PadWords& w) {
+  if (zero_bytes_any(w.p[0] & w.p[1] & w.p[2] & w.p[3]) == 0) return true;
+  return (zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0;
+}
+
 __device__ __forceinline__ float apply_pad(f32x16& acc, const PadWords& w, int lane, float qs = 1.0f) {
-  if ((zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0)
-    return 0.0f;
+  if (no_key_padded(w)) return 0.0f;
   if ((w.p[0] | w.p[1] | w.p[2] | w.p[3]) == 0) return kMaskRaw;
   const uint32_t m = zero_byte_mask(w.p[0]) | (zero_byte_mask(w.p[1]) << 8) |
                      (zero_byte_mask(w.p[2]) << 16) | (zero_byte_mask(w.p[3]) << 24);
@@ -520,6 +529,7 @@ struct TileList {
   int global;            // 1: global unit, 0: middle unit
   int skip;              // middle unit: position of its first tile in the block's list
                          // (non-zero only for the key chunks of kind 3 units)
+  int r;                 // middle unit: random blocks per row (entries of `rand`); 0 otherwise
   const_i32_ptr rand;    // middle unit: its row of the random-block table
 };
 
@@ -531,6 +541,39 @@ __device__ __forceinline__ int tile_at(const TileList& tl, int u) {
   if (u == tl.nwin + 1) return tl.nb - 1;
   int e = tl.rand[u - tl.nwin - 2];
   return e < 1 ? 1 : (e > tl.nb - 2 ? tl.nb - 2 : e);   // never read outside the sequence
+}
+
+typedef const __attribute__((address_space(1))) int32_t* gi32_ptr;
+
+// This lane's id, computed where the call stands (volatile asm: not hoisted
+// out of a loop, so no register holds it across one).
+__device__ __forceinline__ int lane_id_here() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+
+// tile_at() for 64 list positions at once, one per lane: lane j gets the tile
+// of position u + j (positions at or past the list's end get some tile inside
+// the sequence; the caller never uses them).  Selects instead of branches, and
+// one vector load of the random-table row (its index clamped into the row)
+// instead of one dependent scalar load per random position; the steps then
+// take their ids with one lane read each.
+__device__ __forceinline__ int tile_ids(const TileList& tl, int u, int lane) {
+  const int p = u + lane;
+  if (tl.global) return tl.first + p;
+  const int q = p + tl.skip;
+  int t = q == 0 ? 0 : (q <= tl.nwin ? tl.first + q - 1 : tl.nb - 1);
+  if (tl.r > 0) {
+    // a buffer load bounded by the row: an entry index outside [0, r)
+    // (positions before the random part) reads 0 instead of memory
+    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)reinterpret_cast<uintptr_t>(tl.rand), 0, 4 * tl.r, 0x00020000);
+    int e = __builtin_amdgcn_raw_buffer_load_b32(row, 4 * (q - tl.nwin - 2), 0, 0);
+    e = e < 1 ? 1 : (e > tl.nb - 2 ? tl.nb - 2 : e);   // never read outside the sequence
+    t = q > tl.nwin + 1 ? e : t;
+  }
+  return t;
 }
 
 // A decoded work unit (all values wave-uniform).  Per (b, h) the units are the
@@ -634,6 +677,7 @@ __device__ __forceinline__ Unit decode_unit(kargs_ptr a, const Cursor& c) {
       w.tl.first = chunk * nb / gc;                // balanced chunks: none is empty (gc <= nb)
       w.ntiles = (chunk + 1) * nb / gc - w.tl.first;
       w.tl.nwin = 0;
+      w.tl.r = 0;
       w.tl.rand = nullptr;
     } else {
       const int v = (c.u - 2 * gc * QS) >> LQS;
@@ -648,6 +692,7 @@ __device__ __forceinline__ Unit decode_unit(kargs_ptr a, const Cursor& c) {
       w.tl.global = 0;
       w.tl.first = lo;
       w.tl.nwin = hi - lo + 1;
+      w.tl.r = r;
       w.tl.rand = (const_i32_ptr)(a->rand_idx + (static_cast<size_t>(c.h) * (nb - 2) + (qb - 1)) * r);
       const int nt = 2 + w.tl.nwin + r;            // mc <= the fewest tiles of any middle block
       w.tl.skip = chunk * nt / mc;
@@ -668,6 +713,7 @@ __device__ __forceinline__ Unit decode_unit(kargs_ptr a, const Cursor& c) {
     w.tl.global = 1;
     w.tl.first = chunk * kChunkTiles;
     w.tl.nwin = 0;
+    w.tl.r = 0;
     w.tl.rand = nullptr;
     w.ntiles = nb - w.tl.first < kChunkTiles ? nb - w.tl.first : kChunkTiles;
   } else {
@@ -682,6 +728,7 @@ __device__ __forceinline__ Unit decode_unit(kargs_ptr a, const Cursor& c) {
     w.tl.first = lo;
     w.tl.nwin = hi - lo + 1;
     const int r = a->r;
+    w.tl.r = r;
     w.tl.rand = (const_i32_ptr)(a->rand_idx + (static_cast<size_t>(c.h) * (nb - 2) + (qb - 1)) * r);
     w.ntiles = 2 + w.tl.nwin + r;
   }
@@ -950,8 +997,7 @@ __device__ __forceinline__ PadClass classify_pad(const PadWords& w) {
   PadClass c;
   c.bias = 0.0f;
   c.mixed = 0u;
-  if ((zero_bytes_any(w.p[0]) | zero_bytes_any(w.p[1]) | zero_bytes_any(w.p[2]) | zero_bytes_any(w.p[3])) == 0)
-    return c;
+  if (no_key_padded(w)) return c;
   if ((w.p[0] | w.p[1] | w.p[2] | w.p[3]) == 0) {
     c.bias = kMaskRaw;
     return c;
@@ -1104,10 +1150,10 @@ __device__ __forceinline__ void run(int n_units) {
   for (;;) {
     // Per-lane address arithmetic is redone for every unit rather than kept
     // live across the unit loop (register pressure).
-    // (The lane id is rebuilt from the exec mask rather than kept in a
-    // register: kept, it was spilled, and reloading it drained the prefetch.)
-    int lane_u = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
-    asm volatile("" : "+v"(lane_u));
+    // (The lane id is rebuilt from the exec mask for every unit, by asm the
+    // compiler cannot hoist, rather than kept in a register: kept, it was
+    // spilled, and reloading it drained the prefetch.)
+    const int lane_u = lane_id_here();
     const Cursor nxt = cursor_advance<T, BS, kind>(kargs(), cur, stride);
     const bool has_next = nxt.unit < end;
     NextUnit nx;
@@ -1149,9 +1195,11 @@ __device__ __forceinline__ void run(int n_units) {
     // ---- tile loop: trips of 8 straight-line steps ----------------------------
     // Middle units at r <= 3 and the global chunks have at most 8 tiles, so
     // one trip covers them; longer lists take more.  Tile ids are computed
-    // once per trip: the trip's and the one after it (its last step
-    // prefetches that tile), two per scalar register.
-    // (Trips of 12, with their 14 guarded ids, were 1% slower at r = 3.)
+    // once per trip, one list position per lane (tile_ids()): the trip's and
+    // the one after it (its last step prefetches that tile), then read out of
+    // their lanes two per scalar register (nb < 65536), so that no vector
+    // register holds them across the trip.
+    // (Trips of 12 were 1% slower at r = 3.)
     constexpr int TRIP = 8;
     static_assert(TRIP % 2 == 0, "trip must keep the stage parity aligned");
     for (int u = 0; u < ntiles; u += TRIP) {
@@ -1160,13 +1208,13 @@ __device__ __forceinline__ void run(int n_units) {
       // ntiles - k per step (scalar registers that would spill).
       int rem = ntiles - u;
       asm volatile("" : "+s"(rem));
-      // tile ids of the trip, two 16-bit ids per scalar register (nb < 65536)
       uint32_t tp[(TRIP + 2) / 2];
+      {
+        const int tv = tile_ids(cu.tl, u, lane_u);
 #pragma unroll
-      for (int k = 0; k < (TRIP + 2) / 2; ++k) {
-        const uint32_t t0 = 2 * k < rem ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k)) : 0u;
-        const uint32_t t1 = 2 * k + 1 < rem ? static_cast<uint32_t>(tile_at(cu.tl, u + 2 * k + 1)) : 0u;
-        tp[k] = t0 | (t1 << 16);
+        for (int k = 0; k < (TRIP + 2) / 2; ++k)
+          tp[k] = static_cast<uint32_t>(__builtin_amdgcn_readlane(tv, 2 * k)) |
+                  (static_cast<uint32_t>(__builtin_amdgcn_readlane(tv, 2 * k + 1)) << 16);
       }
 #define BB_TILE(k) static_cast<int>((tp[(k) >> 1] >> (16 * ((k) & 1))) & 0xffffu)
 #define BB_STEP(k)                                                                                  \
