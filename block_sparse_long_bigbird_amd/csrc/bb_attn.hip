@@ -543,8 +543,6 @@ __device__ __forceinline__ int tile_at(const TileList& tl, int u) {
   return e < 1 ? 1 : (e > tl.nb - 2 ? tl.nb - 2 : e);   // never read outside the sequence
 }
 
-typedef const __attribute__((address_space(1))) int32_t* gi32_ptr;
-
 // This lane's id, computed where the call stands (volatile asm: not hoisted
 // out of a loop, so no register holds it across one).
 __device__ __forceinline__ int lane_id_here() {
@@ -556,7 +554,7 @@ __device__ __forceinline__ int lane_id_here() {
 // tile_at() for 64 list positions at once, one per lane: lane j gets the tile
 // of position u + j (positions at or past the list's end get some tile inside
 // the sequence; the caller never uses them).  Selects instead of branches, and
-// one vector load of the random-table row (its index clamped into the row)
+// one vector load of the random-table row, bounded by the row's length,
 // instead of one dependent scalar load per random position; the steps then
 // take their ids with one lane read each.
 __device__ __forceinline__ int tile_ids(const TileList& tl, int u, int lane) {
@@ -565,8 +563,9 @@ __device__ __forceinline__ int tile_ids(const TileList& tl, int u, int lane) {
   const int q = p + tl.skip;
   int t = q == 0 ? 0 : (q <= tl.nwin ? tl.first + q - 1 : tl.nb - 1);
   if (tl.r > 0) {
-    // a buffer load bounded by the row: an entry index outside [0, r)
-    // (positions before the random part) reads 0 instead of memory
+    // a buffer load bounded by the row (4 r bytes): an entry index outside
+    // [0, r) (positions before or after the random part) reads 0 instead of
+    // memory.  Descriptor word 3: 32-bit data format, no swizzle, no stride.
     const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
         (void*)reinterpret_cast<uintptr_t>(tl.rand), 0, 4 * tl.r, 0x00020000);
     int e = __builtin_amdgcn_raw_buffer_load_b32(row, 4 * (q - tl.nwin - 2), 0, 0);
