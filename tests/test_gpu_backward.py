@@ -171,6 +171,26 @@ def check_grads(got, exp, units=None, dtype="bf16"):
     return worst
 
 
+def test_backward_pad_bytes_other_than_one(dev):
+    """pad_mask is "nonzero = real token" in the backward too: valid bytes of
+    0x55 and 0xAA (alternating per 8-byte word, so the AND of a subtile's pad
+    words has zero bytes without any padded key) give the 0/1 mask's
+    gradients bit for bit."""
+    w = small("bwd_padbytes_nb8_r2", B=2, H=2, L=8 * 64, block=64, r=2, pad="fixed",
+              valid_len=8 * 64 - 100, data_seed=75)
+    q, k, v, pad = make_inputs(w)
+    dout = make_dout(w)
+    ri = bb.bb_rand_idx_build(w.rand_seed, w.H, w.L, w.block, w.r)
+    t = np.arange(w.L)
+    vals = np.where((t // 8) % 2 == 0, 0x55, 0xAA).astype(np.uint8)
+    odd = torch.from_numpy(np.where(pad.numpy() != 0, vals[None, :], 0).astype(np.uint8))
+    ref = run_backward(w, dev, (q, k, v, pad), ri, dout)
+    got = run_backward(w, dev, (q, k, v, odd), ri, dout)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert not np.isnan(a).any(), name
+        assert np.array_equal(a, b), name
+
+
 @pytest.mark.parametrize("units", ["default", "ordinary"])
 @pytest.mark.parametrize("w", BWD_CASES, ids=[w.name for w in BWD_CASES])
 def test_backward_matches_oracle(dev, w, units):

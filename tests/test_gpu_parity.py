@@ -366,6 +366,43 @@ def test_errors_raise_before_launch(dev):
     torch.cuda.synchronize()
 
 
+# ------------------------------------------- pad bytes other than 0 and 1 ---
+
+def odd_pad_bytes(pad):
+    """The same mask with every real token's byte replaced by 0x55 or 0xAA,
+    alternating per 8-byte word: the AND of a 32-byte subtile's four words then
+    has zero bytes even where no key is padding, so the kernels' all-valid
+    pre-test (on that AND) falls through to their exact per-word test."""
+    t = np.arange(pad.shape[1])
+    vals = np.where((t // 8) % 2 == 0, 0x55, 0xAA).astype(np.uint8)
+    return torch.from_numpy(np.where(pad.numpy() != 0, vals[None, :], 0).astype(np.uint8))
+
+
+PADBYTE_CASES = [
+    small("padbytes_nb8_r2_ragged", B=2, H=2, L=8 * 64, block=64, r=2, pad="fixed",
+          valid_len=8 * 64 - 100, data_seed=71),
+    small("padbytes_nb10_r3_seq", B=3, H=2, L=10 * 64, block=64, r=3, pad="per_seq_blocks",
+          pad_lo_blocks=4, pad_hi_blocks=10, data_seed=72),
+    small("padbytes_bs128_nb6_r1", B=2, H=2, L=6 * 128, block=128, r=1, pad="fixed",
+          valid_len=6 * 128 - 200, data_seed=73),
+    small("padbytes_fp32_nb8_r2", B=1, H=2, L=8 * 64, block=64, r=2, dtype="fp32", pad="fixed",
+          valid_len=8 * 64 - 100, data_seed=74),
+]
+
+
+@pytest.mark.parametrize("flags", [bb.BB_LAUNCH_FUSED, bb.BB_ORDINARY_UNITS], ids=["default", "ordinary"])
+@pytest.mark.parametrize("w", PADBYTE_CASES, ids=[w.name for w in PADBYTE_CASES])
+def test_pad_bytes_other_than_one(dev, w, flags):
+    """pad_mask is "nonzero = real token": valid bytes of 0x55 and 0xAA give
+    the 0/1 mask's output bit for bit, and both match the oracle."""
+    q, k, v, pad = make_inputs(w)
+    ref, _, ri = run_gpu(w, dev, flags, inputs=(q, k, v, pad))
+    got, _, _ = run_gpu(w, dev, flags, inputs=(q, k, v, odd_pad_bytes(pad)))
+    assert not np.isnan(got).any()
+    assert np.array_equal(got, ref)
+    compare_full(w, got, (q, k, v, pad), ri)
+
+
 # --------------------------------------------------- pair masking (flag) ---
 
 QMASK_NAMES = ("nb12_r3_pad", "nb10_r2_pad_ragged", "bs128_nb11_r4_pad", "fp32_nb9_r3_pad",
